@@ -1,0 +1,176 @@
+"""CPU oracle for the shard-local step (reduce -> mixed-precision AdamW -> gather).
+
+TEST INFRASTRUCTURE ONLY. The test suite, the smoke check and the benchmark's
+CPU-baseline leg are its only users; the product library never imports it.
+
+The element arithmetic lives in ``zs_oracle.c`` (plain C, one fp32 rounding per
+operation); the integer shard plan lives in ``plan.py``. This module marshals
+numpy arrays into the C functions. bf16 arrays are numpy ``uint16`` holding the
+raw bit patterns.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+from .plan import OraclePlan, plan_flat, plan_per_tensor, roundup  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libzs_oracle.so")
+_lib = None
+
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        L = ctypes.CDLL(_LIB_PATH)
+        L.ora_f32_to_bf16.restype = ctypes.c_uint16
+        L.ora_f32_to_bf16.argtypes = [ctypes.c_float]
+        L.ora_bf16_to_f32.restype = ctypes.c_float
+        L.ora_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.ora_f32_to_bf16_array.argtypes = [_f32p, _u16p, _i64]
+        L.ora_reduce.argtypes = [ctypes.POINTER(_u16p), _i32, _i64, _i64, _u16p]
+        L.ora_adamw_coef.argtypes = [ctypes.c_double] * 5 + [_i64, _f32p]
+        L.ora_adamw.argtypes = [_f32p, _u16p, _f32p, _f32p, _f32p, _u16p, _i64, _i64]
+        L.ora_gather.argtypes = [_u16p, _i64, _i32, _i64, _i64, _u16p]
+        L.ora_shard_step.argtypes = [_f32p, ctypes.POINTER(_u16p), _i32, _u16p, _f32p, _f32p, _f32p,
+                                     _u16p, _u16p, _i64, _i32, _i64, _i64]
+        L.ora_time_shard_step.restype = ctypes.c_int
+        L.ora_time_shard_step.argtypes = [_f32p, ctypes.POINTER(_u16p), _i32, _u16p, _f32p, _f32p,
+                                          _f32p, _u16p, _u16p, _i64, _i32, _i64, _i32, _i32,
+                                          ctypes.POINTER(ctypes.c_double)]
+        _lib = L
+    return _lib
+
+
+def _p16(a):
+    assert a.dtype == np.uint16 and a.flags.c_contiguous
+    return a.ctypes.data_as(_u16p)
+
+
+def _p32(a):
+    assert a.dtype == np.float32 and a.flags.c_contiguous
+    return a.ctypes.data_as(_f32p)
+
+
+def _contrib_table(contribs):
+    arr = (_u16p * len(contribs))()
+    for q, c in enumerate(contribs):
+        arr[q] = _p16(c)
+    return arr
+
+
+# ---------------------------------------------------------------- bf16
+
+
+def f32_to_bf16(x):
+    """RNE narrowing of a float32 array (any shape) to bf16 bit patterns (uint16)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().ora_f32_to_bf16_array(_p32(x.reshape(-1)), _p16(out.reshape(-1)), x.size)
+    return out
+
+
+def bf16_to_f32(h):
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    return (h.astype(np.uint32) << 16).view(np.float32)
+
+
+# ---------------------------------------------------------------- AdamW scalars
+
+
+def adamw_coef(lr, beta1, beta2, eps, weight_decay, step):
+    c = np.zeros(9, dtype=np.float32)
+    lib().ora_adamw_coef(lr, beta1, beta2, eps, weight_decay, step, _p32(c))
+    return c
+
+
+class HParams:
+    def __init__(self, lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1):
+        self.lr, self.beta1, self.beta2 = lr, beta1, beta2
+        self.eps, self.weight_decay, self.step = eps, weight_decay, step
+
+    def coef(self):
+        return adamw_coef(self.lr, self.beta1, self.beta2, self.eps, self.weight_decay, self.step)
+
+    def at(self, step):
+        return HParams(self.lr, self.beta1, self.beta2, self.eps, self.weight_decay, step)
+
+
+# ---------------------------------------------------------------- element ops
+
+
+def reduce(contribs, lo=0, hi=None, out=None):
+    """Averaged bf16 gradient over owned elements [lo, hi) of N bf16 contributions."""
+    n = len(contribs)
+    S = contribs[0].size
+    hi = S if hi is None else hi
+    for c in contribs:
+        assert c.size == S
+    out = np.zeros(S, dtype=np.uint16) if out is None else out
+    lib().ora_reduce(_contrib_table(contribs), n, lo, hi, _p16(out))
+    return out
+
+
+def adamw(hp, g, master, m, v, p, lo=0, hi=None):
+    """In-place AdamW on fp32 master/m/v; writes bf16 p. Arrays are 1-D, same length."""
+    hi = g.size if hi is None else hi
+    lib().ora_adamw(_p32(hp.coef()), _p16(g), _p32(master), _p32(m), _p32(v), _p16(p), lo, hi)
+
+
+def gather(p, rank, full, lo=0, hi=None):
+    S = p.size
+    hi = S if hi is None else hi
+    assert full.size >= (rank + 1) * S
+    lib().ora_gather(_p16(p), S, rank, lo, hi, _p16(full))
+
+
+def shard_step(hp, contribs, g, master, m, v, p, full, rank, lo=0, hi=None):
+    S = g.size
+    hi = S if hi is None else hi
+    lib().ora_shard_step(_p32(hp.coef()), _contrib_table(contribs), len(contribs), _p16(g),
+                         _p32(master), _p32(m), _p32(v), _p16(p),
+                         _p16(full) if full is not None else None, S, rank, lo, hi)
+
+
+def time_shard_step(hp, contribs, g, master, m, v, p, full, rank, nthreads, reps):
+    """Wall-clock seconds of ``reps`` whole-window shard steps over all of g's elements."""
+    S = g.size
+    secs = (ctypes.c_double * reps)()
+    rc = lib().ora_time_shard_step(_p32(hp.coef()), _contrib_table(contribs), len(contribs),
+                                   _p16(g), _p32(master), _p32(m), _p32(v), _p16(p),
+                                   _p16(full) if full is not None else None, S, 0, S, nthreads,
+                                   reps, secs)
+    if rc != 0:
+        raise RuntimeError("oracle timing failed")
+    return list(secs)
+
+
+# ---------------------------------------------------------------- whole plans
+
+
+def plan_step(plan, hp, contribs_by_piece, state_by_piece, full_by_tensor=None):
+    """One shard step over every owned piece of a PER_TENSOR or FLAT plan.
+
+    contribs_by_piece[i] is the list of N bf16 arrays of piece i (length = piece
+    length); state_by_piece[i] = (g, master, m, v, p) arrays of piece i; the
+    gathered tensor i (padded, T_i) receives the piece at own_lo when
+    full_by_tensor is given.
+    """
+    for k, pc in enumerate(plan.pieces):
+        g, master, m, v, p = state_by_piece[k]
+        if g.size == 0:
+            continue
+        reduce(contribs_by_piece[k], out=g)
+        adamw(hp, g, master, m, v, p)
+        if full_by_tensor is not None:
+            full_by_tensor[pc.tensor][pc.own_lo:pc.own_hi] = p
