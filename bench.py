@@ -1,0 +1,339 @@
+"""Benchmark of one rank's shard-local step (reduce + mixed-precision AdamW +
+gather) on one MI355X.
+
+A step is one pass of the whole path over the owned shard: the average of the
+N bf16 gradient contributions, AdamW on the fp32 master/m/v state, and the
+bf16 parameter write into the gathered buffer. Inputs are synthetic (seeded
+generator, generated in HBM before the timed region); the other N-1 ranks'
+contributions are local buffers on the one GPU.
+
+Default workload: the Llama-7B shape (6,738,415,616 parameters, 291 tensors)
+at N=8, rank 0 -- an 842,301,952-element shard -- through the fused kernel.
+Prints one JSON line. ``--gpus`` above 1 exits: this benchmark is one GPU's
+share by construction.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E peak
+KERNEL_SRC = os.path.join(ROOT, "fsdp_sharded_mixed_flatten_amd", "csrc", "zs_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+METRIC = "shard step: params updated/s + achieved HBM GB/s (% of MI355X peak)"
+
+
+def kernel_hash():
+    with open(KERNEL_SRC, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def fused_bytes_per_param(N, write_grad=False, write_param=False):
+    # read: N bf16 contributions + fp32 master, m, v; write: fp32 master, m, v + bf16 slice of full
+    return 2 * N + 12 + 12 + 2 + (2 if write_grad else 0) + (2 if write_param else 0)
+
+
+def unfused_bytes_per_param(N):
+    # reduce (2N read + 2 write) + AdamW (2 + 12 read, 12 + 2 write) + gather (2 + 2)
+    return (2 * N + 2) + 28 + 4
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama7b",
+                    choices=["tiny", "qwen3b", "llama7b", "llama7b_wrap", "llama70b"])
+    ap.add_argument("--no-unfused", action="store_true", help="skip the unfused path's timing")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-window", type=int, default=25_000_000,
+                    help="owned elements of the CPU oracle's timed window")
+    ap.add_argument("--calib-copy-gib", type=float, default=0.0,
+                    help="also run a plain device copy of this many GiB (counter calibration)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream the kernels run on)."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, s):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append((s, e))
+
+    def ms(self):
+        self.torch.cuda.synchronize()
+        return [s.elapsed_time(e) for s, e in self.pairs]
+
+
+def flat_setup(zs, synth, wl):
+    import torch
+    plan = zs.zs_shard_plan(wl.numels, wl.world, wl.rank, wl.align, zs.ZS_LAYOUT_FLAT)
+    S, T = plan.shard_numel, plan.padded_numel
+    base, valid = wl.rank * S, sum(wl.numels)
+    st = {}
+    st["contribs"] = [torch.empty(S, dtype=torch.int16, device="cuda") for _ in range(wl.world)]
+    for q, c in enumerate(st["contribs"]):
+        synth.gpu_bf16(c, base, wl.contrib_spec(q, 1, valid))
+    st["master"] = torch.empty(S, dtype=torch.float32, device="cuda")
+    synth.gpu_f32(st["master"], base, wl.master_spec(valid))
+    st["m"] = torch.zeros(S, dtype=torch.float32, device="cuda")
+    st["v"] = torch.zeros(S, dtype=torch.float32, device="cuda")
+    st["grad"] = torch.empty(S, dtype=torch.int16, device="cuda")
+    st["param"] = torch.empty(S, dtype=torch.int16, device="cuda")
+    free, _ = torch.cuda.mem_get_info()
+    # the full gathered buffer (T elements) when it fits; rank 0 writes only [0, S)
+    full_elems = T if free > T * 2 + (4 << 30) else (wl.rank + 1) * S
+    st["full"] = torch.empty(full_elems, dtype=torch.int16, device="cuda")
+    st["full_is_T"] = full_elems == T
+    torch.cuda.synchronize()
+    return plan, st
+
+
+def per_tensor_setup(zs, synth, oracle, wl):
+    import torch
+    plan = zs.zs_shard_plan(wl.numels, wl.world, wl.rank, 1, zs.ZS_LAYOUT_PER_TENSOR)
+    op = oracle.plan_per_tensor(wl.numels, wl.world, wl.rank)
+    pieces, contribs = [], [[] for _ in range(wl.world)]
+    for i, pc in enumerate(op.pieces):
+        Si = pc.own_hi - pc.own_lo
+        valid = op.offsets[i] + wl.numels[i]
+        d = dict(grad=torch.empty(Si, dtype=torch.int16, device="cuda"),
+                 master=torch.empty(Si, dtype=torch.float32, device="cuda"),
+                 m=torch.zeros(Si, dtype=torch.float32, device="cuda"),
+                 v=torch.zeros(Si, dtype=torch.float32, device="cuda"),
+                 param=torch.empty(Si, dtype=torch.int16, device="cuda"),
+                 full=torch.empty(op.padded[i], dtype=torch.int16, device="cuda"))
+        synth.gpu_f32(d["master"], pc.full_off, wl.master_spec(valid))
+        pieces.append(d)
+        for q in range(wl.world):
+            c = torch.empty(Si, dtype=torch.int16, device="cuda")
+            synth.gpu_bf16(c, pc.full_off, wl.contrib_spec(q, 1, valid))
+            contribs[q].append(c)
+    ws = torch.zeros(zs.zs_multi_workspace_bytes(plan, wl.world), dtype=torch.uint8, device="cuda")
+    zs.zs_multi_bind(plan, pieces, contribs, ws)
+    nofull = [dict(pc, full=None, param=None, grad=None) for pc in pieces]
+    ws_fused = torch.zeros_like(ws)
+    zs.zs_multi_bind(plan, [dict(pc, param=None, grad=None) for pc in pieces], contribs, ws_fused)
+    torch.cuda.synchronize()
+    del nofull
+    return plan, dict(pieces=pieces, contribs=contribs, ws=ws, ws_fused=ws_fused)
+
+
+def time_loop(fn, warmup, steps):
+    """Runs fn(t) for warmup + steps steps; returns per-step ms (wall, bracketed
+    by device synchronization) and the HIP-event durations fn recorded."""
+    import torch
+    for i in range(warmup):
+        fn(i + 1, None)
+    torch.cuda.synchronize()
+    timer = Timer()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(warmup + i + 1, timer)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    return wall_ms, timer.ms()
+
+
+def cpu_baseline(oracle, synth, wl, S, window, fused_bpp):
+    """The oracle's shard step timed on this host over a window of the same workload."""
+    import numpy as np
+    n = min(window, S)
+    base, valid = wl.rank * S, sum(wl.numels)
+    contribs = [synth.cpu_bf16(n, base, wl.contrib_spec(q, 1, valid)) for q in range(wl.world)]
+    master = synth.cpu_f32(n, base, wl.master_spec(valid))
+    m, v = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    g, p = np.zeros(n, np.uint16), np.zeros(n, np.uint16)
+    full = np.zeros(n, np.uint16)  # the window's slice of the gathered buffer (rank 0: offset 0)
+    threads = max(1, min(16, os.cpu_count() or 1))
+    hp = oracle.HParams(wl.lr, wl.beta1, wl.beta2, wl.eps, wl.weight_decay, 1)
+    secs = oracle.time_shard_step(hp, contribs, g, master, m, v, p, full, threads, 4)
+    med = statistics.median(secs[1:])
+    secs1 = oracle.time_shard_step(hp, contribs, g, master, m, v, p, full, 1, 1)
+    return {"value": n / med, "unit": "params/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n:,}-element window of the {wl.name} shard (N={wl.world}), "
+                      f"median of 3 timed passes after 1 warm-up, {threads} threads",
+            "gbps_algorithmic": n * fused_bpp / med / 1e9,
+            "single_thread_params_per_s": n / secs1[0]}
+
+
+def read_traffic(kernel_name, workload):
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        data = json.load(open(TRAFFIC_FILE))
+    except ValueError:
+        return None
+    rec = data.get(f"{workload}:{kernel_name}")
+    if not rec or rec.get("kernel_src_sha256_16") != kernel_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's shard step; --gpus {args.gpus} is not supported "
+              f"(this build runs on a single GPU; see DESIGN.md for how the path shards).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import fsdp_sharded_mixed_flatten_amd as zs
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    wl = synth.workloads()[args.workload]
+    N = wl.world
+    hp0 = zs.AdamWHParams(wl.lr, wl.beta1, wl.beta2, wl.eps, wl.weight_decay, 1)
+    log(f"[bench] workload={wl.name} N={N} rank={wl.rank} layout={wl.layout}")
+    result_paths = {}
+
+    if args.calib_copy_gib > 0:
+        n = int(args.calib_copy_gib * 2**30) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: {n * 4:,} bytes read and written per launch, 3 launches")
+        del a, b
+
+    if wl.layout == "flat":
+        plan, st = flat_setup(zs, synth, wl)
+        S = plan.shard_numel
+        log(f"[bench] S={S:,} T={plan.padded_numel:,} gathered buffer {'full' if st['full_is_T'] else 'owned slice'}")
+
+        def fused(t, timer):
+            e = timer.start() if timer else None
+            zs.zs_fused_shard_step(plan, hp0.at(t), st["contribs"], st["master"], st["m"], st["v"],
+                                   full=st["full"])
+            if timer:
+                timer.stop(e)
+
+        wall_ms, ev = time_loop(fused, args.warmup, args.steps)
+        bpp = fused_bytes_per_param(N)
+        kern_ms = statistics.mean(ev)
+        result_paths["fused"] = {"ms_per_step": wall_ms, "kernel_ms_mean": kern_ms,
+                                 "kernel_ms_median": statistics.median(ev), "kernel_ms_p99": max(ev),
+                                 "bytes_per_param": bpp, "launches_per_step": 1,
+                                 "kernel": "k_fused"}
+        main_path = "fused"
+        if not args.no_unfused:
+            B = wl.bucket_elems or S
+
+            def unfused(t, timer):
+                e = timer.start() if timer else None
+                for off in range(0, S, B):
+                    zs.zs_reduce_shard(plan, st["contribs"], st["grad"], off, min(B, S - off))
+                zs.zs_adamw_shard_step(plan, hp0.at(t), st["grad"], st["master"], st["m"], st["v"],
+                                       st["param"])
+                zs.zs_gather_params(plan, st["param"], st["full"])
+                if timer:
+                    timer.stop(e)
+
+            u_wall, u_ev = time_loop(unfused, 1, max(3, args.steps // 2))
+            result_paths["unfused"] = {"ms_per_step": u_wall, "events_ms_mean": statistics.mean(u_ev),
+                                       "bytes_per_param": unfused_bytes_per_param(N),
+                                       "launches_per_step": (S + B - 1) // B + 2,
+                                       "reduce_buckets": (S + B - 1) // B}
+    else:
+        import oracle
+        plan, st = per_tensor_setup(zs, synth, oracle, wl)
+        S = plan.shard_numel
+        log(f"[bench] per-tensor plan: {plan.num_tensors} pieces, S={S:,}")
+
+        def fused(t, timer):
+            e = timer.start() if timer else None
+            zs.zs_fused_shard_step_multi(plan, hp0.at(t), st["ws_fused"])
+            if timer:
+                timer.stop(e)
+
+        wall_ms, ev = time_loop(fused, args.warmup, args.steps)
+        bpp = fused_bytes_per_param(N)
+        kern_ms = statistics.mean(ev)
+        result_paths["fused_multi"] = {"ms_per_step": wall_ms, "kernel_ms_mean": kern_ms,
+                                       "kernel_ms_median": statistics.median(ev),
+                                       "kernel_ms_p99": max(ev), "bytes_per_param": bpp,
+                                       "launches_per_step": 1, "kernel": "k_multi"}
+        main_path = "fused_multi"
+        if not args.no_unfused:
+            def unfused(t, timer):
+                e = timer.start() if timer else None
+                zs.zs_reduce_shard_multi(plan, st["ws"])
+                zs.zs_adamw_shard_step_multi(plan, hp0.at(t), st["ws"])
+                zs.zs_gather_params_multi(plan, st["ws"])
+                if timer:
+                    timer.stop(e)
+
+            u_wall, u_ev = time_loop(unfused, 1, max(3, args.steps // 2))
+            result_paths["unfused_multi"] = {"ms_per_step": u_wall, "events_ms_mean": statistics.mean(u_ev),
+                                             "bytes_per_param": unfused_bytes_per_param(N),
+                                             "launches_per_step": 3}
+
+    params_per_s = S / (wall_ms / 1e3)
+    achieved = S * bpp / (kern_ms / 1e3) / 1e9
+    step_gbps = S * bpp / (wall_ms / 1e3) / 1e9
+    kname = result_paths[main_path]["kernel"]
+    traffic = read_traffic(kname, wl.name)
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        log(f"[bench] CPU oracle baseline on a {min(args.cpu_window, S):,}-element window")
+        cpu = cpu_baseline(oracle, synth, wl, S, args.cpu_window, bpp)
+    out = {
+        "metric": METRIC,
+        "value": params_per_s,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded counter-based generator; model shapes only, no weights)",
+        "config": {"workload": f"{wl.name}_n{N}_{main_path}", "world_size": N, "rank": wl.rank,
+                   "layout": wl.layout, "shard_elems": S, "bytes_per_param": bpp,
+                   "gathered_buffer": "full" if wl.layout != "flat" or st.get("full_is_T") else "owned slice"},
+        "hbm_gbps": step_gbps,
+        "pct_of_peak": 100.0 * step_gbps / HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kernel": kname, "algorithmic_bytes_per_launch": S * bpp},
+        "cpu_baseline": cpu,
+        "paths": result_paths,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,332 @@
+"""Python binding of ``libzs.so``, the MI355X shard-local step (ZeRO / FSDP).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels. Functions carry the C ABI's names (``include/zs.h``). Device buffers
+are PyTorch CUDA tensors (or raw integer device addresses); the stream is
+``torch.cuda.current_stream()`` unless one is given. Before each call the
+binding checks that every tensor is a contiguous CUDA tensor of the right
+dtype and at least as long as the kernels will touch, so a wrong shape is a
+Python exception instead of an out-of-bounds access on the device.
+
+If the library has not been built this module raises on import: there is no
+fallback path.
+"""
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+# ZS_LIB selects another build of the same library (launch-shape variants).
+LIB_PATH = os.environ.get("ZS_LIB") or os.path.join(_HERE, "libzs.so")
+
+ZS_OK, ZS_EINVAL, ZS_EALIGN, ZS_ERANGE, ZS_EHIP, ZS_ENOMEM = 0, -1, -2, -3, -4, -5
+ZS_LAYOUT_FLAT, ZS_LAYOUT_PER_TENSOR = 0, 1
+ZS_MAX_CONTRIBS = 256
+
+_STATUS_NAMES = {0: "ZS_OK", -1: "ZS_EINVAL", -2: "ZS_EALIGN", -3: "ZS_ERANGE", -4: "ZS_EHIP",
+                 -5: "ZS_ENOMEM"}
+
+
+class ZsError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class AdamWHParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double),
+                ("step", ctypes.c_int64)]
+
+    def __init__(self, lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1):
+        super().__init__(lr, beta1, beta2, eps, weight_decay, step)
+
+    def at(self, step):
+        return AdamWHParams(self.lr, self.beta1, self.beta2, self.eps, self.weight_decay, step)
+
+
+class TensorInfo(ctypes.Structure):
+    _fields_ = [("numel", ctypes.c_int64), ("flat_off", ctypes.c_int64),
+                ("padded_numel", ctypes.c_int64), ("own_lo", ctypes.c_int64),
+                ("own_hi", ctypes.c_int64), ("shard_off", ctypes.c_int64)]
+
+
+class PiecePtrs(ctypes.Structure):
+    _fields_ = [("grad", ctypes.c_void_p), ("master", ctypes.c_void_p), ("m", ctypes.c_void_p),
+                ("v", ctypes.c_void_p), ("param", ctypes.c_void_p), ("full", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built (run __graft_entry__.build() or "
+                          f"python {os.path.join(_HERE, 'build.py')})")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    st = ctypes.c_int
+    sigs = {
+        "zs_shard_plan": (st, [ctypes.POINTER(i64), i32, i32, i32, i32, i32, ctypes.POINTER(vp)]),
+        "zs_plan_destroy": (None, [vp]),
+        "zs_plan_padded_numel": (i64, [vp]),
+        "zs_plan_shard_numel": (i64, [vp]),
+        "zs_plan_persistent_bytes": (i64, [vp]),
+        "zs_plan_num_tensors": (i32, [vp]),
+        "zs_plan_world_size": (i32, [vp]),
+        "zs_plan_rank": (i32, [vp]),
+        "zs_plan_layout": (i32, [vp]),
+        "zs_plan_tensor": (st, [vp, i32, ctypes.POINTER(TensorInfo)]),
+        "zs_reduce_shard": (st, [vp, ctypes.POINTER(vp), i32, vp, i64, i64, vp]),
+        "zs_adamw_shard_step": (st, [vp, ctypes.POINTER(AdamWHParams), vp, vp, vp, vp, vp, vp]),
+        "zs_gather_params": (st, [vp, vp, vp, vp]),
+        "zs_fused_shard_step": (st, [vp, ctypes.POINTER(AdamWHParams), ctypes.POINTER(vp), i32, vp, vp,
+                                     vp, vp, vp, vp, vp]),
+        "zs_multi_workspace_bytes": (i64, [vp, i32]),
+        "zs_multi_bind": (st, [vp, ctypes.POINTER(PiecePtrs), ctypes.POINTER(vp), i32, vp, i64, vp]),
+        "zs_reduce_shard_multi": (st, [vp, vp, vp]),
+        "zs_adamw_shard_step_multi": (st, [vp, ctypes.POINTER(AdamWHParams), vp, vp]),
+        "zs_gather_params_multi": (st, [vp, vp, vp]),
+        "zs_fused_shard_step_multi": (st, [vp, ctypes.POINTER(AdamWHParams), vp, vp]),
+        "zs_last_error": (ctypes.c_char_p, []),
+        "zs_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sigs.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
+
+
+_lib = _load()
+EXPORTED = ("zs_shard_plan", "zs_plan_destroy", "zs_plan_padded_numel", "zs_plan_shard_numel",
+            "zs_plan_persistent_bytes", "zs_plan_num_tensors", "zs_plan_world_size", "zs_plan_rank",
+            "zs_plan_layout", "zs_plan_tensor", "zs_reduce_shard", "zs_adamw_shard_step",
+            "zs_gather_params", "zs_fused_shard_step", "zs_multi_workspace_bytes", "zs_multi_bind",
+            "zs_reduce_shard_multi", "zs_adamw_shard_step_multi", "zs_gather_params_multi",
+            "zs_fused_shard_step_multi", "zs_last_error", "zs_version")
+
+
+def lib():
+    return _lib
+
+
+def _check(status):
+    if status != ZS_OK:
+        raise ZsError(status, _lib.zs_last_error().decode())
+
+
+# ---------------------------------------------------------------- marshalling helpers
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+_BF16_NAMES = ("bfloat16", "int16", "uint16")
+
+
+def _ptr(t, kind, need, what):
+    """Device address of ``t`` after checking dtype, device, contiguity and length."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    import torch
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a CUDA tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if kind == "bf16":
+        if str(t.dtype).split(".")[-1] not in _BF16_NAMES:
+            raise ValueError(f"{what} must hold bf16 (bfloat16 or 16-bit integer storage), got {t.dtype}")
+    elif t.dtype != torch.float32:
+        raise ValueError(f"{what} must be float32, got {t.dtype}")
+    if t.numel() < need:
+        raise ValueError(f"{what} holds {t.numel()} elements, the call touches {need}")
+    return t.data_ptr()
+
+
+def _ptr_array(ptrs):
+    arr = (ctypes.c_void_p * max(len(ptrs), 1))()
+    for i, p in enumerate(ptrs):
+        arr[i] = p
+    return arr
+
+
+# ---------------------------------------------------------------- plan
+
+
+class Plan:
+    """Owns a ``zs_plan*``; destroyed with the object (or by ``close``)."""
+
+    def __init__(self, handle):
+        self._h = ctypes.c_void_p(handle)
+
+    @property
+    def handle(self):
+        if not self._h:
+            raise ValueError("plan is closed")
+        return self._h
+
+    def close(self):
+        if self._h:
+            _lib.zs_plan_destroy(self._h)
+            self._h = ctypes.c_void_p(None)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def padded_numel(self):
+        return _lib.zs_plan_padded_numel(self.handle)
+
+    @property
+    def shard_numel(self):
+        return _lib.zs_plan_shard_numel(self.handle)
+
+    @property
+    def persistent_bytes(self):
+        return _lib.zs_plan_persistent_bytes(self.handle)
+
+    @property
+    def num_tensors(self):
+        return _lib.zs_plan_num_tensors(self.handle)
+
+    @property
+    def world_size(self):
+        return _lib.zs_plan_world_size(self.handle)
+
+    @property
+    def rank(self):
+        return _lib.zs_plan_rank(self.handle)
+
+    @property
+    def layout(self):
+        return _lib.zs_plan_layout(self.handle)
+
+    def tensor(self, i):
+        info = TensorInfo()
+        _check(_lib.zs_plan_tensor(self.handle, i, ctypes.byref(info)))
+        return info
+
+
+def zs_shard_plan(numels, world_size, rank, tensor_align_elems=1, layout=ZS_LAYOUT_FLAT):
+    arr = (ctypes.c_int64 * max(len(numels), 1))(*numels)
+    out = ctypes.c_void_p()
+    _check(_lib.zs_shard_plan(arr, len(numels), world_size, rank, tensor_align_elems, layout,
+                              ctypes.byref(out)))
+    return Plan(out.value)
+
+
+# ---------------------------------------------------------------- flat step
+
+
+def zs_reduce_shard(plan, contribs, grad, off=0, length=None, stream=None):
+    S = plan.shard_numel
+    length = S - off if length is None else length
+    end = min(max(off + length, 0), S)  # a bucket outside the shard is the library's ZS_ERANGE
+    ptrs = [_ptr(c, "bf16", end, f"contribs[{q}]") for q, c in enumerate(contribs)]
+    g = _ptr(grad, "bf16", end, "grad")
+    _check(_lib.zs_reduce_shard(plan.handle, _ptr_array(ptrs), len(ptrs), g, off, length,
+                                _stream(stream)))
+
+
+def zs_adamw_shard_step(plan, hp, grad, master, m, v, param, stream=None):
+    S = plan.shard_numel
+    _check(_lib.zs_adamw_shard_step(plan.handle, ctypes.byref(hp), _ptr(grad, "bf16", S, "grad"),
+                                    _ptr(master, "f32", S, "master"), _ptr(m, "f32", S, "m"),
+                                    _ptr(v, "f32", S, "v"), _ptr(param, "bf16", S, "param"),
+                                    _stream(stream)))
+
+
+def zs_gather_params(plan, param, full, stream=None):
+    S, r = plan.shard_numel, plan.rank
+    _check(_lib.zs_gather_params(plan.handle, _ptr(param, "bf16", S, "param"),
+                                 _ptr(full, "bf16", (r + 1) * S, "full"), _stream(stream)))
+
+
+def zs_fused_shard_step(plan, hp, contribs, master, m, v, grad=None, param=None, full=None,
+                        stream=None):
+    S, r = plan.shard_numel, plan.rank
+    ptrs = [_ptr(c, "bf16", S, f"contribs[{q}]") for q, c in enumerate(contribs)]
+    _check(_lib.zs_fused_shard_step(plan.handle, ctypes.byref(hp), _ptr_array(ptrs), len(ptrs),
+                                    _ptr(master, "f32", S, "master"), _ptr(m, "f32", S, "m"),
+                                    _ptr(v, "f32", S, "v"), _ptr(grad, "bf16", S, "grad"),
+                                    _ptr(param, "bf16", S, "param"),
+                                    _ptr(full, "bf16", (r + 1) * S, "full"), _stream(stream)))
+
+
+# ---------------------------------------------------------------- multi-tensor
+
+
+def zs_multi_workspace_bytes(plan, n_contribs):
+    n = _lib.zs_multi_workspace_bytes(plan.handle, n_contribs)
+    if n < 0:
+        raise ZsError(ZS_EINVAL, "multi-tensor workspace needs a PER_TENSOR plan")
+    return n
+
+
+def zs_multi_bind(plan, pieces, contribs, workspace, stream=None):
+    """pieces[i]: dict with keys grad, master, m, v, param, full (tensors or
+    None) for tensor i; contribs: None or contribs[q][i] = rank q's piece of
+    tensor i. workspace: a CUDA uint8 tensor of zs_multi_workspace_bytes."""
+    n = plan.num_tensors
+    if len(pieces) != n:
+        raise ValueError(f"{len(pieces)} piece records for a plan of {n} tensors")
+    recs = (PiecePtrs * max(n, 1))()
+    for i, pc in enumerate(pieces):
+        info = plan.tensor(i)
+        Si = info.own_hi - info.own_lo
+        recs[i] = PiecePtrs(_ptr(pc.get("grad"), "bf16", Si, f"pieces[{i}].grad"),
+                            _ptr(pc.get("master"), "f32", Si, f"pieces[{i}].master"),
+                            _ptr(pc.get("m"), "f32", Si, f"pieces[{i}].m"),
+                            _ptr(pc.get("v"), "f32", Si, f"pieces[{i}].v"),
+                            _ptr(pc.get("param"), "bf16", Si, f"pieces[{i}].param"),
+                            _ptr(pc.get("full"), "bf16", info.padded_numel, f"pieces[{i}].full"))
+    nq = 0 if contribs is None else len(contribs)
+    flat = []
+    for q in range(nq):
+        if len(contribs[q]) != n:
+            raise ValueError(f"contribs[{q}] has {len(contribs[q])} pieces, the plan has {n}")
+        for i in range(n):
+            info = plan.tensor(i)
+            flat.append(_ptr(contribs[q][i], "bf16", info.own_hi - info.own_lo, f"contribs[{q}][{i}]"))
+    import torch
+    if not (isinstance(workspace, torch.Tensor) and workspace.is_cuda):
+        raise ValueError("workspace must be a CUDA tensor")
+    _check(_lib.zs_multi_bind(plan.handle, recs, _ptr_array(flat) if nq else None, nq,
+                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                              _stream(stream)))
+
+
+def zs_reduce_shard_multi(plan, workspace, stream=None):
+    _check(_lib.zs_reduce_shard_multi(plan.handle, workspace.data_ptr(), _stream(stream)))
+
+
+def zs_adamw_shard_step_multi(plan, hp, workspace, stream=None):
+    _check(_lib.zs_adamw_shard_step_multi(plan.handle, ctypes.byref(hp), workspace.data_ptr(),
+                                          _stream(stream)))
+
+
+def zs_gather_params_multi(plan, workspace, stream=None):
+    _check(_lib.zs_gather_params_multi(plan.handle, workspace.data_ptr(), _stream(stream)))
+
+
+def zs_fused_shard_step_multi(plan, hp, workspace, stream=None):
+    _check(_lib.zs_fused_shard_step_multi(plan.handle, ctypes.byref(hp), workspace.data_ptr(),
+                                          _stream(stream)))
+
+
+def zs_last_error():
+    return _lib.zs_last_error().decode()
+
+
+def zs_version():
+    return _lib.zs_version().decode()

@@ -1,0 +1,56 @@
+"""Builds the shard-step library libzs.so for gfx950, in-tree.
+
+Host code (plan, validation) is C++17; kernels are HIP compiled for gfx950
+with contraction off (the element arithmetic must round operation by
+operation) and packed-fp32 instruction generation disabled.
+"""
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
+LIB = os.path.join(HERE, "libzs.so")
+BUILD = os.path.join(HERE, "_build")
+
+HIPCC = os.environ.get("HIPCC", "hipcc")
+ARCH = "gfx950"
+COMMON = ["-O3", "-fPIC", "-std=c++17", "-ffp-contract=off", "-Wall", "-Wextra", f"-I{INCLUDE}"]
+HIP_ONLY = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(line for line in res.stderr.splitlines() if noise not in line)
+    if res.returncode != 0:
+        raise RuntimeError(f"build step failed: {' '.join(cmd)}\n{err}")
+    if err.strip() and verbose:
+        print(err)
+
+
+def build(verbose=False, out=None, defines=()):
+    """Builds libzs.so (or ``out``); ``defines`` are extra -D flags for the
+    kernels' launch-shape constants."""
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    api_o = os.path.join(BUILD, "zs_api.o")
+    _run(["g++", *COMMON, "-c", os.path.join(CSRC, "zs_api.cpp"), "-o", api_o], verbose)
+    objs.append(api_o)
+    ker_o = os.path.join(BUILD, "zs_kernels.o")
+    _run([HIPCC, *COMMON, *HIP_ONLY, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, "zs_kernels.hip"),
+          "-o", ker_o], verbose)
+    objs.append(ker_o)
+    target = out or LIB
+    tmp = target + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+    os.replace(tmp, target)
+    return target
+
+
+if __name__ == "__main__":
+    build(verbose="-v" in sys.argv)

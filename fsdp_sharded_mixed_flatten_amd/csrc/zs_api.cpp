@@ -1,0 +1,473 @@
+// Host side of the C ABI: shard plan, argument validation, error reporting
+// and the multi-tensor workspace binding. Every device-touching entry point
+// validates all of its arguments before it enqueues anything.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "zs_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+zs_status fail(zs_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+constexpr int64_t kMaxElems = int64_t(1) << 60;
+
+int64_t roundup(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+zs_status check_ptr(const void* p, const char* what) {
+    if (!p) return fail(ZS_EINVAL, "%s is NULL", what);
+    if (!aligned16(p)) return fail(ZS_EALIGN, "%s (%p) is not 16-byte aligned", what, p);
+    return ZS_OK;
+}
+
+zs_status check_opt_ptr(const void* p, const char* what) { return p ? check_ptr(p, what) : ZS_OK; }
+
+zs_status check_plan(const zs_plan* plan) {
+    if (!plan) return fail(ZS_EINVAL, "plan is NULL");
+    return ZS_OK;
+}
+
+zs_status check_hp(const zs_adamw_hparams* hp) {
+    if (!hp) return fail(ZS_EINVAL, "hparams is NULL");
+    const double v[5] = {hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay};
+    for (double x : v)
+        if (!std::isfinite(x)) return fail(ZS_EINVAL, "hparams hold a non-finite value");
+    if (hp->beta1 < 0.0 || hp->beta1 >= 1.0 || hp->beta2 < 0.0 || hp->beta2 >= 1.0)
+        return fail(ZS_EINVAL, "beta1 = %g and beta2 = %g must lie in [0, 1)", hp->beta1, hp->beta2);
+    if (hp->eps < 0.0) return fail(ZS_EINVAL, "eps = %g is negative", hp->eps);
+    if (hp->step < 1) return fail(ZS_EINVAL, "step = %lld, the first AdamW step is 1", (long long)hp->step);
+    return ZS_OK;
+}
+
+zs_status check_contribs(const zs_plan* plan, const void* const* contribs, int32_t n) {
+    if (!contribs) return fail(ZS_EINVAL, "contribs is NULL");
+    if (n != plan->world)
+        return fail(ZS_EINVAL, "n_contribs = %d but the plan's world size is %d", n, plan->world);
+    if (n < 1 || n > ZS_MAX_CONTRIBS)
+        return fail(ZS_EINVAL, "n_contribs = %d outside [1, %d]", n, ZS_MAX_CONTRIBS);
+    for (int32_t q = 0; q < n; ++q) {
+        if (!contribs[q]) return fail(ZS_EINVAL, "contribs[%d] is NULL (no contribution from rank %d)", q, q);
+        if (!aligned16(contribs[q])) return fail(ZS_EALIGN, "contribs[%d] is not 16-byte aligned", q);
+    }
+    return ZS_OK;
+}
+
+zs_status hip_status(int err, const char* what) {
+    if (err == 0) return ZS_OK;
+    return fail(ZS_EHIP, "%s: HIP error %d (%s)", what, err, zs::hip_error_text(err));
+}
+
+// Registry of bound multi-tensor workspaces: which plan and which fields.
+struct Binding {
+    const zs_plan* plan;
+    int32_t flags;
+    int32_t n_contribs;
+};
+std::mutex g_bind_mu;
+std::unordered_map<const void*, Binding> g_bind;
+
+}  // namespace
+
+namespace zs {
+
+AdamCoef make_coef(const zs_adamw_hparams& hp) {
+    AdamCoef c;
+    c.b1 = (float)hp.beta1;
+    c.omb1 = (float)(1.0 - hp.beta1);
+    c.b2 = (float)hp.beta2;
+    c.omb2 = (float)(1.0 - hp.beta2);
+    c.lr = (float)hp.lr;
+    c.eps = (float)hp.eps;
+    c.decay = (float)(1.0 - hp.lr * hp.weight_decay);
+    c.bc1 = (float)(1.0 - std::pow(hp.beta1, (double)hp.step));
+    c.bc2 = (float)(1.0 - std::pow(hp.beta2, (double)hp.step));
+    return c;
+}
+
+}  // namespace zs
+
+extern "C" {
+
+const char* zs_last_error(void) { return g_err.c_str(); }
+
+const char* zs_version(void) { return "0.1.0"; }
+
+// ------------------------------------------------------------------ plan
+
+zs_status zs_shard_plan(const int64_t* numels, int32_t n_tensors, int32_t world_size, int32_t rank,
+                        int32_t tensor_align_elems, int32_t layout, zs_plan** out) {
+    if (!out) return fail(ZS_EINVAL, "out is NULL");
+    if (n_tensors < 0) return fail(ZS_EINVAL, "n_tensors = %d is negative", n_tensors);
+    if (n_tensors > 0 && !numels) return fail(ZS_EINVAL, "numels is NULL");
+    if (world_size < 1) return fail(ZS_EINVAL, "world_size = %d must be >= 1", world_size);
+    if (rank < 0 || rank >= world_size)
+        return fail(ZS_EINVAL, "rank = %d outside [0, %d)", rank, world_size);
+    if (layout != ZS_LAYOUT_FLAT && layout != ZS_LAYOUT_PER_TENSOR)
+        return fail(ZS_EINVAL, "unknown layout %d", layout);
+    if (layout == ZS_LAYOUT_FLAT && tensor_align_elems < 1)
+        return fail(ZS_EINVAL, "tensor_align_elems = %d must be >= 1", tensor_align_elems);
+    for (int32_t i = 0; i < n_tensors; ++i)
+        if (numels[i] < 0 || numels[i] > kMaxElems)
+            return fail(ZS_EINVAL, "numels[%d] = %lld out of range", i, (long long)numels[i]);
+
+    zs_plan* p = new (std::nothrow) zs_plan();
+    if (!p) return fail(ZS_ENOMEM, "out of host memory");
+    p->layout = layout;
+    p->world = world_size;
+    p->rank = rank;
+    p->align = layout == ZS_LAYOUT_FLAT ? tensor_align_elems : 1;
+    const int64_t granule = int64_t(8) * world_size;  // N shards of whole 16-byte vectors
+    try {
+        p->tensors.resize((size_t)n_tensors);
+        if (layout == ZS_LAYOUT_FLAT) {
+            int64_t end = 0;
+            for (int32_t i = 0; i < n_tensors; ++i) {
+                zs::TensorEntry& t = p->tensors[(size_t)i];
+                t.numel = numels[i];
+                t.flat_off = roundup(end, p->align);
+                t.padded = t.numel;
+                end = t.flat_off + t.numel;
+                if (end > kMaxElems) {
+                    delete p;
+                    return fail(ZS_EINVAL, "flat buffer exceeds 2^60 elements");
+                }
+            }
+            p->T = roundup(end, granule);
+            p->S = p->T / world_size;
+            const int64_t lo = (int64_t)rank * p->S, hi = lo + p->S;
+            for (auto& t : p->tensors) {
+                const int64_t a = std::max(t.flat_off, lo), b = std::min(t.flat_off + t.numel, hi);
+                if (a < b) {
+                    t.own_lo = a - t.flat_off;
+                    t.own_hi = b - t.flat_off;
+                    t.shard_off = a - lo;
+                } else {
+                    t.own_lo = t.own_hi = 0;
+                    t.shard_off = std::min(std::max(t.flat_off - lo, int64_t(0)), p->S);
+                }
+            }
+        } else {
+            int64_t full = 0, shard = 0;
+            for (int32_t i = 0; i < n_tensors; ++i) {
+                zs::TensorEntry& t = p->tensors[(size_t)i];
+                t.numel = numels[i];
+                t.padded = roundup(t.numel, granule);
+                t.flat_off = full;
+                const int64_t Si = t.padded / world_size;
+                t.own_lo = (int64_t)rank * Si;
+                t.own_hi = t.own_lo + Si;
+                t.shard_off = shard;
+                full += t.padded;
+                shard += Si;
+                if (full > kMaxElems) {
+                    delete p;
+                    return fail(ZS_EINVAL, "packed buffer exceeds 2^60 elements");
+                }
+                for (int64_t c = 0; c < Si; c += zs::kChunkElems)
+                    p->chunks.push_back(zs::Chunk{i, (int32_t)std::min<int64_t>(zs::kChunkElems, Si - c), c});
+            }
+            p->T = full;
+            p->S = shard;
+            if (p->chunks.size() > (size_t)INT32_MAX) {
+                delete p;
+                return fail(ZS_EINVAL, "too many multi-tensor chunks");
+            }
+        }
+    } catch (const std::bad_alloc&) {
+        delete p;
+        return fail(ZS_ENOMEM, "out of host memory");
+    }
+    *out = p;
+    return ZS_OK;
+}
+
+void zs_plan_destroy(zs_plan* plan) {
+    if (!plan) return;
+    {
+        std::lock_guard<std::mutex> lk(g_bind_mu);
+        for (auto it = g_bind.begin(); it != g_bind.end();)
+            it = it->second.plan == plan ? g_bind.erase(it) : std::next(it);
+    }
+    delete plan;
+}
+
+int64_t zs_plan_padded_numel(const zs_plan* p) { return p ? p->T : -1; }
+int64_t zs_plan_shard_numel(const zs_plan* p) { return p ? p->S : -1; }
+int64_t zs_plan_persistent_bytes(const zs_plan* p) { return p ? 16 * p->S : -1; }
+int32_t zs_plan_num_tensors(const zs_plan* p) { return p ? (int32_t)p->tensors.size() : -1; }
+int32_t zs_plan_world_size(const zs_plan* p) { return p ? p->world : -1; }
+int32_t zs_plan_rank(const zs_plan* p) { return p ? p->rank : -1; }
+int32_t zs_plan_layout(const zs_plan* p) { return p ? p->layout : -1; }
+
+zs_status zs_plan_tensor(const zs_plan* p, int32_t i, zs_tensor_info* out) {
+    if (zs_status st = check_plan(p)) return st;
+    if (!out) return fail(ZS_EINVAL, "out is NULL");
+    if (i < 0 || i >= (int32_t)p->tensors.size())
+        return fail(ZS_EINVAL, "tensor index %d outside [0, %zu)", i, p->tensors.size());
+    const zs::TensorEntry& t = p->tensors[(size_t)i];
+    out->numel = t.numel;
+    out->flat_off = t.flat_off;
+    out->padded_numel = t.padded;
+    out->own_lo = t.own_lo;
+    out->own_hi = t.own_hi;
+    out->shard_off = t.shard_off;
+    return ZS_OK;
+}
+
+// ------------------------------------------------------------------ flat step
+
+zs_status zs_reduce_shard(const zs_plan* plan, const void* const* contribs, int32_t n_contribs,
+                          void* grad_bf16, int64_t off, int64_t len, void* stream) {
+    if (zs_status st = check_plan(plan)) return st;
+    if (zs_status st = check_contribs(plan, contribs, n_contribs)) return st;
+    if (zs_status st = check_ptr(grad_bf16, "grad_bf16")) return st;
+    if (off < 0 || len < 0 || off % 8 || len % 8 || off > plan->S || len > plan->S - off)
+        return fail(ZS_ERANGE, "bucket [%lld, %lld) must be multiples of 8 inside the shard [0, %lld)",
+                    (long long)off, (long long)(off + len), (long long)plan->S);
+    if (len == 0) return ZS_OK;
+    const void* shifted[ZS_MAX_CONTRIBS];
+    for (int32_t q = 0; q < n_contribs; ++q) shifted[q] = static_cast<const char*>(contribs[q]) + 2 * off;
+    return hip_status(zs::launch_reduce(shifted, n_contribs, static_cast<char*>(grad_bf16) + 2 * off, len, stream),
+                      "reduce launch");
+}
+
+zs_status zs_adamw_shard_step(const zs_plan* plan, const zs_adamw_hparams* hp, const void* grad_bf16,
+                              float* master, float* m, float* v, void* param_bf16, void* stream) {
+    if (zs_status st = check_plan(plan)) return st;
+    if (zs_status st = check_hp(hp)) return st;
+    if (zs_status st = check_ptr(grad_bf16, "grad_bf16")) return st;
+    if (zs_status st = check_ptr(master, "master")) return st;
+    if (zs_status st = check_ptr(m, "m")) return st;
+    if (zs_status st = check_ptr(v, "v")) return st;
+    if (zs_status st = check_ptr(param_bf16, "param_bf16")) return st;
+    if (plan->S == 0) return ZS_OK;
+    return hip_status(zs::launch_adamw(zs::make_coef(*hp), grad_bf16, master, m, v, param_bf16, plan->S, stream),
+                      "adamw launch");
+}
+
+zs_status zs_gather_params(const zs_plan* plan, const void* param_bf16, void* full_bf16, void* stream) {
+    if (zs_status st = check_plan(plan)) return st;
+    if (plan->layout != ZS_LAYOUT_FLAT)
+        return fail(ZS_EINVAL, "zs_gather_params needs a FLAT plan; PER_TENSOR plans gather through "
+                               "zs_gather_params_multi");
+    if (zs_status st = check_ptr(param_bf16, "param_bf16")) return st;
+    if (zs_status st = check_ptr(full_bf16, "full_bf16")) return st;
+    if (plan->S == 0) return ZS_OK;
+    char* own = static_cast<char*>(full_bf16) + 2 * (int64_t)plan->rank * plan->S;
+    return hip_status(zs::launch_gather(param_bf16, own, plan->S, stream), "gather launch");
+}
+
+zs_status zs_fused_shard_step(const zs_plan* plan, const zs_adamw_hparams* hp, const void* const* contribs,
+                              int32_t n_contribs, float* master, float* m, float* v, void* grad_bf16,
+                              void* param_bf16, void* full_bf16, void* stream) {
+    if (zs_status st = check_plan(plan)) return st;
+    if (zs_status st = check_hp(hp)) return st;
+    if (zs_status st = check_contribs(plan, contribs, n_contribs)) return st;
+    if (zs_status st = check_ptr(master, "master")) return st;
+    if (zs_status st = check_ptr(m, "m")) return st;
+    if (zs_status st = check_ptr(v, "v")) return st;
+    if (zs_status st = check_opt_ptr(grad_bf16, "grad_bf16")) return st;
+    if (zs_status st = check_opt_ptr(param_bf16, "param_bf16")) return st;
+    if (zs_status st = check_opt_ptr(full_bf16, "full_bf16")) return st;
+    if (full_bf16 && plan->layout != ZS_LAYOUT_FLAT)
+        return fail(ZS_EINVAL, "a gather into full_bf16 needs a FLAT plan; PER_TENSOR plans use "
+                               "zs_fused_shard_step_multi");
+    if (plan->S == 0) return ZS_OK;
+    char* own = full_bf16 ? static_cast<char*>(full_bf16) + 2 * (int64_t)plan->rank * plan->S : nullptr;
+    return hip_status(zs::launch_fused(zs::make_coef(*hp), contribs, n_contribs, master, m, v, grad_bf16,
+                                       param_bf16, own, plan->S, stream),
+                      "fused launch");
+}
+
+// ------------------------------------------------------------------ multi-tensor
+
+namespace {
+
+struct MultiLayout {
+    int64_t pieces_off, contribs_off, chunks_off, total;
+};
+
+MultiLayout multi_layout(const zs_plan* p, int32_t n_contribs) {
+    auto al = [](int64_t x) { return roundup(x, 256); };
+    MultiLayout L;
+    const int64_t n = (int64_t)p->tensors.size();
+    L.pieces_off = al((int64_t)sizeof(zs::MultiHeader));
+    L.contribs_off = al(L.pieces_off + n * (int64_t)sizeof(zs::PieceDev));
+    L.chunks_off = al(L.contribs_off + n * (int64_t)n_contribs * (int64_t)sizeof(void*));
+    L.total = al(L.chunks_off + (int64_t)p->chunks.size() * (int64_t)sizeof(zs::Chunk));
+    return L;
+}
+
+zs_status check_multi_plan(const zs_plan* plan) {
+    if (zs_status st = check_plan(plan)) return st;
+    if (plan->layout != ZS_LAYOUT_PER_TENSOR)
+        return fail(ZS_EINVAL, "multi-tensor calls need a PER_TENSOR plan");
+    return ZS_OK;
+}
+
+zs_status lookup_binding(const zs_plan* plan, const void* ws, int32_t need, Binding* out) {
+    if (!ws) return fail(ZS_EINVAL, "workspace is NULL");
+    std::lock_guard<std::mutex> lk(g_bind_mu);
+    auto it = g_bind.find(ws);
+    if (it == g_bind.end()) return fail(ZS_EINVAL, "workspace %p was never bound by zs_multi_bind", ws);
+    if (it->second.plan != plan) return fail(ZS_EINVAL, "workspace %p was bound to another plan", ws);
+    if ((it->second.flags & need) != need)
+        return fail(ZS_EINVAL, "workspace %p lacks fields this call needs (bound 0x%x, needed 0x%x)", ws,
+                    it->second.flags, need);
+    *out = it->second;
+    return ZS_OK;
+}
+
+}  // namespace
+
+int64_t zs_multi_workspace_bytes(const zs_plan* plan, int32_t n_contribs) {
+    if (!plan || plan->layout != ZS_LAYOUT_PER_TENSOR || n_contribs < 0 || n_contribs > ZS_MAX_CONTRIBS) return -1;
+    return multi_layout(plan, n_contribs).total;
+}
+
+zs_status zs_multi_bind(const zs_plan* plan, const zs_piece_ptrs* pieces, const void* const* contribs,
+                        int32_t n_contribs, void* workspace, int64_t workspace_bytes, void* stream) {
+    if (zs_status st = check_multi_plan(plan)) return st;
+    if (!pieces && !plan->tensors.empty()) return fail(ZS_EINVAL, "pieces is NULL");
+    if (zs_status st = check_ptr(workspace, "workspace")) return st;
+    if (n_contribs != 0 && n_contribs != plan->world)
+        return fail(ZS_EINVAL, "n_contribs = %d must be 0 or the world size %d", n_contribs, plan->world);
+    if (n_contribs > 0 && !contribs) return fail(ZS_EINVAL, "contribs is NULL");
+    const MultiLayout L = multi_layout(plan, n_contribs);
+    if (workspace_bytes < L.total)
+        return fail(ZS_ENOMEM, "workspace holds %lld bytes, the binding needs %lld", (long long)workspace_bytes,
+                    (long long)L.total);
+
+    const int32_t n = (int32_t)plan->tensors.size();
+    // Which fields are bound: decided by the first non-empty piece, and every
+    // other non-empty piece must agree.
+    int32_t flags = -1;
+    for (int32_t i = 0; i < n; ++i) {
+        const zs::TensorEntry& t = plan->tensors[(size_t)i];
+        if (t.own_hi == t.own_lo) continue;
+        const zs_piece_ptrs& pc = pieces[i];
+        int32_t f = 0;
+        if (pc.grad) f |= zs::kHasGrad;
+        if (pc.master || pc.m || pc.v) {
+            if (!(pc.master && pc.m && pc.v))
+                return fail(ZS_EINVAL, "piece %d binds only part of master/m/v", i);
+            f |= zs::kHasState;
+        }
+        if (pc.param) f |= zs::kHasParam;
+        if (pc.full) f |= zs::kHasFull;
+        if (flags < 0) flags = f;
+        if (f != flags) return fail(ZS_EINVAL, "piece %d binds a different set of fields than piece 0", i);
+        const void* ptrs[6] = {pc.grad, pc.master, pc.m, pc.v, pc.param, pc.full};
+        const char* names[6] = {"grad", "master", "m", "v", "param", "full"};
+        for (int k = 0; k < 6; ++k)
+            if (ptrs[k] && !aligned16(ptrs[k])) return fail(ZS_EALIGN, "piece %d: %s is not 16-byte aligned", i, names[k]);
+        if (pc.full && ((t.own_lo * 2) & 15))
+            return fail(ZS_EALIGN, "piece %d: owned offset of the gathered tensor is not 16-byte aligned", i);
+        for (int32_t q = 0; q < n_contribs; ++q) {
+            const void* c = contribs[(int64_t)q * n + i];
+            if (!c) return fail(ZS_EINVAL, "contribution of rank %d for piece %d is NULL", q, i);
+            if (!aligned16(c)) return fail(ZS_EALIGN, "contribution of rank %d for piece %d is not aligned", q, i);
+        }
+    }
+    if (flags < 0) flags = 0;
+    if (n_contribs > 0) flags |= zs::kHasContribs;
+
+    std::vector<char> host;
+    try {
+        host.assign((size_t)L.total, 0);
+    } catch (const std::bad_alloc&) {
+        return fail(ZS_ENOMEM, "out of host memory");
+    }
+    zs::MultiHeader* h = reinterpret_cast<zs::MultiHeader*>(host.data());
+    h->magic = zs::kMultiMagic;
+    h->n_pieces = n;
+    h->n_chunks = (int32_t)plan->chunks.size();
+    h->n_contribs = n_contribs;
+    h->flags = flags;
+    h->pieces_off = L.pieces_off;
+    h->contribs_off = L.contribs_off;
+    h->chunks_off = L.chunks_off;
+    zs::PieceDev* pd = reinterpret_cast<zs::PieceDev*>(host.data() + L.pieces_off);
+    const void** cd = reinterpret_cast<const void**>(host.data() + L.contribs_off);
+    for (int32_t i = 0; i < n; ++i) {
+        const zs::TensorEntry& t = plan->tensors[(size_t)i];
+        const zs_piece_ptrs& pc = pieces[i];
+        pd[i].grad = pc.grad;
+        pd[i].master = pc.master;
+        pd[i].m = pc.m;
+        pd[i].v = pc.v;
+        pd[i].param = pc.param;
+        pd[i].full_own = pc.full ? static_cast<char*>(pc.full) + 2 * t.own_lo : nullptr;
+        pd[i].len = t.own_hi - t.own_lo;
+        for (int32_t q = 0; q < n_contribs; ++q) cd[(int64_t)i * n_contribs + q] = contribs[(int64_t)q * n + i];
+    }
+    std::memcpy(host.data() + L.chunks_off, plan->chunks.data(), plan->chunks.size() * sizeof(zs::Chunk));
+    if (zs_status st = hip_status(zs::copy_h2d_sync(workspace, host.data(), L.total, stream), "workspace copy"))
+        return st;
+    std::lock_guard<std::mutex> lk(g_bind_mu);
+    g_bind[workspace] = Binding{plan, flags, n_contribs};
+    return ZS_OK;
+}
+
+zs_status zs_reduce_shard_multi(const zs_plan* plan, const void* workspace, void* stream) {
+    if (zs_status st = check_multi_plan(plan)) return st;
+    Binding b;
+    if (zs_status st = lookup_binding(plan, workspace, zs::kHasContribs | zs::kHasGrad, &b)) return st;
+    return hip_status(zs::launch_multi(zs::kOpReduce, nullptr, workspace, (int)plan->chunks.size(), b.n_contribs,
+                                       b.flags, stream),
+                      "multi reduce launch");
+}
+
+zs_status zs_adamw_shard_step_multi(const zs_plan* plan, const zs_adamw_hparams* hp, const void* workspace,
+                                    void* stream) {
+    if (zs_status st = check_multi_plan(plan)) return st;
+    if (zs_status st = check_hp(hp)) return st;
+    Binding b;
+    if (zs_status st = lookup_binding(plan, workspace, zs::kHasGrad | zs::kHasState, &b)) return st;
+    const zs::AdamCoef c = zs::make_coef(*hp);
+    return hip_status(zs::launch_multi(zs::kOpAdamw, &c, workspace, (int)plan->chunks.size(), b.n_contribs, b.flags,
+                                       stream),
+                      "multi adamw launch");
+}
+
+zs_status zs_gather_params_multi(const zs_plan* plan, const void* workspace, void* stream) {
+    if (zs_status st = check_multi_plan(plan)) return st;
+    Binding b;
+    if (zs_status st = lookup_binding(plan, workspace, zs::kHasParam | zs::kHasFull, &b)) return st;
+    return hip_status(zs::launch_multi(zs::kOpGather, nullptr, workspace, (int)plan->chunks.size(), b.n_contribs,
+                                       b.flags, stream),
+                      "multi gather launch");
+}
+
+zs_status zs_fused_shard_step_multi(const zs_plan* plan, const zs_adamw_hparams* hp, const void* workspace,
+                                    void* stream) {
+    if (zs_status st = check_multi_plan(plan)) return st;
+    if (zs_status st = check_hp(hp)) return st;
+    Binding b;
+    if (zs_status st = lookup_binding(plan, workspace, zs::kHasContribs | zs::kHasState, &b)) return st;
+    const zs::AdamCoef c = zs::make_coef(*hp);
+    return hip_status(zs::launch_multi(zs::kOpFused, &c, workspace, (int)plan->chunks.size(), b.n_contribs, b.flags,
+                                       stream),
+                      "multi fused launch");
+}
+
+}  // extern "C"

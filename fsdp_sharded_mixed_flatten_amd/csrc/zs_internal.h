@@ -1,0 +1,102 @@
+// Internal declarations shared by the host side (plan, C ABI) and the HIP
+// kernel launchers. Not part of the public ABI.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/zs.h"
+
+namespace zs {
+
+// fp32 scalars of one AdamW step, each rounded once from double.
+struct AdamCoef {
+    float b1, omb1, b2, omb2, lr, eps, decay, bc1, bc2;
+};
+
+AdamCoef make_coef(const zs_adamw_hparams& hp);
+
+struct TensorEntry {
+    int64_t numel;
+    int64_t flat_off;  // FLAT: start in the flat buffer; PER_TENSOR: packed start of padded tensor
+    int64_t padded;    // PER_TENSOR: T_i; FLAT: numel
+    int64_t own_lo, own_hi;  // owned range, tensor-local coordinates
+    int64_t shard_off;       // start of the owned range in the packed shard
+};
+
+// One multi-tensor-apply chunk: `len` elements of piece `piece` from `start`.
+struct Chunk {
+    int32_t piece;
+    int32_t len;
+    int64_t start;
+};
+
+}  // namespace zs
+
+struct zs_plan {
+    int32_t layout;
+    int32_t world;
+    int32_t rank;
+    int32_t align;
+    int64_t T;  // padded flat length (PER_TENSOR: sum of T_i)
+    int64_t S;  // owned elements (PER_TENSOR: sum of S_i)
+    std::vector<zs::TensorEntry> tensors;
+    std::vector<zs::Chunk> chunks;  // multi-tensor chunk list of the owned pieces
+};
+
+namespace zs {
+
+#ifndef ZS_CHUNK_ELEMS
+#define ZS_CHUNK_ELEMS 4096
+#endif
+// Multi-tensor chunk length (elements): one block per chunk.
+constexpr int32_t kChunkElems = ZS_CHUNK_ELEMS;
+
+// Device-side multi-tensor table, stored at the start of the workspace.
+struct MultiHeader {
+    uint64_t magic;
+    int32_t n_pieces;
+    int32_t n_chunks;
+    int32_t n_contribs;
+    int32_t flags;
+    int64_t pieces_off;    // byte offset of PieceDev[n_pieces]
+    int64_t contribs_off;  // byte offset of const void*[n_pieces * n_contribs]
+    int64_t chunks_off;    // byte offset of Chunk[n_chunks]
+};
+
+struct PieceDev {
+    void* grad;
+    float* master;
+    float* m;
+    float* v;
+    void* param;
+    void* full_own;  // gathered tensor + r*S_i (already offset)
+    int64_t len;     // S_i
+};
+
+enum MultiFlags : int32_t {
+    kHasGrad = 1,
+    kHasState = 2,
+    kHasParam = 4,
+    kHasFull = 8,
+    kHasContribs = 16,
+};
+
+constexpr uint64_t kMultiMagic = 0x7A734D554C544931ull;
+
+// Launchers (zs_kernels.hip). They return a hipError_t value cast to int.
+int launch_reduce(const void* const* contribs, int n, void* grad, int64_t len, void* stream);
+int launch_adamw(const AdamCoef& c, const void* grad, float* master, float* m, float* v,
+                 void* param, int64_t len, void* stream);
+int launch_gather(const void* param, void* full_at_own, int64_t len, void* stream);
+int launch_fused(const AdamCoef& c, const void* const* contribs, int n, float* master, float* m,
+                 float* v, void* grad, void* param, void* full_at_own, int64_t len, void* stream);
+
+enum MultiOp : int32_t { kOpReduce = 0, kOpAdamw = 1, kOpGather = 2, kOpFused = 3 };
+int launch_multi(int op, const AdamCoef* c, const void* workspace, int n_chunks, int n_contribs,
+                 int flags, void* stream);
+int copy_h2d_sync(void* dst, const void* src, int64_t bytes, void* stream);
+const char* hip_error_text(int err);
+
+}  // namespace zs

@@ -1,0 +1,493 @@
+// HIP kernels of the shard-local step for CDNA4 (gfx950).
+//
+// Everything here is a pure HBM stream: per owned element the step reads
+// 2N + 14 bytes and writes 14 (fused: 2N + 12 read, 14 written), with about
+// 25 fp32 operations, so no kernel is compute-bound and none uses MFMA.
+// Design points:
+//   * 64-lane wavefronts, 256-thread blocks, one tile per block: the grid
+//     covers the shard once and the hardware dispatches blocks in order, so
+//     the resident blocks stream a compact window that advances through
+//     every array (DRAM row locality).
+//   * Kernels that mix bf16 and fp32 arrays give each lane 4 consecutive
+//     elements: fp32 arrays move as one 16-byte dwordx4 per lane, bf16 arrays
+//     as one 8-byte dwordx2; every wave-wide access is a contiguous, fully
+//     used 1 KiB / 512 B span. bf16-only kernels give each lane 8 elements
+//     (one dwordx4).
+//   * Read-once data (the N contributions) and write-once data (the gathered
+//     buffer) use nontemporal loads/stores so they do not evict anything.
+//   * The rank loop is unrolled for the common world sizes (template N); any
+//     other N up to ZS_MAX_CONTRIBS runs a runtime loop.
+//   * The element arithmetic is the IEEE fp32 sequence of the C ABI contract,
+//     compiled with -ffp-contract=off: no FMA contraction, correctly rounded
+//     division and square root (the HIP defaults), denormals kept.
+#include <hip/hip_runtime.h>
+
+#include "zs_internal.h"
+
+namespace zs {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBlock = 256;
+
+// ------------------------------------------------------------------ bf16
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, IEEE round to nearest even; NaN -> quiet NaN, sign kept.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? ((u >> 16) | 0x40u) : r;
+}
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) { return bf16_rne(a) | (bf16_rne(b) << 16); }
+
+// ------------------------------------------------------------------ AdamW element
+
+__device__ __forceinline__ void adamw_elem(const AdamCoef& c, float gf, float& w, float& m, float& v) {
+    float wd = w * c.decay;
+    float mn = c.b1 * m + c.omb1 * gf;
+    float vn = c.b2 * v + c.omb2 * (gf * gf);
+    float mh = mn / c.bc1;
+    float vh = vn / c.bc2;
+    float den = sqrtf(vh) + c.eps;
+    w = wd - c.lr * (mh / den);
+    m = mn;
+    v = vn;
+}
+
+// ------------------------------------------------------------------ memory helpers
+
+template <typename T>
+__device__ __forceinline__ T ld_nt(const T* p) { return __builtin_nontemporal_load(p); }
+template <typename T>
+__device__ __forceinline__ void st_nt(T* p, T x) { __builtin_nontemporal_store(x, p); }
+
+template <int CAP>
+struct Ptrs {
+    const void* p[CAP];
+};
+
+// ------------------------------------------------------------------ rank sums
+//
+// The N contributions of a lane's units are summed in fp32, one add at a time
+// in rank order 0..N-1 starting from +0. Loads are issued a group of G ranks
+// at a time for all U units of the lane before any of them is consumed, so
+// every lane keeps G*U independent loads in flight (a plain rank loop makes
+// the compiler wait for each load before issuing the next).
+
+template <typename V>
+struct Lanes;
+template <>
+struct Lanes<u32x2> {
+    static constexpr int E = 4;  // bf16 elements per vector
+};
+template <>
+struct Lanes<u32x4> {
+    static constexpr int E = 8;
+};
+
+template <typename V>
+__device__ __forceinline__ void acc_add(float* a, const V& x) {
+    a[0] = a[0] + lo_bf16(x.x);
+    a[1] = a[1] + hi_bf16(x.x);
+    a[2] = a[2] + lo_bf16(x.y);
+    a[3] = a[3] + hi_bf16(x.y);
+    if constexpr (Lanes<V>::E == 8) {
+        a[4] = a[4] + lo_bf16(x.z);
+        a[5] = a[5] + hi_bf16(x.z);
+        a[6] = a[6] + lo_bf16(x.w);
+        a[7] = a[7] + hi_bf16(x.w);
+    }
+}
+
+// Adds ranks [q0, q0 + G) into a[k][*] for the U units u[k] with ok[k].
+template <typename V, int U, int G>
+__device__ __forceinline__ void sum_group(const void* const* p, int q0, const int64_t* u, const bool* ok,
+                                          float (*a)[Lanes<V>::E]) {
+    V x[G][U];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+            if (ok[k]) x[g][k] = ld_nt(reinterpret_cast<const V*>(p[q0 + g]) + u[k]);
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+            if (ok[k]) acc_add<V>(a[k], x[g][k]);
+}
+
+// Full rank sum: compile-time N in groups of min(N, GMAX); runtime N in
+// groups of 4 plus a remainder loop.
+template <typename V, int U, int N, int GMAX>
+__device__ __forceinline__ void rank_sum(const void* const* p, int n_rt, const int64_t* u, const bool* ok,
+                                         float (*a)[Lanes<V>::E]) {
+#pragma unroll
+    for (int k = 0; k < U; ++k)
+#pragma unroll
+        for (int e = 0; e < Lanes<V>::E; ++e) a[k][e] = 0.0f;
+    if constexpr (N > 0) {
+        constexpr int G = N < GMAX ? N : GMAX;
+        static_assert(N % G == 0, "world sizes with compiled loops are powers of two");
+#pragma unroll
+        for (int q0 = 0; q0 < N; q0 += G) sum_group<V, U, G>(p, q0, u, ok, a);
+    } else {
+        int q0 = 0;
+        for (; q0 + 4 <= n_rt; q0 += 4) sum_group<V, U, 4>(p, q0, u, ok, a);
+        for (; q0 < n_rt; ++q0) sum_group<V, U, 1>(p, q0, u, ok, a);
+    }
+}
+
+// The average: one division by N (compile-time N: a division by a power of
+// two, which the compiler turns into the exact multiplication by 1/N).
+template <int N>
+__device__ __forceinline__ float div_n(float x, float nf) {
+    if constexpr (N > 0)
+        return x / (float)N;
+    else
+        return x / nf;
+}
+
+// ------------------------------------------------------------------ reduce
+
+// grad[j] = bf16(avg_q contrib_q[j]); each lane owns U units of 8 elements.
+template <int N, int CAP, int U>
+__global__ __launch_bounds__(kBlock) void k_reduce(Ptrs<CAP> cp, int n_rt, float nf,
+                                                   u32x4* __restrict__ out, int64_t n8) {
+    {  // one tile of kBlock * U units per block; the grid covers the shard once
+        const int64_t base = (int64_t)blockIdx.x * kBlock * U + threadIdx.x;
+        int64_t u[U];
+        bool ok[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            u[k] = base + (int64_t)k * kBlock;
+            ok[k] = u[k] < n8;
+        }
+        float a[U][8];
+        rank_sum<u32x4, U, N, 8>(cp.p, n_rt, u, ok, a);
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            if (!ok[k]) continue;
+            u32x4 o;
+            o.x = pack2(div_n<N>(a[k][0], nf), div_n<N>(a[k][1], nf));
+            o.y = pack2(div_n<N>(a[k][2], nf), div_n<N>(a[k][3], nf));
+            o.z = pack2(div_n<N>(a[k][4], nf), div_n<N>(a[k][5], nf));
+            o.w = pack2(div_n<N>(a[k][6], nf), div_n<N>(a[k][7], nf));
+            out[u[k]] = o;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ AdamW
+
+__device__ __forceinline__ void adamw_unit(const AdamCoef& c, u32x2 g, f32x4& w, f32x4& m, f32x4& v) {
+    float w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
+    float m0 = m.x, m1 = m.y, m2 = m.z, m3 = m.w;
+    float v0 = v.x, v1 = v.y, v2 = v.z, v3 = v.w;
+    adamw_elem(c, lo_bf16(g.x), w0, m0, v0);
+    adamw_elem(c, hi_bf16(g.x), w1, m1, v1);
+    adamw_elem(c, lo_bf16(g.y), w2, m2, v2);
+    adamw_elem(c, hi_bf16(g.y), w3, m3, v3);
+    w = f32x4{w0, w1, w2, w3};
+    m = f32x4{m0, m1, m2, m3};
+    v = f32x4{v0, v1, v2, v3};
+}
+
+__device__ __forceinline__ u32x2 to_bf16x4(const f32x4& w) {
+    u32x2 p;
+    p.x = pack2(w.x, w.y);
+    p.y = pack2(w.z, w.w);
+    return p;
+}
+
+template <int U>
+__global__ __launch_bounds__(kBlock) void k_adamw(AdamCoef c, const u32x2* __restrict__ g,
+                                                  f32x4* __restrict__ master, f32x4* __restrict__ m,
+                                                  f32x4* __restrict__ v, u32x2* __restrict__ param,
+                                                  int64_t n4) {
+    {  // one tile of kBlock * U units per block; the grid covers the shard once
+        const int64_t base = (int64_t)blockIdx.x * kBlock * U + threadIdx.x;
+        u32x2 gv[U];
+        f32x4 wv[U], mv[U], vv[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int64_t u = base + (int64_t)k * kBlock;
+            if (u < n4) {
+                gv[k] = ld_nt(g + u);
+                wv[k] = ld_nt(master + u);
+                mv[k] = ld_nt(m + u);
+                vv[k] = ld_nt(v + u);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int64_t u = base + (int64_t)k * kBlock;
+            if (u < n4) {
+                adamw_unit(c, gv[k], wv[k], mv[k], vv[k]);
+                st_nt(master + u, wv[k]);
+                st_nt(m + u, mv[k]);
+                st_nt(v + u, vv[k]);
+                st_nt(param + u, to_bf16x4(wv[k]));
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ gather
+
+__global__ __launch_bounds__(kBlock) void k_gather(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                   int64_t n8) {
+    const int64_t u = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (u < n8) st_nt(dst + u, ld_nt(src + u));
+}
+
+// ------------------------------------------------------------------ fused
+
+// reduce + AdamW + gather write per 4-element unit. grad, param and full are
+// optional (nullptr: skipped; the test is uniform across the grid).
+template <int N, int CAP, int U>
+__global__ __launch_bounds__(kBlock) void k_fused(AdamCoef c, Ptrs<CAP> cp, int n_rt, float nf,
+                                                  f32x4* __restrict__ master, f32x4* __restrict__ m,
+                                                  f32x4* __restrict__ v, u32x2* __restrict__ grad,
+                                                  u32x2* __restrict__ param, u32x2* __restrict__ full,
+                                                  int64_t n4) {
+    {  // one tile of kBlock * U units per block; the grid covers the shard once
+        const int64_t base = (int64_t)blockIdx.x * kBlock * U + threadIdx.x;
+        int64_t u[U];
+        bool ok[U];
+        f32x4 wv[U], mv[U], vv[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            u[k] = base + (int64_t)k * kBlock;
+            ok[k] = u[k] < n4;
+            if (ok[k]) {
+                wv[k] = ld_nt(master + u[k]);
+                mv[k] = ld_nt(m + u[k]);
+                vv[k] = ld_nt(v + u[k]);
+            }
+        }
+        float a[U][4];
+        rank_sum<u32x2, U, N, 8>(cp.p, n_rt, u, ok, a);
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            if (!ok[k]) continue;
+            u32x2 g;
+            g.x = pack2(div_n<N>(a[k][0], nf), div_n<N>(a[k][1], nf));
+            g.y = pack2(div_n<N>(a[k][2], nf), div_n<N>(a[k][3], nf));
+            adamw_unit(c, g, wv[k], mv[k], vv[k]);
+            st_nt(master + u[k], wv[k]);
+            st_nt(m + u[k], mv[k]);
+            st_nt(v + u[k], vv[k]);
+            const u32x2 p = to_bf16x4(wv[k]);
+            if (grad) st_nt(grad + u[k], g);
+            if (param) st_nt(param + u[k], p);
+            if (full) st_nt(full + u[k], p);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ multi-tensor
+
+// One block per chunk. The chunk's piece supplies every pointer; contribs
+// of piece i are cps[i * N .. i * N + N).
+template <int OP, int N>
+__global__ __launch_bounds__(kBlock) void k_multi(AdamCoef c, const MultiHeader* __restrict__ hdr,
+                                                  int n_rt, float nf) {
+    const Chunk ch = reinterpret_cast<const Chunk*>(reinterpret_cast<const char*>(hdr) + hdr->chunks_off)[blockIdx.x];
+    const PieceDev pc = reinterpret_cast<const PieceDev*>(reinterpret_cast<const char*>(hdr) + hdr->pieces_off)[ch.piece];
+    const int flags = hdr->flags;
+    const void* const* cps = reinterpret_cast<const void* const*>(reinterpret_cast<const char*>(hdr) + hdr->contribs_off) +
+                             (int64_t)ch.piece * (N > 0 ? N : n_rt);
+    const int64_t u0 = ch.start >> 2;  // chunk start and length are multiples of 8
+    const int64_t nu = ch.len >> 2;
+    for (int64_t t = threadIdx.x; t < nu; t += kBlock) {
+        const int64_t u = u0 + t;
+        if (OP == kOpGather) {
+            st_nt(reinterpret_cast<u32x2*>(pc.full_own) + u, ld_nt(reinterpret_cast<const u32x2*>(pc.param) + u));
+            continue;
+        }
+        u32x2 g;
+        if (OP == kOpReduce || OP == kOpFused) {
+            const int64_t uu[1] = {u};
+            const bool ok[1] = {true};
+            float a[1][4];
+            rank_sum<u32x2, 1, N, 8>(cps, n_rt, uu, ok, a);
+            g.x = pack2(div_n<N>(a[0][0], nf), div_n<N>(a[0][1], nf));
+            g.y = pack2(div_n<N>(a[0][2], nf), div_n<N>(a[0][3], nf));
+            if (OP == kOpReduce) {
+                st_nt(reinterpret_cast<u32x2*>(pc.grad) + u, g);
+                continue;
+            }
+        } else {
+            g = ld_nt(reinterpret_cast<const u32x2*>(pc.grad) + u);
+        }
+        f32x4 w = ld_nt(reinterpret_cast<const f32x4*>(pc.master) + u);
+        f32x4 m = ld_nt(reinterpret_cast<const f32x4*>(pc.m) + u);
+        f32x4 v = ld_nt(reinterpret_cast<const f32x4*>(pc.v) + u);
+        adamw_unit(c, g, w, m, v);
+        st_nt(reinterpret_cast<f32x4*>(pc.master) + u, w);
+        st_nt(reinterpret_cast<f32x4*>(pc.m) + u, m);
+        st_nt(reinterpret_cast<f32x4*>(pc.v) + u, v);
+        const u32x2 p = to_bf16x4(w);
+        if (OP == kOpFused && (flags & kHasGrad)) st_nt(reinterpret_cast<u32x2*>(pc.grad) + u, g);
+        if (flags & kHasParam) st_nt(reinterpret_cast<u32x2*>(pc.param) + u, p);
+        if (OP == kOpFused && (flags & kHasFull)) st_nt(reinterpret_cast<u32x2*>(pc.full_own) + u, p);
+    }
+}
+
+// ------------------------------------------------------------------ launch helpers
+
+// Grid of a tile launch: one block per tile of kBlock * per_thread units.
+// Blocks are dispatched in index order, so the blocks resident at any moment
+// stream one compact, advancing window of each array (good DRAM row
+// locality); a persistent grid-stride grid spreads its blocks over the whole
+// array and measured ~25% slower on MI355X.
+unsigned grid_for(int64_t units, int per_thread) {
+    const int64_t per_block = (int64_t)kBlock * per_thread;
+    int64_t blocks = (units + per_block - 1) / per_block;
+    if (blocks < 1) blocks = 1;
+    return (unsigned)blocks;
+}
+
+// Launch shape: units of work per lane. Overridable at build time for sweeps.
+#ifndef ZS_REDUCE_U
+#define ZS_REDUCE_U 1
+#endif
+#ifndef ZS_ADAMW_U
+#define ZS_ADAMW_U 1
+#endif
+#ifndef ZS_FUSED_U
+#define ZS_FUSED_U 1
+#endif
+constexpr int kReduceU = ZS_REDUCE_U;
+constexpr int kAdamwU = ZS_ADAMW_U;
+constexpr int kFusedU = ZS_FUSED_U;
+
+template <int N, int CAP>
+int launch_reduce_t(const void* const* contribs, int n, void* grad, int64_t len, hipStream_t s) {
+    Ptrs<CAP> cp{};
+    for (int q = 0; q < n; ++q) cp.p[q] = contribs[q];
+    const int64_t n8 = len / 8;
+    hipLaunchKernelGGL((k_reduce<N, CAP, kReduceU>), dim3(grid_for(n8, kReduceU)), dim3(kBlock), 0, s,
+                       cp, n, (float)n, reinterpret_cast<u32x4*>(grad), n8);
+    return (int)hipGetLastError();
+}
+
+template <int N, int CAP>
+int launch_fused_t(const AdamCoef& c, const void* const* contribs, int n, float* master, float* m,
+                   float* v, void* grad, void* param, void* full, int64_t len, hipStream_t s) {
+    Ptrs<CAP> cp{};
+    for (int q = 0; q < n; ++q) cp.p[q] = contribs[q];
+    const int64_t n4 = len / 4;
+    hipLaunchKernelGGL((k_fused<N, CAP, kFusedU>), dim3(grid_for(n4, kFusedU)), dim3(kBlock), 0, s, c,
+                       cp, n, (float)n, reinterpret_cast<f32x4*>(master), reinterpret_cast<f32x4*>(m),
+                       reinterpret_cast<f32x4*>(v), reinterpret_cast<u32x2*>(grad),
+                       reinterpret_cast<u32x2*>(param), reinterpret_cast<u32x2*>(full), n4);
+    return (int)hipGetLastError();
+}
+
+template <int OP, int N>
+int launch_multi_t(const AdamCoef& c, const void* ws, int n_chunks, int n, hipStream_t s) {
+    hipLaunchKernelGGL((k_multi<OP, N>), dim3((unsigned)n_chunks), dim3(kBlock), 0, s, c,
+                       reinterpret_cast<const MultiHeader*>(ws), n, (float)n);
+    return (int)hipGetLastError();
+}
+
+template <int OP>
+int launch_multi_op(const AdamCoef& c, const void* ws, int n_chunks, int n, hipStream_t s) {
+    switch (n) {
+        case 1: return launch_multi_t<OP, 1>(c, ws, n_chunks, n, s);
+        case 2: return launch_multi_t<OP, 2>(c, ws, n_chunks, n, s);
+        case 4: return launch_multi_t<OP, 4>(c, ws, n_chunks, n, s);
+        case 8: return launch_multi_t<OP, 8>(c, ws, n_chunks, n, s);
+        case 16: return launch_multi_t<OP, 16>(c, ws, n_chunks, n, s);
+        case 32: return launch_multi_t<OP, 32>(c, ws, n_chunks, n, s);
+        case 64: return launch_multi_t<OP, 64>(c, ws, n_chunks, n, s);
+        default: return launch_multi_t<OP, 0>(c, ws, n_chunks, n, s);
+    }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ public launchers
+
+int launch_reduce(const void* const* contribs, int n, void* grad, int64_t len, void* stream) {
+    if (len <= 0) return 0;
+    hipStream_t s = (hipStream_t)stream;
+    switch (n) {
+        case 1: return launch_reduce_t<1, 1>(contribs, n, grad, len, s);
+        case 2: return launch_reduce_t<2, 2>(contribs, n, grad, len, s);
+        case 4: return launch_reduce_t<4, 4>(contribs, n, grad, len, s);
+        case 8: return launch_reduce_t<8, 8>(contribs, n, grad, len, s);
+        case 16: return launch_reduce_t<16, 16>(contribs, n, grad, len, s);
+        case 32: return launch_reduce_t<32, 32>(contribs, n, grad, len, s);
+        case 64: return launch_reduce_t<64, 64>(contribs, n, grad, len, s);
+        default: return launch_reduce_t<0, ZS_MAX_CONTRIBS>(contribs, n, grad, len, s);
+    }
+}
+
+int launch_adamw(const AdamCoef& c, const void* grad, float* master, float* m, float* v, void* param,
+                 int64_t len, void* stream) {
+    if (len <= 0) return 0;
+    const int64_t n4 = len / 4;
+    hipLaunchKernelGGL((k_adamw<kAdamwU>), dim3(grid_for(n4, kAdamwU)), dim3(kBlock), 0,
+                       (hipStream_t)stream, c, reinterpret_cast<const u32x2*>(grad),
+                       reinterpret_cast<f32x4*>(master), reinterpret_cast<f32x4*>(m),
+                       reinterpret_cast<f32x4*>(v), reinterpret_cast<u32x2*>(param), n4);
+    return (int)hipGetLastError();
+}
+
+int launch_gather(const void* param, void* full_at_own, int64_t len, void* stream) {
+    if (len <= 0) return 0;
+    const int64_t n8 = len / 8;
+    hipLaunchKernelGGL(k_gather, dim3(grid_for(n8, 1)), dim3(kBlock), 0, (hipStream_t)stream,
+                       reinterpret_cast<const u32x4*>(param), reinterpret_cast<u32x4*>(full_at_own), n8);
+    return (int)hipGetLastError();
+}
+
+int launch_fused(const AdamCoef& c, const void* const* contribs, int n, float* master, float* m, float* v,
+                 void* grad, void* param, void* full_at_own, int64_t len, void* stream) {
+    if (len <= 0) return 0;
+    hipStream_t s = (hipStream_t)stream;
+    switch (n) {
+        case 1: return launch_fused_t<1, 1>(c, contribs, n, master, m, v, grad, param, full_at_own, len, s);
+        case 2: return launch_fused_t<2, 2>(c, contribs, n, master, m, v, grad, param, full_at_own, len, s);
+        case 4: return launch_fused_t<4, 4>(c, contribs, n, master, m, v, grad, param, full_at_own, len, s);
+        case 8: return launch_fused_t<8, 8>(c, contribs, n, master, m, v, grad, param, full_at_own, len, s);
+        case 16: return launch_fused_t<16, 16>(c, contribs, n, master, m, v, grad, param, full_at_own, len, s);
+        case 32: return launch_fused_t<32, 32>(c, contribs, n, master, m, v, grad, param, full_at_own, len, s);
+        case 64: return launch_fused_t<64, 64>(c, contribs, n, master, m, v, grad, param, full_at_own, len, s);
+        default:
+            return launch_fused_t<0, ZS_MAX_CONTRIBS>(c, contribs, n, master, m, v, grad, param, full_at_own, len, s);
+    }
+}
+
+int launch_multi(int op, const AdamCoef* c, const void* workspace, int n_chunks, int n_contribs, int flags,
+                 void* stream) {
+    (void)flags;
+    if (n_chunks <= 0) return 0;
+    const AdamCoef cc = c ? *c : AdamCoef{};
+    hipStream_t s = (hipStream_t)stream;
+    switch (op) {
+        case kOpReduce: return launch_multi_op<kOpReduce>(cc, workspace, n_chunks, n_contribs, s);
+        case kOpAdamw: return launch_multi_t<kOpAdamw, 1>(cc, workspace, n_chunks, 1, s);
+        case kOpGather: return launch_multi_t<kOpGather, 1>(cc, workspace, n_chunks, 1, s);
+        default: return launch_multi_op<kOpFused>(cc, workspace, n_chunks, n_contribs, s);
+    }
+}
+
+int copy_h2d_sync(void* dst, const void* src, int64_t bytes, void* stream) {
+    hipError_t e = hipMemcpyAsync(dst, src, (size_t)bytes, hipMemcpyHostToDevice, (hipStream_t)stream);
+    if (e != hipSuccess) return (int)e;
+    return (int)hipStreamSynchronize((hipStream_t)stream);
+}
+
+const char* hip_error_text(int err) { return hipGetErrorString((hipError_t)err); }
+
+}  // namespace zs

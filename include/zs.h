@@ -1,0 +1,228 @@
+/*
+ * zs.h -- C ABI of one rank's shard-local step of ZeRO / FSDP data parallelism
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The step (sources: the four pages on ZeRO and FSDP):
+ *   1. plan    flatten the model's tensors into one flat buffer (FSDP's
+ *              FlatParameter: "ZeRO vs FSDP: A Rigorous Dissection for
+ *              Distributed Training Engineers", section 3.2) or shard each
+ *              tensor on its own (FSDP2's per-parameter sharding, "从 Data
+ *              Parallel 到 ZeRO/FSDP", section "ZeRO 与 FSDP 的关系"); pad and
+ *              cut into N equal shards, rank r owning shard r ("ZeRO vs FSDP...",
+ *              section 2).
+ *   2. reduce  average the N ranks' bf16 gradient contributions for the owned
+ *              shard, the slice a reduce-scatter leaves on rank r ("ZeRO vs
+ *              FSDP...", section 2.1; "从 Data Parallel 到 ZeRO/FSDP", sections
+ *              "Data Parallel 保证的数学语义" and "DDP 为什么单卡仍是 16P").
+ *   3. AdamW   mixed-precision AdamW on the owned shard's 16 bytes/param of
+ *              persistent state: bf16 param, bf16 grad, fp32 master, m and v
+ *              ("FSDP2's parameter lifecycle, and the wrap-policy bug...",
+ *              section "16 bytes per parameter is where planning starts";
+ *              "ZeRO vs FSDP...", section 1.1).
+ *   4. gather  write the updated bf16 shard into the full gathered parameter
+ *              buffer at its offset, this rank's part of the all-gather
+ *              ("ZeRO vs FSDP...", section 2.1; "从 Data Parallel 到 ZeRO/FSDP",
+ *              section "ZeRO Stage 1").
+ *
+ * Arithmetic of steps 2-3, per owned element j (fp32 IEEE operations, one
+ * rounding each, in this order; bf16 narrowing is round-to-nearest-even):
+ *   acc = +0; for q in 0..N-1: acc += f32(contrib_q[j]);  g = bf16(acc / N)
+ *   gf = f32(g); w = master*(1-lr*wd); m = b1*m + (1-b1)*gf;
+ *   v = b2*v + (1-b2)*(gf*gf); mhat = m/(1-b1^t); vhat = v/(1-b2^t);
+ *   w = w - lr*(mhat/(sqrt(vhat)+eps)); master = w; param = bf16(w)
+ * The scalars (1-b1, 1-lr*wd, 1-b1^t, ...) are computed in double on the
+ * host and rounded once to fp32.
+ *
+ * Memory: every device buffer is owned by the caller (normally a PyTorch
+ * tensor); the library never allocates, frees or retains device memory. A
+ * plan is owned by the library between zs_shard_plan and zs_plan_destroy,
+ * is immutable, and may be shared between threads.
+ *
+ * Dtypes are fixed: contributions, gradients and parameters are bf16 (raw
+ * 16-bit patterns), master/m/v are fp32. Every device pointer must be 16-byte
+ * aligned.
+ *
+ * Execution: every zs_* call that touches device memory only validates its
+ * arguments on the host and enqueues kernels on `stream` (a hipStream_t; NULL
+ * is the default stream). It never synchronizes; a device-side fault is seen
+ * at the caller's next synchronization. Calls on different streams that
+ * write the same memory race.
+ *
+ * Errors: a call that returns anything but ZS_OK has enqueued nothing and
+ * changed nothing; zs_last_error() then returns a thread-local description.
+ */
+#ifndef ZS_H
+#define ZS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Largest number of gradient contributions (world size) one call accepts. */
+#define ZS_MAX_CONTRIBS 256
+
+typedef enum zs_status {
+    ZS_OK = 0,
+    ZS_EINVAL = -1, /* bad argument: NULL, out of range, inconsistent sizes */
+    ZS_EALIGN = -2, /* a device pointer is not 16-byte aligned */
+    ZS_ERANGE = -3, /* bucket [off, off+len) outside the owned shard or not a multiple of 8 */
+    ZS_EHIP = -4,   /* the HIP runtime refused a launch or a copy */
+    ZS_ENOMEM = -5  /* host allocation failed, or a workspace is too small */
+} zs_status;
+
+typedef enum zs_layout {
+    ZS_LAYOUT_FLAT = 0,      /* one flat buffer, cut into N equal shards */
+    ZS_LAYOUT_PER_TENSOR = 1 /* every tensor padded and cut into N pieces on its own */
+} zs_layout;
+
+typedef struct zs_plan zs_plan;
+
+/* AdamW hyperparameters of one step. step is t >= 1 (bias corrections use
+ * beta^t); all doubles must be finite, 0 <= beta1, beta2 < 1, eps >= 0. */
+typedef struct zs_adamw_hparams {
+    double lr;
+    double beta1;
+    double beta2;
+    double eps;
+    double weight_decay;
+    int64_t step;
+} zs_adamw_hparams;
+
+/* Where tensor i sits in a plan. Coordinates are elements.
+ *   FLAT:       flat_off = start of tensor i in the flat buffer
+ *               (a multiple of tensor_align_elems); padded_numel = numel.
+ *   PER_TENSOR: flat_off = start of padded tensor i in the packed gathered
+ *               buffer (tensors back to back); padded_numel = T_i =
+ *               roundup(numel, 8*N).
+ * own_lo/own_hi: the owned range of tensor i in tensor-local coordinates
+ * (FLAT: clipped to the real elements; PER_TENSOR: [r*S_i, (r+1)*S_i),
+ * which may cover padding). Empty when own_lo == own_hi.
+ * shard_off: start of that range in the rank's packed shard. */
+typedef struct zs_tensor_info {
+    int64_t numel;
+    int64_t flat_off;
+    int64_t padded_numel;
+    int64_t own_lo;
+    int64_t own_hi;
+    int64_t shard_off;
+} zs_tensor_info;
+
+/* ------------------------------------------------------------------ plan */
+
+/* Builds the shard plan of n_tensors tensors (numels[i] >= 0 elements each,
+ * in flatten order) for rank `rank` of `world_size`.
+ *   FLAT: tensor i starts at off_i = roundup(off_{i-1} + numel_{i-1},
+ *   tensor_align_elems); the flat length T = roundup(end of last tensor,
+ *   8*N) so the shards are equal and whole 16-byte vectors; S = T/N; rank r
+ *   owns [r*S, (r+1)*S).
+ *   PER_TENSOR: T_i = roundup(numel_i, 8*N), S_i = T_i/N, rank r owns
+ *   [r*S_i, (r+1)*S_i) of tensor i; the rank's packed shard concatenates
+ *   its pieces (S = sum S_i) and the packed gathered buffer concatenates the
+ *   padded tensors (T = sum T_i). tensor_align_elems is ignored.
+ * Padding elements are part of the shards; they hold +0 and stay +0 under
+ * the step when their contributions are +0.
+ * Host only. On success *out owns a new plan; on error *out is untouched. */
+zs_status zs_shard_plan(const int64_t* numels, int32_t n_tensors, int32_t world_size, int32_t rank,
+                        int32_t tensor_align_elems, int32_t layout, zs_plan** out);
+void zs_plan_destroy(zs_plan* plan);
+
+/* Queries (host only; a NULL plan gives -1). */
+int64_t zs_plan_padded_numel(const zs_plan* plan);     /* T */
+int64_t zs_plan_shard_numel(const zs_plan* plan);      /* S */
+int64_t zs_plan_persistent_bytes(const zs_plan* plan); /* 16*S: the per-rank ledger */
+int32_t zs_plan_num_tensors(const zs_plan* plan);
+int32_t zs_plan_world_size(const zs_plan* plan);
+int32_t zs_plan_rank(const zs_plan* plan);
+int32_t zs_plan_layout(const zs_plan* plan);
+zs_status zs_plan_tensor(const zs_plan* plan, int32_t i, zs_tensor_info* out);
+
+/* ------------------------------------------------------------------ flat step
+ * In these calls the rank's shard is one packed buffer of S elements.
+ * contribs is a HOST array of n_contribs device pointers; contribs[q] is rank
+ * q's bf16 gradient for this rank's shard, S elements, element j belonging
+ * to global index r*S + j (FLAT). n_contribs must equal the plan's world
+ * size, 1 <= N <= ZS_MAX_CONTRIBS. full_bf16 is the gathered parameter
+ * buffer of T elements; only [r*S, (r+1)*S) is written. */
+
+/* Averaged reduce of the bucket [off, off+len) of the shard (reduce-scatter
+ * bucketed as gradients become ready: "从 Data Parallel 到 ZeRO/FSDP", section
+ * "ReduceScatter 必须尽早释放 Gradient"). Writes grad_bf16[off, off+len).
+ * off and len must be multiples of 8 with off + len <= S; len == 0 does
+ * nothing. Buckets give the same bytes as one call over the whole shard. */
+zs_status zs_reduce_shard(const zs_plan* plan, const void* const* contribs, int32_t n_contribs,
+                          void* grad_bf16, int64_t off, int64_t len, void* stream);
+
+/* AdamW over the S owned elements: reads grad_bf16, updates master, m, v in
+ * place and writes param_bf16 = bf16(master). */
+zs_status zs_adamw_shard_step(const zs_plan* plan, const zs_adamw_hparams* hp, const void* grad_bf16,
+                              float* master, float* m, float* v, void* param_bf16, void* stream);
+
+/* full_bf16[r*S + j] = param_bf16[j] for j < S. FLAT plans only. */
+zs_status zs_gather_params(const zs_plan* plan, const void* param_bf16, void* full_bf16,
+                           void* stream);
+
+/* reduce + AdamW + gather in one pass over the shard, bit-identical to
+ * zs_reduce_shard over the whole shard, then zs_adamw_shard_step, then
+ * zs_gather_params. grad_bf16, param_bf16 and full_bf16 are each optional
+ * (NULL: not written); full_bf16 requires a FLAT plan. */
+zs_status zs_fused_shard_step(const zs_plan* plan, const zs_adamw_hparams* hp,
+                              const void* const* contribs, int32_t n_contribs, float* master,
+                              float* m, float* v, void* grad_bf16, void* param_bf16,
+                              void* full_bf16, void* stream);
+
+/* ------------------------------------------------------------------ multi-tensor
+ * Multi-tensor apply over the owned pieces of a PER_TENSOR plan whose
+ * per-tensor state lives in separate allocations (FSDP2's per-parameter
+ * sharding with one unit per Linear or norm: "FSDP2's parameter lifecycle...",
+ * section "Wrap granularity is the lever"). One launch covers every piece,
+ * however small.
+ *
+ * zs_multi_bind writes a device table of the pieces' pointers and a
+ * chunk list into a caller-allocated device workspace of at least
+ * zs_multi_workspace_bytes(plan, n_contribs) bytes. It enqueues one
+ * host-to-device copy on `stream` and then synchronizes that stream, so the
+ * host arrays may be freed on return. The per-step calls then read only the
+ * workspace; rebind when any pointer changes. Pieces of zero length are
+ * skipped. A NULL field disables that read or write for every piece (all
+ * pieces must agree on which fields are NULL). */
+typedef struct zs_piece_ptrs {
+    void* grad;    /* bf16 [S_i]: reduce output, AdamW input */
+    float* master; /* fp32 [S_i] */
+    float* m;      /* fp32 [S_i] */
+    float* v;      /* fp32 [S_i] */
+    void* param;   /* bf16 [S_i]: updated bf16 shard piece, or NULL */
+    void* full;    /* bf16 [T_i]: gathered tensor i (written at [r*S_i, (r+1)*S_i)), or NULL */
+} zs_piece_ptrs;
+
+int64_t zs_multi_workspace_bytes(const zs_plan* plan, int32_t n_contribs);
+
+/* pieces: host array of zs_plan_num_tensors(plan) records. contribs: host
+ * array of n_contribs * num_tensors device pointers, contribs[q*n_tensors+i]
+ * = rank q's bf16 gradient piece of tensor i (S_i elements), or NULL when
+ * n_contribs == 0 (no reduce possible on this binding). */
+zs_status zs_multi_bind(const zs_plan* plan, const zs_piece_ptrs* pieces, const void* const* contribs,
+                        int32_t n_contribs, void* workspace, int64_t workspace_bytes, void* stream);
+
+zs_status zs_reduce_shard_multi(const zs_plan* plan, const void* workspace, void* stream);
+zs_status zs_adamw_shard_step_multi(const zs_plan* plan, const zs_adamw_hparams* hp,
+                                    const void* workspace, void* stream);
+zs_status zs_gather_params_multi(const zs_plan* plan, const void* workspace, void* stream);
+/* reduce + AdamW + gather for every piece in one launch; writes grad, param
+ * and full only where those fields were bound non-NULL. */
+zs_status zs_fused_shard_step_multi(const zs_plan* plan, const zs_adamw_hparams* hp,
+                                    const void* workspace, void* stream);
+
+/* ------------------------------------------------------------------ misc */
+
+/* Thread-local text describing the last non-OK status of this thread. */
+const char* zs_last_error(void);
+/* Library version, "major.minor.patch". */
+const char* zs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZS_H */

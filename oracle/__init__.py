@@ -142,8 +142,10 @@ def shard_step(hp, contribs, g, master, m, v, p, full, rank, lo=0, hi=None):
                          _p16(full) if full is not None else None, S, rank, lo, hi)
 
 
-def time_shard_step(hp, contribs, g, master, m, v, p, full, rank, nthreads, reps):
-    """Wall-clock seconds of ``reps`` whole-window shard steps over all of g's elements."""
+def time_shard_step(hp, contribs, g, master, m, v, p, full, nthreads, reps):
+    """Wall-clock seconds of ``reps`` whole-window shard steps over all of g's
+    elements, split over ``nthreads`` host threads; the window is rank 0's, so
+    its gather writes full[0:len(g)]."""
     S = g.size
     secs = (ctypes.c_double * reps)()
     rc = lib().ora_time_shard_step(_p32(hp.coef()), _contrib_table(contribs), len(contribs),

@@ -1,0 +1,157 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, its host-only planner matches the oracle's plan integer for
+integer, and argument validation rejects bad calls before any launch."""
+import ctypes
+import os
+import random
+import re
+
+import pytest
+
+from oracle.plan import plan_flat, plan_per_tensor
+from synth import shapes
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zs.h")
+
+
+@pytest.fixture(scope="module")
+def zs():
+    lib = os.path.join(ROOT, "fsdp_sharded_mixed_flatten_amd", "libzs.so")
+    if not os.path.exists(lib):
+        from fsdp_sharded_mixed_flatten_amd import build as b  # noqa: F401 -- only when nothing is built
+    import importlib
+    try:
+        mod = importlib.import_module("fsdp_sharded_mixed_flatten_amd")
+    except ImportError:
+        import subprocess
+        import sys
+        subprocess.run([sys.executable, os.path.join(ROOT, "fsdp_sharded_mixed_flatten_amd", "build.py")],
+                       check=True)
+        mod = importlib.import_module("fsdp_sharded_mixed_flatten_amd")
+    return mod
+
+
+def test_exports_every_declared_symbol(zs):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"\b(zs_[a-z0-9_]+)\s*\(", text))
+    assert len(declared) >= 20
+    raw = ctypes.CDLL(zs.LIB_PATH)
+    missing = [s for s in sorted(declared) if not hasattr(raw, s)]
+    assert not missing, missing
+    assert declared == set(zs.EXPORTED)
+
+
+def _compare_plan(zs, numels, world, rank, align, layout):
+    p = zs.zs_shard_plan(numels, world, rank, align, layout)
+    o = plan_flat(numels, world, rank, align) if layout == zs.ZS_LAYOUT_FLAT else plan_per_tensor(numels, world, rank)
+    assert (p.padded_numel, p.shard_numel, p.persistent_bytes) == (o.T, o.S, o.persistent_bytes)
+    assert p.num_tensors == len(numels) and p.world_size == world and p.rank == rank
+    by_tensor = {pc.tensor: pc for pc in o.pieces}
+    for i in range(len(numels)):
+        info = p.tensor(i)
+        assert info.numel == numels[i]
+        assert info.flat_off == o.offsets[i]
+        if layout == zs.ZS_LAYOUT_PER_TENSOR:
+            assert info.padded_numel == o.padded[i]
+        pc = by_tensor.get(i)
+        if pc is None:
+            assert info.own_lo == info.own_hi
+        else:
+            assert (info.own_lo, info.own_hi, info.shard_off) == (pc.own_lo, pc.own_hi, pc.shard_off)
+    p.close()
+
+
+@pytest.mark.parametrize("name,fn,world,align", [
+    ("tiny", shapes.tiny, 4, 1), ("qwen3b", shapes.qwen25_3b, 4, 128),
+    ("llama7b", shapes.llama_7b, 8, 128), ("llama70b", shapes.llama_70b, 64, 128)])
+def test_plan_matches_oracle_on_model_shapes(zs, name, fn, world, align):
+    for rank in sorted({0, 1, world - 1}):
+        _compare_plan(zs, fn(), world, rank, align, zs.ZS_LAYOUT_FLAT)
+        _compare_plan(zs, fn(), world, rank, 1, zs.ZS_LAYOUT_PER_TENSOR)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_plan_matches_oracle_random(zs, seed):
+    rnd = random.Random(seed)
+    numels = [rnd.choice([0, 1, 5, 8, 9, 64, 100, 768, 4093, 65536, 100_003]) for _ in range(rnd.randint(0, 15))]
+    world = rnd.choice([1, 2, 3, 4, 5, 7, 8, 16, 64, 100, 256])
+    rank = rnd.randrange(world)
+    align = rnd.choice([1, 2, 4, 8, 64, 128])
+    _compare_plan(zs, numels, world, rank, align, zs.ZS_LAYOUT_FLAT)
+    _compare_plan(zs, numels, world, rank, align, zs.ZS_LAYOUT_PER_TENSOR)
+
+
+def test_plan_rejects_bad_arguments(zs):
+    for args in (([10], 0, 0, 1, 0), ([10], 4, 4, 1, 0), ([10], 4, -1, 1, 0), ([10], 4, 0, 0, 0),
+                 ([-1], 4, 0, 1, 0), ([10], 4, 0, 1, 7)):
+        with pytest.raises(zs.ZsError) as e:
+            zs.zs_shard_plan(*args)
+        assert e.value.status == zs.ZS_EINVAL and e.value.message
+
+
+def test_empty_plan(zs):
+    p = zs.zs_shard_plan([], 4, 0)
+    assert p.padded_numel == 0 and p.shard_numel == 0 and p.persistent_bytes == 0
+
+
+# Device entry points with bad arguments must return before touching the
+# device; fake 16-byte-aligned addresses are fine because nothing is launched.
+FAKE = 1 << 40
+
+
+def test_validation_without_device(zs):
+    L = zs.lib()
+    plan = zs.zs_shard_plan([1000], 4, 1)
+    h = plan.handle
+    vp = ctypes.c_void_p
+    good = (vp * 4)(FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288)
+    hp = zs.AdamWHParams()
+
+    def st(fn, *a):
+        return fn(*a)
+
+    # wrong number of contributions, NULL contribution, misaligned contribution
+    assert st(L.zs_reduce_shard, h, good, 3, FAKE, 0, 8, None) == zs.ZS_EINVAL
+    bad = (vp * 4)(FAKE, None, FAKE, FAKE)
+    assert st(L.zs_reduce_shard, h, bad, 4, FAKE, 0, 8, None) == zs.ZS_EINVAL
+    assert "contribs[1]" in zs.zs_last_error()
+    mis = (vp * 4)(FAKE, FAKE + 2, FAKE, FAKE)
+    assert st(L.zs_reduce_shard, h, mis, 4, FAKE, 0, 8, None) == zs.ZS_EALIGN
+    # bucket out of range / not a multiple of 8
+    S = plan.shard_numel
+    assert st(L.zs_reduce_shard, h, good, 4, FAKE, 0, S + 8, None) == zs.ZS_ERANGE
+    assert st(L.zs_reduce_shard, h, good, 4, FAKE, 4, 8, None) == zs.ZS_ERANGE
+    assert st(L.zs_reduce_shard, h, good, 4, FAKE, -8, 8, None) == zs.ZS_ERANGE
+    # empty bucket is a no-op that succeeds without launching
+    assert st(L.zs_reduce_shard, h, good, 4, FAKE, 8, 0, None) == zs.ZS_OK
+    # hyperparameters
+    for bad_hp in (zs.AdamWHParams(step=0), zs.AdamWHParams(beta1=1.0), zs.AdamWHParams(eps=-1.0),
+                   zs.AdamWHParams(lr=float("nan")), zs.AdamWHParams(weight_decay=float("inf"))):
+        assert L.zs_adamw_shard_step(h, ctypes.byref(bad_hp), FAKE, FAKE, FAKE, FAKE, FAKE, None) == zs.ZS_EINVAL
+    assert L.zs_adamw_shard_step(h, ctypes.byref(hp), FAKE, None, FAKE, FAKE, FAKE, None) == zs.ZS_EINVAL
+    assert L.zs_adamw_shard_step(h, ctypes.byref(hp), FAKE, FAKE + 8, FAKE, FAKE, FAKE, None) == zs.ZS_EALIGN
+    assert L.zs_gather_params(h, FAKE, None, None) == zs.ZS_EINVAL
+    assert L.zs_fused_shard_step(h, ctypes.byref(hp), good, 4, FAKE, FAKE, FAKE, FAKE + 1, None, None, None) == zs.ZS_EALIGN
+    assert L.zs_plan_shard_numel(None) == -1
+
+
+def test_multi_validation_without_device(zs):
+    L = zs.lib()
+    flat = zs.zs_shard_plan([4096, 512], 8, 0)
+    assert zs.zs_multi_workspace_bytes.__name__  # binding present
+    assert L.zs_multi_workspace_bytes(flat.handle, 8) == -1
+    pt = zs.zs_shard_plan([4096, 512], 8, 0, 1, zs.ZS_LAYOUT_PER_TENSOR)
+    need = L.zs_multi_workspace_bytes(pt.handle, 8)
+    assert need > 0 and need % 256 == 0
+    recs = (zs.PiecePtrs * 2)()
+    # too-small workspace
+    assert L.zs_multi_bind(pt.handle, recs, None, 0, FAKE, 16, None) == zs.ZS_ENOMEM
+    # a step on a workspace that was never bound
+    assert L.zs_adamw_shard_step_multi(pt.handle, ctypes.byref(zs.AdamWHParams()), FAKE, None) == zs.ZS_EINVAL
+    assert "never bound" in zs.zs_last_error()
+    # partial master/m/v
+    recs[0] = zs.PiecePtrs(FAKE, FAKE, None, FAKE, None, None)
+    assert L.zs_multi_bind(pt.handle, recs, None, 0, FAKE, need, None) == zs.ZS_EINVAL
+    # flat plans have no multi-tensor form
+    assert L.zs_gather_params_multi(flat.handle, FAKE, None) == zs.ZS_EINVAL

@@ -1,0 +1,382 @@
+"""GPU <-> oracle parity at sizes the oracle covers element by element.
+
+Every case builds its inputs on the host from the seeded generator (padding
+positions +0), copies them to the device, runs the HIP path through the C
+ABI and compares every output element with the CPU oracle: fp32 master/m/v
+within relative 1e-6 (exact where the oracle is 0), bf16 grad/param/gathered
+values within 1 ulp, untouched memory bit-identical. The path mirrors the
+oracle's operation order, so the tests also count elements that are not
+bit-identical and require that count to be zero.
+"""
+import random
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import check_bf16, check_f32, dev16, dev32, host16, host32
+
+pytestmark = pytest.mark.gpu
+
+SENT = 0x5A5A  # sentinel for memory the step must not touch
+
+
+@pytest.fixture(scope="module")
+def zs():
+    import torch
+
+    import fsdp_sharded_mixed_flatten_amd as m
+    torch.cuda.init()
+    return m
+
+
+def _flat_inputs(numels, world, align, steps, seed, zero_prob=0.0, tail_prob=0.0):
+    plan = oracle.plan_flat(numels, world, 0, align)
+    T = plan.T
+    pad = np.frombuffer(bytes(plan.padding_mask_full()), dtype=np.uint8).astype(bool)
+    master = synth.cpu_f32(T, 0, synth.spec(seed, synth.STREAM_MASTER, 0, 0.02))
+    master[pad] = 0
+    contribs = {}
+    for t in range(1, steps + 1):
+        cs = []
+        for q in range(world):
+            c = synth.cpu_bf16(T, 0, synth.spec(seed, synth.STREAM_CONTRIB + q, t, 1e-3, 2**62, 0.1,
+                                                tail_prob, zero_prob))
+            c[pad] = 0
+            cs.append(c)
+        contribs[t] = cs
+    return T, master, contribs
+
+
+class FlatRun:
+    """Oracle and GPU state of one rank over several steps of a FLAT plan."""
+
+    def __init__(self, zs, numels, world, rank, align, steps, seed, hp, bucket=0, fused=False,
+                 zero_prob=0.0, tail_prob=0.0):
+        import torch
+        self.zs = zs
+        self.plan = zs.zs_shard_plan(numels, world, rank, align, zs.ZS_LAYOUT_FLAT)
+        T, S = self.plan.padded_numel, self.plan.shard_numel
+        self.T, self.S, self.rank, self.world = T, S, rank, world
+        T2, master, contribs = _flat_inputs(numels, world, align, steps, seed, zero_prob, tail_prob)
+        assert T2 == T
+        lo = rank * S
+        self.mine = {t: [c[lo:lo + S].copy() for c in cs] for t, cs in contribs.items()}
+        self.hp = hp
+        self.bucket = bucket
+        self.fused = fused
+        # oracle state
+        self.o = dict(g=np.zeros(S, np.uint16), master=master[lo:lo + S].copy(),
+                      m=np.zeros(S, np.float32), v=np.zeros(S, np.float32), p=np.zeros(S, np.uint16),
+                      full=np.full(T, SENT, np.uint16))
+        # device state, with a guard band after each buffer
+        G = 64
+        self.G = G
+
+        def guarded32(a):
+            return dev32(np.concatenate([a, np.full(G, 7.0, np.float32)]))
+
+        def guarded16(a):
+            return dev16(np.concatenate([a, np.full(G, SENT, np.uint16)]))
+
+        self.d = dict(g=guarded16(np.zeros(S, np.uint16)), master=guarded32(self.o["master"]),
+                      m=guarded32(np.zeros(S, np.float32)), v=guarded32(np.zeros(S, np.float32)),
+                      p=guarded16(np.zeros(S, np.uint16)), full=guarded16(np.full(T, SENT, np.uint16)))
+        self.dc = {t: [dev16(c) for c in cs] for t, cs in self.mine.items()}
+        torch.cuda.synchronize()
+
+    def step(self, t):
+        zs, d, hp = self.zs, self.d, self.hp.at(t)
+        S = self.S
+        if self.fused:
+            zs.zs_fused_shard_step(self.plan, hp, self.dc[t], d["master"], d["m"], d["v"],
+                                   grad=d["g"], param=d["p"], full=d["full"])
+        else:
+            B = self.bucket or max(S, 8)
+            for off in range(0, S, B):
+                zs.zs_reduce_shard(self.plan, self.dc[t], d["g"], off, min(B, S - off))
+            zs.zs_adamw_shard_step(self.plan, hp, d["g"], d["master"], d["m"], d["v"], d["p"])
+            zs.zs_gather_params(self.plan, d["p"], d["full"])
+        o = self.o
+        oracle.shard_step(oracle.HParams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, t),
+                          self.mine[t], o["g"], o["master"], o["m"], o["v"], o["p"], o["full"], self.rank)
+
+    def check(self, exact=True):
+        import torch
+        torch.cuda.synchronize()
+        S, T, G = self.S, self.T, self.G
+        d, o = self.d, self.o
+        diffs = {}
+        diffs["g"] = check_bf16(host16(d["g"])[:S], o["g"], "grad")
+        diffs["master"] = check_f32(host32(d["master"])[:S], o["master"], "master")
+        diffs["m"] = check_f32(host32(d["m"])[:S], o["m"], "m")
+        diffs["v"] = check_f32(host32(d["v"])[:S], o["v"], "v")
+        diffs["p"] = check_bf16(host16(d["p"])[:S], o["p"], "param")
+        full = host16(d["full"])
+        # placement in the gathered buffer and every untouched byte: bit-exact
+        assert np.array_equal(full[:T], o["full"]), "gathered buffer differs"
+        for k in ("g", "p", "full"):
+            assert np.all(host16(d[k])[-G:] == SENT), f"guard band after {k} overwritten"
+        for k in ("master", "m", "v"):
+            assert np.all(host32(d[k])[-G:] == 7.0), f"guard band after {k} overwritten"
+        if exact:
+            assert not any(diffs.values()), f"not bit-identical: {diffs}"
+        return diffs
+
+
+def _hp(zs, **kw):
+    base = dict(lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1)
+    base.update(kw)
+    return zs.AdamWHParams(**base)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_tiny_config_three_steps(zs, fused):
+    """1,000,003-element param padded to N*8, N=4, rank 1, 3 AdamW steps."""
+    run = FlatRun(zs, [1_000_003], 4, 1, 1, 3, synth.DEFAULT_SEED, _hp(zs), bucket=65536, fused=fused)
+    for t in (1, 2, 3):
+        run.step(t)
+        run.check()
+
+
+def test_tiny_all_ranks_equal_unsharded_update(zs):
+    """Sharding invariance on the GPU: N ranks' gathered updates == DDP update."""
+    import torch
+    numels, N, steps = [1_000_003], 4, 2
+    T, master, contribs = _flat_inputs(numels, N, 1, steps, 99)
+    hp = _hp(zs)
+    plans = [zs.zs_shard_plan(numels, N, r, 1) for r in range(N)]
+    S = plans[0].shard_numel
+    full = dev16(np.full(T, SENT, np.uint16))
+    st = [dict(master=dev32(master[r * S:(r + 1) * S]), m=torch.zeros(S, device="cuda"),
+               v=torch.zeros(S, device="cuda")) for r in range(N)]
+    for t in range(1, steps + 1):
+        for r in range(N):
+            mine = [dev16(c[r * S:(r + 1) * S]) for c in contribs[t]]
+            zs.zs_fused_shard_step(plans[r], hp.at(t), mine, st[r]["master"], st[r]["m"], st[r]["v"],
+                                   full=full)
+    # DDP reference: every replica reduces the full buffers and updates all of it
+    g = np.zeros(T, np.uint16)
+    mo, mm, mv, mp = master.copy(), np.zeros(T, np.float32), np.zeros(T, np.float32), np.zeros(T, np.uint16)
+    for t in range(1, steps + 1):
+        oracle.reduce(contribs[t], out=g)
+        oracle.adamw(oracle.HParams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, t), g, mo, mm, mv, mp)
+    torch.cuda.synchronize()
+    assert np.array_equal(host16(full), mp)
+    got_master = np.concatenate([host32(s["master"]) for s in st])
+    assert check_f32(got_master, mo, "master") == 0
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_flat_plans(zs, seed):
+    """Alignment gaps, tail padding, odd world sizes (runtime-N kernels), ragged buckets."""
+    rnd = random.Random(seed)
+    numels = [rnd.choice([1, 7, 64, 100, 768, 4093, 20_000, 65_537]) for _ in range(rnd.randint(1, 8))]
+    world = rnd.choice([1, 2, 3, 4, 5, 8, 16, 32, 64, 100])
+    rank = rnd.randrange(world)
+    align = rnd.choice([1, 8, 128])
+    plan = oracle.plan_flat(numels, world, rank, align)
+    if plan.S == 0:
+        pytest.skip("empty shard")
+    bucket = rnd.choice([0, 8, 4096, 8 * rnd.randint(1, 4000)])
+    fused = rnd.random() < 0.5
+    hp = _hp(zs, lr=rnd.choice([1e-4, 1e-3]), weight_decay=rnd.choice([0.0, 0.1]))
+    run = FlatRun(zs, numels, world, rank, align, 2, 1000 + seed, hp, bucket=bucket, fused=fused,
+                  zero_prob=0.05)
+    for t in (1, 2):
+        run.step(t)
+    run.check()
+
+
+@pytest.mark.parametrize("N", [1, 2, 4, 8, 16, 32, 64, 3, 7, 256])
+def test_world_sizes(zs, N):
+    """Every compiled rank-loop variant (N = 1..64) and the runtime loop."""
+    rank = N - 1 if N <= 100 else N // 2  # a rank that owns real elements and some padding
+    for fused in (False, True):
+        run = FlatRun(zs, [50_001], N, rank, 1, 1, 7 + N, _hp(zs), fused=fused)
+        run.step(1)
+        run.check()
+
+
+def test_fused_equals_unfused_bit_exact(zs):
+    a = FlatRun(zs, [300_017, 5], 8, 3, 128, 3, 5, _hp(zs), bucket=8192, fused=False)
+    b = FlatRun(zs, [300_017, 5], 8, 3, 128, 3, 5, _hp(zs), fused=True)
+    for t in (1, 2, 3):
+        a.step(t)
+        b.step(t)
+    for k in ("g", "master", "m", "v", "p", "full"):
+        assert np.array_equal(a.d[k].cpu().numpy(), b.d[k].cpu().numpy()), k
+
+
+def test_edge_values(zs):
+    """Signed zeros, subnormals, huge values, inf and NaN in the contributions."""
+    import torch
+    S, N = 4096, 4
+    plan = zs.zs_shard_plan([S * N], N, 0, 1)
+    rng = np.random.default_rng(3)
+    specials = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x7F7F, 0xFF7F,
+                         0x7F80, 0xFF80, 0x7FC0, 0x3F80, 0xBF80, 0x1234, 0x9234, 0x4000], np.uint16)
+    cs = [rng.choice(specials, S).astype(np.uint16) for _ in range(N)]
+    master = rng.standard_normal(S).astype(np.float32) * 0.02
+    master[:16] = [0, -0.0, 1e-45, -1e-45, 3e38, -3e38, 1e-38, np.inf, -np.inf, np.nan, 1, -1, 2, 0.5, 1e-30, 7]
+    hp = _hp(zs, lr=1e-3)
+    d_m, d_v = torch.zeros(S, device="cuda"), torch.zeros(S, device="cuda")
+    d_master = dev32(master)
+    d_g, d_p = dev16(np.zeros(S, np.uint16)), dev16(np.zeros(S, np.uint16))
+    zs.zs_fused_shard_step(plan, hp, [dev16(c) for c in cs], d_master, d_m, d_v, grad=d_g, param=d_p)
+    g = oracle.reduce(cs)
+    m, v, p = np.zeros(S, np.float32), np.zeros(S, np.float32), np.zeros(S, np.uint16)
+    mo = master.copy()
+    oracle.adamw(oracle.HParams(1e-3, 0.9, 0.95, 1e-8, 0.1, 1), g, mo, m, v, p)
+    torch.cuda.synchronize()
+    nd = check_bf16(host16(d_g), g, "grad")
+    nd += check_f32(host32(d_master), mo, "master")
+    nd += check_f32(host32(d_m), m, "m")
+    nd += check_f32(host32(d_v), v, "v")
+    nd += check_bf16(host16(d_p), p, "param")
+    assert nd == 0, f"{nd} non-NaN elements not bit-identical"
+    assert np.isnan(mo).sum() > 100  # the case does exercise NaN propagation
+
+
+def test_empty_and_minimal_shards(zs):
+    import torch
+    hp = _hp(zs)
+    empty = zs.zs_shard_plan([], 4, 0)
+    z = torch.zeros(8, device="cuda")
+    z16 = torch.zeros(8, dtype=torch.int16, device="cuda")
+    zs.zs_fused_shard_step(empty, hp, [z16] * 4, z, z, z, grad=z16, param=z16, full=z16)
+    zs.zs_adamw_shard_step(empty, hp, z16, z, z, z, z16)
+    zs.zs_gather_params(empty, z16, z16)
+    run = FlatRun(zs, [3], 1, 0, 1, 2, 4, hp, fused=False)  # S = 8: one vector, 5 of it padding
+    run.step(1)
+    run.step(2)
+    run.check()
+    torch.cuda.synchronize()
+
+
+def test_error_paths_on_device_buffers(zs):
+    import torch
+    plan = zs.zs_shard_plan([1024], 4, 0)
+    S = plan.shard_numel
+    cs = [torch.zeros(S, dtype=torch.int16, device="cuda") for _ in range(4)]
+    g = torch.zeros(S + 8, dtype=torch.int16, device="cuda")
+    with pytest.raises(zs.ZsError) as e:
+        zs.zs_reduce_shard(plan, cs[:3], g)
+    assert e.value.status == zs.ZS_EINVAL
+    with pytest.raises(zs.ZsError) as e:
+        zs.zs_reduce_shard(plan, cs, g[1:], 0, S)  # 2-byte misaligned output
+    assert e.value.status == zs.ZS_EALIGN
+    with pytest.raises(zs.ZsError) as e:
+        zs.zs_reduce_shard(plan, cs, g, 8, S)  # bucket beyond the shard
+    assert e.value.status in (zs.ZS_ERANGE,)
+    with pytest.raises(ValueError):
+        zs.zs_reduce_shard(plan, [c[:8] for c in cs], g)  # too short for the call
+    bad = zs.AdamWHParams(step=0)
+    with pytest.raises(zs.ZsError):
+        zs.zs_adamw_shard_step(plan, bad, g, torch.zeros(S, device="cuda"), torch.zeros(S, device="cuda"),
+                               torch.zeros(S, device="cuda"), g)
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- multi-tensor
+
+
+def _small_model(H=256, I=688, V=1000, L=2):
+    sizes = [V * H]
+    for _ in range(L):
+        sizes += [H * H, H * H, H * H, H * H, I * H, I * H, H * I, H, H]
+    sizes += [H, V * H, 1000, 3]  # plus two sizes that need per-tensor padding
+    return sizes
+
+
+class MultiRun:
+    def __init__(self, zs, numels, world, rank, steps, seed, hp):
+        import torch
+        self.zs, self.hp, self.world, self.rank = zs, hp, world, rank
+        self.plan = zs.zs_shard_plan(numels, world, rank, 1, zs.ZS_LAYOUT_PER_TENSOR)
+        self.oplan = oracle.plan_per_tensor(numels, world, rank)
+        self.pieces = []
+        self.o = []
+        self.contribs = {}
+        for i, pc in enumerate(self.oplan.pieces):
+            Si = pc.own_hi - pc.own_lo
+            base = pc.full_off  # packed global index of the piece's first element
+            valid = self.oplan.offsets[i] + numels[i]
+            master = synth.cpu_f32(Si, base, synth.spec(seed, synth.STREAM_MASTER, 0, 0.02, valid))
+            self.o.append(dict(g=np.zeros(Si, np.uint16), master=master.copy(), m=np.zeros(Si, np.float32),
+                               v=np.zeros(Si, np.float32), p=np.zeros(Si, np.uint16),
+                               full=np.full(self.oplan.padded[i], SENT, np.uint16)))
+            self.pieces.append(dict(grad=torch.zeros(Si, dtype=torch.int16, device="cuda"), master=dev32(master),
+                                    m=torch.zeros(Si, device="cuda"), v=torch.zeros(Si, device="cuda"),
+                                    param=torch.zeros(Si, dtype=torch.int16, device="cuda"),
+                                    full=dev16(np.full(self.oplan.padded[i], SENT, np.uint16))))
+            for t in range(1, steps + 1):
+                for q in range(world):
+                    c = synth.cpu_bf16(Si, base, synth.spec(seed, synth.STREAM_CONTRIB + q, t, 1e-3, valid))
+                    self.contribs.setdefault(t, [[None] * len(numels) for _ in range(world)])[q][i] = c
+        self.dcontribs = {t: [[dev16(c) for c in row] for row in cs] for t, cs in self.contribs.items()}
+        nbytes = zs.zs_multi_workspace_bytes(self.plan, world)
+        self.ws = {t: torch.zeros(nbytes, dtype=torch.uint8, device="cuda") for t in self.contribs}
+        for t in self.contribs:
+            zs.zs_multi_bind(self.plan, self.pieces, self.dcontribs[t], self.ws[t])
+
+    def step(self, t, fused):
+        zs = self.zs
+        hp = self.hp.at(t)
+        if fused:
+            zs.zs_fused_shard_step_multi(self.plan, hp, self.ws[t])
+        else:
+            zs.zs_reduce_shard_multi(self.plan, self.ws[t])
+            zs.zs_adamw_shard_step_multi(self.plan, hp, self.ws[t])
+            zs.zs_gather_params_multi(self.plan, self.ws[t])
+        h = oracle.HParams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, t)
+        for i, pc in enumerate(self.oplan.pieces):
+            o = self.o[i]
+            if o["g"].size == 0:
+                continue
+            cs = [self.contribs[t][q][i] for q in range(self.world)]
+            oracle.reduce(cs, out=o["g"])
+            oracle.adamw(h, o["g"], o["master"], o["m"], o["v"], o["p"])
+            o["full"][pc.own_lo:pc.own_hi] = o["p"]
+
+    def check(self):
+        import torch
+        torch.cuda.synchronize()
+        nd = 0
+        for i, (o, d) in enumerate(zip(self.o, self.pieces)):
+            nd += check_bf16(host16(d["grad"]), o["g"], f"grad[{i}]")
+            nd += check_f32(host32(d["master"]), o["master"], f"master[{i}]")
+            nd += check_f32(host32(d["m"]), o["m"], f"m[{i}]")
+            nd += check_f32(host32(d["v"]), o["v"], f"v[{i}]")
+            nd += check_bf16(host16(d["param"]), o["p"], f"param[{i}]")
+            assert np.array_equal(host16(d["full"]), o["full"]), f"gathered tensor {i}"
+        assert nd == 0, f"{nd} elements not bit-identical"
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_multi_tensor_apply(zs, fused):
+    run = MultiRun(zs, _small_model(), 8, 3, 2, 77, _hp(zs))
+    for t in (1, 2):
+        run.step(t, fused)
+        run.check()
+
+
+def test_multi_tensor_runtime_world(zs):
+    run = MultiRun(zs, _small_model(H=128, I=344, V=300, L=1), 5, 4, 1, 78, _hp(zs))
+    run.step(1, True)
+    run.check()
+
+
+def test_generator_gpu_equals_host(zs):
+    import torch
+    n = 1_000_003
+    for sp in (synth.spec(3, synth.STREAM_MASTER, 0, 0.02, n - 5),
+               synth.spec(3, synth.STREAM_CONTRIB + 5, 2, 1e-3, 2**62, 0.1, 0.001, 0.01)):
+        a = torch.empty(n, dtype=torch.float32, device="cuda")
+        synth.gpu_f32(a, 12345, sp)
+        b = torch.empty(n, dtype=torch.int16, device="cuda")
+        synth.gpu_bf16(b, 12345, sp)
+        torch.cuda.synchronize()
+        assert np.array_equal(host32(a).view(np.uint32), synth.cpu_f32(n, 12345, sp).view(np.uint32))
+        assert np.array_equal(host16(b), synth.cpu_bf16(n, 12345, sp))
