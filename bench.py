@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-window", type=int, default=25_000_000,
                     help="owned elements of the CPU oracle's timed window")
+    ap.add_argument("--arena-pad-kb", type=int, default=-1,
+                    help="allocate the N contributions (and master/m/v) as rows of one buffer whose "
+                         "rows start this many KiB apart beyond their length (-1: separate tensors)")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
     return ap.parse_args()
@@ -89,19 +92,31 @@ class Timer:
         return [s.elapsed_time(e) for s, e in self.pairs]
 
 
-def flat_setup(zs, synth, wl):
+def rows(n_rows, S, dtype, pad_kb):
+    """n_rows buffers of S elements: separate tensors (pad_kb < 0) or rows of
+    one allocation whose starts are S*itemsize + pad_kb KiB apart."""
+    import torch
+    if pad_kb < 0:
+        return [torch.empty(S, dtype=dtype, device="cuda") for _ in range(n_rows)]
+    item = torch.empty(0, dtype=dtype).element_size()
+    pitch = S + pad_kb * 1024 // item
+    arena = torch.empty(n_rows * pitch, dtype=dtype, device="cuda")
+    return [arena[r * pitch:r * pitch + S] for r in range(n_rows)]
+
+
+def flat_setup(zs, synth, wl, pad_kb=-1):
     import torch
     plan = zs.zs_shard_plan(wl.numels, wl.world, wl.rank, wl.align, zs.ZS_LAYOUT_FLAT)
     S, T = plan.shard_numel, plan.padded_numel
     base, valid = wl.rank * S, sum(wl.numels)
     st = {}
-    st["contribs"] = [torch.empty(S, dtype=torch.int16, device="cuda") for _ in range(wl.world)]
+    st["contribs"] = rows(wl.world, S, torch.int16, pad_kb)
     for q, c in enumerate(st["contribs"]):
         synth.gpu_bf16(c, base, wl.contrib_spec(q, 1, valid))
-    st["master"] = torch.empty(S, dtype=torch.float32, device="cuda")
+    st["master"], st["m"], st["v"] = rows(3, S, torch.float32, pad_kb)
     synth.gpu_f32(st["master"], base, wl.master_spec(valid))
-    st["m"] = torch.zeros(S, dtype=torch.float32, device="cuda")
-    st["v"] = torch.zeros(S, dtype=torch.float32, device="cuda")
+    st["m"].zero_()
+    st["v"].zero_()
     st["grad"] = torch.empty(S, dtype=torch.int16, device="cuda")
     st["param"] = torch.empty(S, dtype=torch.int16, device="cuda")
     free, _ = torch.cuda.mem_get_info()
@@ -227,7 +242,7 @@ def main():
         del a, b
 
     if wl.layout == "flat":
-        plan, st = flat_setup(zs, synth, wl)
+        plan, st = flat_setup(zs, synth, wl, args.arena_pad_kb)
         S = plan.shard_numel
         log(f"[bench] S={S:,} T={plan.padded_numel:,} gathered buffer {'full' if st['full_is_T'] else 'owned slice'}")
 

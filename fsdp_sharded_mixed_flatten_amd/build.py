@@ -39,7 +39,8 @@ def build(verbose=False, out=None, defines=()):
     os.makedirs(BUILD, exist_ok=True)
     objs = []
     api_o = os.path.join(BUILD, "zs_api.o")
-    _run(["g++", *COMMON, "-c", os.path.join(CSRC, "zs_api.cpp"), "-o", api_o], verbose)
+    _run(["g++", *COMMON, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, "zs_api.cpp"), "-o", api_o],
+         verbose)
     objs.append(api_o)
     ker_o = os.path.join(BUILD, "zs_kernels.o")
     _run([HIPCC, *COMMON, *HIP_ONLY, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, "zs_kernels.hip"),

@@ -47,11 +47,18 @@ struct zs_plan {
 
 namespace zs {
 
-#ifndef ZS_CHUNK_ELEMS
-#define ZS_CHUNK_ELEMS 4096
+// Launch shape shared by the host (chunk table) and the kernels. Overridable
+// at build time for sweeps.
+#ifndef ZS_BLOCK
+#define ZS_BLOCK 64
 #endif
-// Multi-tensor chunk length (elements): one block per chunk.
-constexpr int32_t kChunkElems = ZS_CHUNK_ELEMS;
+#ifndef ZS_MULTI_U
+#define ZS_MULTI_U 1
+#endif
+constexpr int kBlockThreads = ZS_BLOCK;  // threads per block of every kernel
+constexpr int kMultiU = ZS_MULTI_U;      // 4-element units per lane in a multi-tensor chunk
+// Multi-tensor chunk length (elements): one block per chunk, one tile each.
+constexpr int32_t kChunkElems = kBlockThreads * 4 * kMultiU;
 
 // Device-side multi-tensor table, stored at the start of the workspace.
 struct MultiHeader {

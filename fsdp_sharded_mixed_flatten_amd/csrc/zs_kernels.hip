@@ -31,7 +31,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBlock = 256;
+constexpr int kBlock = kBlockThreads;  // threads per block (zs_internal.h)
 
 // ------------------------------------------------------------------ bf16
 
@@ -67,6 +67,38 @@ template <typename T>
 __device__ __forceinline__ T ld_nt(const T* p) { return __builtin_nontemporal_load(p); }
 template <typename T>
 __device__ __forceinline__ void st_nt(T* p, T x) { __builtin_nontemporal_store(x, p); }
+
+// Cache policy per access class (build-time switches, 1 = nontemporal):
+// read-once inputs (contributions, the grad/param inputs of the unfused
+// kernels), the read-modify-write optimizer state, and write-once outputs.
+#ifndef ZS_NT_IN
+#define ZS_NT_IN 1
+#endif
+#ifndef ZS_NT_STATE_LD
+#define ZS_NT_STATE_LD 1
+#endif
+#ifndef ZS_NT_STATE_ST
+#define ZS_NT_STATE_ST 1
+#endif
+#ifndef ZS_NT_OUT
+#define ZS_NT_OUT 1
+#endif
+template <typename T>
+__device__ __forceinline__ T ld_in(const T* p) {
+    if constexpr (ZS_NT_IN) return ld_nt(p); else return *p;
+}
+template <typename T>
+__device__ __forceinline__ T ld_state(const T* p) {
+    if constexpr (ZS_NT_STATE_LD) return ld_nt(p); else return *p;
+}
+template <typename T>
+__device__ __forceinline__ void st_state(T* p, T x) {
+    if constexpr (ZS_NT_STATE_ST) st_nt(p, x); else *p = x;
+}
+template <typename T>
+__device__ __forceinline__ void st_out(T* p, T x) {
+    if constexpr (ZS_NT_OUT) st_nt(p, x); else *p = x;
+}
 
 template <int CAP>
 struct Ptrs {
@@ -115,13 +147,19 @@ __device__ __forceinline__ void sum_group(const void* const* p, int q0, const in
     for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int k = 0; k < U; ++k)
-            if (ok[k]) x[g][k] = ld_nt(reinterpret_cast<const V*>(p[q0 + g]) + u[k]);
+            if (ok[k]) x[g][k] = ld_in(reinterpret_cast<const V*>(p[q0 + g]) + u[k]);
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int k = 0; k < U; ++k)
             if (ok[k]) acc_add<V>(a[k], x[g][k]);
 }
+
+// Ranks whose loads a lane issues together.
+#ifndef ZS_GROUP
+#define ZS_GROUP 8
+#endif
+constexpr int kGroup = ZS_GROUP;
 
 // Full rank sum: compile-time N in groups of min(N, GMAX); runtime N in
 // groups of 4 plus a remainder loop.
@@ -170,7 +208,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce(Ptrs<CAP> cp, int n_rt, float
             ok[k] = u[k] < n8;
         }
         float a[U][8];
-        rank_sum<u32x4, U, N, 8>(cp.p, n_rt, u, ok, a);
+        rank_sum<u32x4, U, N, kGroup>(cp.p, n_rt, u, ok, a);
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             if (!ok[k]) continue;
@@ -179,7 +217,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce(Ptrs<CAP> cp, int n_rt, float
             o.y = pack2(div_n<N>(a[k][2], nf), div_n<N>(a[k][3], nf));
             o.z = pack2(div_n<N>(a[k][4], nf), div_n<N>(a[k][5], nf));
             o.w = pack2(div_n<N>(a[k][6], nf), div_n<N>(a[k][7], nf));
-            out[u[k]] = o;
+            st_out(out + u[k], o);
         }
     }
 }
@@ -219,10 +257,10 @@ __global__ __launch_bounds__(kBlock) void k_adamw(AdamCoef c, const u32x2* __res
         for (int k = 0; k < U; ++k) {
             const int64_t u = base + (int64_t)k * kBlock;
             if (u < n4) {
-                gv[k] = ld_nt(g + u);
-                wv[k] = ld_nt(master + u);
-                mv[k] = ld_nt(m + u);
-                vv[k] = ld_nt(v + u);
+                gv[k] = ld_in(g + u);
+                wv[k] = ld_state(master + u);
+                mv[k] = ld_state(m + u);
+                vv[k] = ld_state(v + u);
             }
         }
 #pragma unroll
@@ -230,10 +268,10 @@ __global__ __launch_bounds__(kBlock) void k_adamw(AdamCoef c, const u32x2* __res
             const int64_t u = base + (int64_t)k * kBlock;
             if (u < n4) {
                 adamw_unit(c, gv[k], wv[k], mv[k], vv[k]);
-                st_nt(master + u, wv[k]);
-                st_nt(m + u, mv[k]);
-                st_nt(v + u, vv[k]);
-                st_nt(param + u, to_bf16x4(wv[k]));
+                st_state(master + u, wv[k]);
+                st_state(m + u, mv[k]);
+                st_state(v + u, vv[k]);
+                st_out(param + u, to_bf16x4(wv[k]));
             }
         }
     }
@@ -244,100 +282,165 @@ __global__ __launch_bounds__(kBlock) void k_adamw(AdamCoef c, const u32x2* __res
 __global__ __launch_bounds__(kBlock) void k_gather(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                    int64_t n8) {
     const int64_t u = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (u < n8) st_nt(dst + u, ld_nt(src + u));
+    if (u < n8) st_out(dst + u, ld_in(src + u));
 }
 
 // ------------------------------------------------------------------ fused
 
-// reduce + AdamW + gather write per 4-element unit. grad, param and full are
-// optional (nullptr: skipped; the test is uniform across the grid).
+// One tile of reduce + AdamW + gather: U units of 4 elements per lane, the
+// lane's units at base, base + kBlock, ...; units at or past `limit` are
+// skipped. grad, param and full are optional (nullptr: not written; the
+// test is uniform across the block).
+template <int N, int U>
+__device__ __forceinline__ void fused_tile(const AdamCoef& c, const void* const* cp, int n_rt, float nf,
+                                           f32x4* __restrict__ master, f32x4* __restrict__ m,
+                                           f32x4* __restrict__ v, u32x2* __restrict__ grad,
+                                           u32x2* __restrict__ param, u32x2* __restrict__ full,
+                                           int64_t base, int64_t limit) {
+    int64_t u[U];
+    bool ok[U];
+    f32x4 wv[U], mv[U], vv[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        u[k] = base + (int64_t)k * kBlock;
+        ok[k] = u[k] < limit;
+        if (ok[k]) {
+            wv[k] = ld_state(master + u[k]);
+            mv[k] = ld_state(m + u[k]);
+            vv[k] = ld_state(v + u[k]);
+        }
+    }
+    float a[U][4];
+    rank_sum<u32x2, U, N, kGroup>(cp, n_rt, u, ok, a);
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        if (!ok[k]) continue;
+        u32x2 g;
+        g.x = pack2(div_n<N>(a[k][0], nf), div_n<N>(a[k][1], nf));
+        g.y = pack2(div_n<N>(a[k][2], nf), div_n<N>(a[k][3], nf));
+        adamw_unit(c, g, wv[k], mv[k], vv[k]);
+        st_state(master + u[k], wv[k]);
+        st_state(m + u[k], mv[k]);
+        st_state(v + u[k], vv[k]);
+        const u32x2 p = to_bf16x4(wv[k]);
+        if (grad) st_out(grad + u[k], g);
+        if (param) st_out(param + u[k], p);
+        if (full) st_out(full + u[k], p);
+    }
+}
+
 template <int N, int CAP, int U>
 __global__ __launch_bounds__(kBlock) void k_fused(AdamCoef c, Ptrs<CAP> cp, int n_rt, float nf,
                                                   f32x4* __restrict__ master, f32x4* __restrict__ m,
                                                   f32x4* __restrict__ v, u32x2* __restrict__ grad,
                                                   u32x2* __restrict__ param, u32x2* __restrict__ full,
                                                   int64_t n4) {
-    {  // one tile of kBlock * U units per block; the grid covers the shard once
-        const int64_t base = (int64_t)blockIdx.x * kBlock * U + threadIdx.x;
-        int64_t u[U];
-        bool ok[U];
-        f32x4 wv[U], mv[U], vv[U];
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-            u[k] = base + (int64_t)k * kBlock;
-            ok[k] = u[k] < n4;
-            if (ok[k]) {
-                wv[k] = ld_nt(master + u[k]);
-                mv[k] = ld_nt(m + u[k]);
-                vv[k] = ld_nt(v + u[k]);
-            }
-        }
-        float a[U][4];
-        rank_sum<u32x2, U, N, 8>(cp.p, n_rt, u, ok, a);
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-            if (!ok[k]) continue;
-            u32x2 g;
-            g.x = pack2(div_n<N>(a[k][0], nf), div_n<N>(a[k][1], nf));
-            g.y = pack2(div_n<N>(a[k][2], nf), div_n<N>(a[k][3], nf));
-            adamw_unit(c, g, wv[k], mv[k], vv[k]);
-            st_nt(master + u[k], wv[k]);
-            st_nt(m + u[k], mv[k]);
-            st_nt(v + u[k], vv[k]);
-            const u32x2 p = to_bf16x4(wv[k]);
-            if (grad) st_nt(grad + u[k], g);
-            if (param) st_nt(param + u[k], p);
-            if (full) st_nt(full + u[k], p);
-        }
-    }
+    // one tile of kBlock * U units per block; the grid covers the shard once
+    fused_tile<N, U>(c, cp.p, n_rt, nf, master, m, v, grad, param, full,
+                     (int64_t)blockIdx.x * kBlock * U + threadIdx.x, n4);
 }
 
 // ------------------------------------------------------------------ multi-tensor
 
-// One block per chunk. The chunk's piece supplies every pointer; contribs
-// of piece i are cps[i * N .. i * N + N).
+// Tiles of the unfused steps in 4-element units, for the multi-tensor kernel.
+template <int N, int U>
+__device__ __forceinline__ void reduce_tile(const void* const* cp, int n_rt, float nf, u32x2* __restrict__ out,
+                                            int64_t base, int64_t limit) {
+    int64_t u[U];
+    bool ok[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        u[k] = base + (int64_t)k * kBlock;
+        ok[k] = u[k] < limit;
+    }
+    float a[U][4];
+    rank_sum<u32x2, U, N, kGroup>(cp, n_rt, u, ok, a);
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        if (!ok[k]) continue;
+        u32x2 g;
+        g.x = pack2(div_n<N>(a[k][0], nf), div_n<N>(a[k][1], nf));
+        g.y = pack2(div_n<N>(a[k][2], nf), div_n<N>(a[k][3], nf));
+        st_out(out + u[k], g);
+    }
+}
+
+template <int U>
+__device__ __forceinline__ void adamw_tile(const AdamCoef& c, const u32x2* __restrict__ g, f32x4* __restrict__ master,
+                                           f32x4* __restrict__ m, f32x4* __restrict__ v, u32x2* __restrict__ param,
+                                           int64_t base, int64_t limit) {
+    u32x2 gv[U];
+    f32x4 wv[U], mv[U], vv[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const int64_t u = base + (int64_t)k * kBlock;
+        if (u < limit) {
+            gv[k] = ld_in(g + u);
+            wv[k] = ld_state(master + u);
+            mv[k] = ld_state(m + u);
+            vv[k] = ld_state(v + u);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const int64_t u = base + (int64_t)k * kBlock;
+        if (u < limit) {
+            adamw_unit(c, gv[k], wv[k], mv[k], vv[k]);
+            st_state(master + u, wv[k]);
+            st_state(m + u, mv[k]);
+            st_state(v + u, vv[k]);
+            if (param) st_out(param + u, to_bf16x4(wv[k]));
+        }
+    }
+}
+
+template <int U>
+__device__ __forceinline__ void copy_tile(const u32x2* __restrict__ src, u32x2* __restrict__ dst, int64_t base,
+                                          int64_t limit) {
+    u32x2 x[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const int64_t u = base + (int64_t)k * kBlock;
+        if (u < limit) x[k] = ld_in(src + u);
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const int64_t u = base + (int64_t)k * kBlock;
+        if (u < limit) st_out(dst + u, x[k]);
+    }
+}
+
+// One block per chunk; a chunk is one tile (kBlock lanes x kMultiU units of
+// 4 elements) of one piece. The piece supplies every pointer; the
+// contributions of piece i are cps[i * N .. i * N + N).
 template <int OP, int N>
 __global__ __launch_bounds__(kBlock) void k_multi(AdamCoef c, const MultiHeader* __restrict__ hdr,
                                                   int n_rt, float nf) {
-    const Chunk ch = reinterpret_cast<const Chunk*>(reinterpret_cast<const char*>(hdr) + hdr->chunks_off)[blockIdx.x];
-    const PieceDev pc = reinterpret_cast<const PieceDev*>(reinterpret_cast<const char*>(hdr) + hdr->pieces_off)[ch.piece];
+    const char* ws = reinterpret_cast<const char*>(hdr);
+    const Chunk ch = reinterpret_cast<const Chunk*>(ws + hdr->chunks_off)[blockIdx.x];
+    const PieceDev pc = reinterpret_cast<const PieceDev*>(ws + hdr->pieces_off)[ch.piece];
     const int flags = hdr->flags;
-    const void* const* cps = reinterpret_cast<const void* const*>(reinterpret_cast<const char*>(hdr) + hdr->contribs_off) +
-                             (int64_t)ch.piece * (N > 0 ? N : n_rt);
     const int64_t u0 = ch.start >> 2;  // chunk start and length are multiples of 8
-    const int64_t nu = ch.len >> 2;
-    for (int64_t t = threadIdx.x; t < nu; t += kBlock) {
-        const int64_t u = u0 + t;
-        if (OP == kOpGather) {
-            st_nt(reinterpret_cast<u32x2*>(pc.full_own) + u, ld_nt(reinterpret_cast<const u32x2*>(pc.param) + u));
-            continue;
-        }
-        u32x2 g;
-        if (OP == kOpReduce || OP == kOpFused) {
-            const int64_t uu[1] = {u};
-            const bool ok[1] = {true};
-            float a[1][4];
-            rank_sum<u32x2, 1, N, 8>(cps, n_rt, uu, ok, a);
-            g.x = pack2(div_n<N>(a[0][0], nf), div_n<N>(a[0][1], nf));
-            g.y = pack2(div_n<N>(a[0][2], nf), div_n<N>(a[0][3], nf));
-            if (OP == kOpReduce) {
-                st_nt(reinterpret_cast<u32x2*>(pc.grad) + u, g);
-                continue;
-            }
+    const int64_t base = u0 + threadIdx.x;
+    const int64_t limit = u0 + (ch.len >> 2);
+    if constexpr (OP == kOpGather) {
+        copy_tile<kMultiU>(reinterpret_cast<const u32x2*>(pc.param), reinterpret_cast<u32x2*>(pc.full_own), base, limit);
+    } else if constexpr (OP == kOpAdamw) {
+        adamw_tile<kMultiU>(c, reinterpret_cast<const u32x2*>(pc.grad), reinterpret_cast<f32x4*>(pc.master),
+                            reinterpret_cast<f32x4*>(pc.m), reinterpret_cast<f32x4*>(pc.v),
+                            (flags & kHasParam) ? reinterpret_cast<u32x2*>(pc.param) : nullptr, base, limit);
+    } else {
+        const void* const* cps =
+            reinterpret_cast<const void* const*>(ws + hdr->contribs_off) + (int64_t)ch.piece * (N > 0 ? N : n_rt);
+        if constexpr (OP == kOpReduce) {
+            reduce_tile<N, kMultiU>(cps, n_rt, nf, reinterpret_cast<u32x2*>(pc.grad), base, limit);
         } else {
-            g = ld_nt(reinterpret_cast<const u32x2*>(pc.grad) + u);
+            fused_tile<N, kMultiU>(c, cps, n_rt, nf, reinterpret_cast<f32x4*>(pc.master), reinterpret_cast<f32x4*>(pc.m),
+                                   reinterpret_cast<f32x4*>(pc.v),
+                                   (flags & kHasGrad) ? reinterpret_cast<u32x2*>(pc.grad) : nullptr,
+                                   (flags & kHasParam) ? reinterpret_cast<u32x2*>(pc.param) : nullptr,
+                                   (flags & kHasFull) ? reinterpret_cast<u32x2*>(pc.full_own) : nullptr, base, limit);
         }
-        f32x4 w = ld_nt(reinterpret_cast<const f32x4*>(pc.master) + u);
-        f32x4 m = ld_nt(reinterpret_cast<const f32x4*>(pc.m) + u);
-        f32x4 v = ld_nt(reinterpret_cast<const f32x4*>(pc.v) + u);
-        adamw_unit(c, g, w, m, v);
-        st_nt(reinterpret_cast<f32x4*>(pc.master) + u, w);
-        st_nt(reinterpret_cast<f32x4*>(pc.m) + u, m);
-        st_nt(reinterpret_cast<f32x4*>(pc.v) + u, v);
-        const u32x2 p = to_bf16x4(w);
-        if (OP == kOpFused && (flags & kHasGrad)) st_nt(reinterpret_cast<u32x2*>(pc.grad) + u, g);
-        if (flags & kHasParam) st_nt(reinterpret_cast<u32x2*>(pc.param) + u, p);
-        if (OP == kOpFused && (flags & kHasFull)) st_nt(reinterpret_cast<u32x2*>(pc.full_own) + u, p);
     }
 }
 
@@ -365,6 +468,31 @@ unsigned grid_for(int64_t units, int per_thread) {
 #ifndef ZS_FUSED_U
 #define ZS_FUSED_U 1
 #endif
+// Occupancy throttle: dynamic LDS (never touched by the kernels) reserved per
+// block, which caps how many blocks a CU holds at once. With the step's mix
+// of reads and writes, fewer resident waves per CU keep fewer DRAM rows in
+// play and raise achieved bandwidth (measured on MI355X: 64-thread blocks
+// with 16 KiB each, ten resident waves per CU, ~8% over unthrottled).
+#ifndef ZS_FUSED_LDS_KB
+#define ZS_FUSED_LDS_KB 16
+#endif
+#ifndef ZS_REDUCE_LDS_KB
+#define ZS_REDUCE_LDS_KB 8
+#endif
+#ifndef ZS_ADAMW_LDS_KB
+#define ZS_ADAMW_LDS_KB 8
+#endif
+#ifndef ZS_GATHER_LDS_KB
+#define ZS_GATHER_LDS_KB 8
+#endif
+#ifndef ZS_MULTI_LDS_KB
+#define ZS_MULTI_LDS_KB 16
+#endif
+constexpr unsigned kFusedLds = ZS_FUSED_LDS_KB * 1024u;
+constexpr unsigned kReduceLds = ZS_REDUCE_LDS_KB * 1024u;
+constexpr unsigned kAdamwLds = ZS_ADAMW_LDS_KB * 1024u;
+constexpr unsigned kGatherLds = ZS_GATHER_LDS_KB * 1024u;
+constexpr unsigned kMultiLds = ZS_MULTI_LDS_KB * 1024u;
 constexpr int kReduceU = ZS_REDUCE_U;
 constexpr int kAdamwU = ZS_ADAMW_U;
 constexpr int kFusedU = ZS_FUSED_U;
@@ -374,7 +502,7 @@ int launch_reduce_t(const void* const* contribs, int n, void* grad, int64_t len,
     Ptrs<CAP> cp{};
     for (int q = 0; q < n; ++q) cp.p[q] = contribs[q];
     const int64_t n8 = len / 8;
-    hipLaunchKernelGGL((k_reduce<N, CAP, kReduceU>), dim3(grid_for(n8, kReduceU)), dim3(kBlock), 0, s,
+    hipLaunchKernelGGL((k_reduce<N, CAP, kReduceU>), dim3(grid_for(n8, kReduceU)), dim3(kBlock), kReduceLds, s,
                        cp, n, (float)n, reinterpret_cast<u32x4*>(grad), n8);
     return (int)hipGetLastError();
 }
@@ -385,7 +513,7 @@ int launch_fused_t(const AdamCoef& c, const void* const* contribs, int n, float*
     Ptrs<CAP> cp{};
     for (int q = 0; q < n; ++q) cp.p[q] = contribs[q];
     const int64_t n4 = len / 4;
-    hipLaunchKernelGGL((k_fused<N, CAP, kFusedU>), dim3(grid_for(n4, kFusedU)), dim3(kBlock), 0, s, c,
+    hipLaunchKernelGGL((k_fused<N, CAP, kFusedU>), dim3(grid_for(n4, kFusedU)), dim3(kBlock), kFusedLds, s, c,
                        cp, n, (float)n, reinterpret_cast<f32x4*>(master), reinterpret_cast<f32x4*>(m),
                        reinterpret_cast<f32x4*>(v), reinterpret_cast<u32x2*>(grad),
                        reinterpret_cast<u32x2*>(param), reinterpret_cast<u32x2*>(full), n4);
@@ -394,7 +522,7 @@ int launch_fused_t(const AdamCoef& c, const void* const* contribs, int n, float*
 
 template <int OP, int N>
 int launch_multi_t(const AdamCoef& c, const void* ws, int n_chunks, int n, hipStream_t s) {
-    hipLaunchKernelGGL((k_multi<OP, N>), dim3((unsigned)n_chunks), dim3(kBlock), 0, s, c,
+    hipLaunchKernelGGL((k_multi<OP, N>), dim3((unsigned)n_chunks), dim3(kBlock), kMultiLds, s, c,
                        reinterpret_cast<const MultiHeader*>(ws), n, (float)n);
     return (int)hipGetLastError();
 }
@@ -436,7 +564,7 @@ int launch_adamw(const AdamCoef& c, const void* grad, float* master, float* m, f
                  int64_t len, void* stream) {
     if (len <= 0) return 0;
     const int64_t n4 = len / 4;
-    hipLaunchKernelGGL((k_adamw<kAdamwU>), dim3(grid_for(n4, kAdamwU)), dim3(kBlock), 0,
+    hipLaunchKernelGGL((k_adamw<kAdamwU>), dim3(grid_for(n4, kAdamwU)), dim3(kBlock), kAdamwLds,
                        (hipStream_t)stream, c, reinterpret_cast<const u32x2*>(grad),
                        reinterpret_cast<f32x4*>(master), reinterpret_cast<f32x4*>(m),
                        reinterpret_cast<f32x4*>(v), reinterpret_cast<u32x2*>(param), n4);
@@ -446,7 +574,7 @@ int launch_adamw(const AdamCoef& c, const void* grad, float* master, float* m, f
 int launch_gather(const void* param, void* full_at_own, int64_t len, void* stream) {
     if (len <= 0) return 0;
     const int64_t n8 = len / 8;
-    hipLaunchKernelGGL(k_gather, dim3(grid_for(n8, 1)), dim3(kBlock), 0, (hipStream_t)stream,
+    hipLaunchKernelGGL(k_gather, dim3(grid_for(n8, 1)), dim3(kBlock), kGatherLds, (hipStream_t)stream,
                        reinterpret_cast<const u32x4*>(param), reinterpret_cast<u32x4*>(full_at_own), n8);
     return (int)hipGetLastError();
 }
