@@ -65,6 +65,11 @@ def parse():
     return ap.parse_args()
 
 
+def p99(xs):
+    ys = sorted(xs)
+    return ys[min(len(ys) - 1, int(round(0.99 * (len(ys) - 1))))]
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -159,19 +164,29 @@ def per_tensor_setup(zs, synth, oracle, wl):
 
 
 def time_loop(fn, warmup, steps):
-    """Runs fn(t) for warmup + steps steps; returns per-step ms (wall, bracketed
-    by device synchronization) and the HIP-event durations fn recorded."""
+    """Runs fn(t, timer) for `warmup` untimed steps, then `steps` timed steps
+    launched back to back. Returns (wall ms per step, bracketed by device
+    synchronization; device ms per step from one HIP event pair on the
+    stream the kernels run on; per-step event durations of a second,
+    separately timed pass, for the median and P99)."""
     import torch
     for i in range(warmup):
         fn(i + 1, None)
     torch.cuda.synchronize()
-    timer = Timer()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    start.record()
     for i in range(steps):
-        fn(warmup + i + 1, timer)
+        fn(warmup + i + 1, None)
+    stop.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    return wall_ms, timer.ms()
+    dev_ms = start.elapsed_time(stop) / steps
+    timer = Timer()
+    for i in range(steps):
+        fn(warmup + steps + i + 1, timer)
+    return wall_ms, dev_ms, timer.ms()
 
 
 def cpu_baseline(oracle, synth, wl, S, window, fused_bpp):
@@ -246,20 +261,25 @@ def main():
         S = plan.shard_numel
         log(f"[bench] S={S:,} T={plan.padded_numel:,} gathered buffer {'full' if st['full_is_T'] else 'owned slice'}")
 
+        # At large N the library runs the fused step as a reduce into the
+        # grad shard followed by AdamW + gather, which needs the grad buffer
+        # (part of the persistent 16 B/param state); its write is counted.
+        write_grad = N >= 64
+        grad_out = st["grad"] if write_grad else None
+
         def fused(t, timer):
             e = timer.start() if timer else None
             zs.zs_fused_shard_step(plan, hp0.at(t), st["contribs"], st["master"], st["m"], st["v"],
-                                   full=st["full"])
+                                   grad=grad_out, full=st["full"])
             if timer:
                 timer.stop(e)
 
-        wall_ms, ev = time_loop(fused, args.warmup, args.steps)
-        bpp = fused_bytes_per_param(N)
-        kern_ms = statistics.mean(ev)
+        wall_ms, kern_ms, ev = time_loop(fused, args.warmup, args.steps)
+        bpp = fused_bytes_per_param(N, write_grad=write_grad)
         result_paths["fused"] = {"ms_per_step": wall_ms, "kernel_ms_mean": kern_ms,
-                                 "kernel_ms_median": statistics.median(ev), "kernel_ms_p99": max(ev),
-                                 "bytes_per_param": bpp, "launches_per_step": 1,
-                                 "kernel": "k_fused"}
+                                 "kernel_ms_median": statistics.median(ev), "kernel_ms_p99": p99(ev),
+                                 "bytes_per_param": bpp, "launches_per_step": 2 if write_grad else 1,
+                                 "kernel": "k_reduce+k_adamw" if write_grad else "k_fused"}
         main_path = "fused"
         if not args.no_unfused:
             B = wl.bucket_elems or S
@@ -274,8 +294,9 @@ def main():
                 if timer:
                     timer.stop(e)
 
-            u_wall, u_ev = time_loop(unfused, 1, max(3, args.steps // 2))
-            result_paths["unfused"] = {"ms_per_step": u_wall, "events_ms_mean": statistics.mean(u_ev),
+            u_wall, u_dev, u_ev = time_loop(unfused, 1, max(3, args.steps // 2))
+            result_paths["unfused"] = {"ms_per_step": u_wall, "device_ms_per_step": u_dev,
+                                       "events_ms_median": statistics.median(u_ev),
                                        "bytes_per_param": unfused_bytes_per_param(N),
                                        "launches_per_step": (S + B - 1) // B + 2,
                                        "reduce_buckets": (S + B - 1) // B}
@@ -291,12 +312,11 @@ def main():
             if timer:
                 timer.stop(e)
 
-        wall_ms, ev = time_loop(fused, args.warmup, args.steps)
+        wall_ms, kern_ms, ev = time_loop(fused, args.warmup, args.steps)
         bpp = fused_bytes_per_param(N)
-        kern_ms = statistics.mean(ev)
         result_paths["fused_multi"] = {"ms_per_step": wall_ms, "kernel_ms_mean": kern_ms,
                                        "kernel_ms_median": statistics.median(ev),
-                                       "kernel_ms_p99": max(ev), "bytes_per_param": bpp,
+                                       "kernel_ms_p99": p99(ev), "bytes_per_param": bpp,
                                        "launches_per_step": 1, "kernel": "k_multi"}
         main_path = "fused_multi"
         if not args.no_unfused:
@@ -308,8 +328,9 @@ def main():
                 if timer:
                     timer.stop(e)
 
-            u_wall, u_ev = time_loop(unfused, 1, max(3, args.steps // 2))
-            result_paths["unfused_multi"] = {"ms_per_step": u_wall, "events_ms_mean": statistics.mean(u_ev),
+            u_wall, u_dev, u_ev = time_loop(unfused, 1, max(3, args.steps // 2))
+            result_paths["unfused_multi"] = {"ms_per_step": u_wall, "device_ms_per_step": u_dev,
+                                             "events_ms_median": statistics.median(u_ev),
                                              "bytes_per_param": unfused_bytes_per_param(N),
                                              "launches_per_step": 3}
 

@@ -260,7 +260,7 @@ zs_status zs_adamw_shard_step(const zs_plan* plan, const zs_adamw_hparams* hp, c
     if (zs_status st = check_ptr(v, "v")) return st;
     if (zs_status st = check_ptr(param_bf16, "param_bf16")) return st;
     if (plan->S == 0) return ZS_OK;
-    return hip_status(zs::launch_adamw(zs::make_coef(*hp), grad_bf16, master, m, v, param_bf16, plan->S, stream),
+    return hip_status(zs::launch_adamw(zs::make_coef(*hp), grad_bf16, master, m, v, param_bf16, nullptr, plan->S, stream),
                       "adamw launch");
 }
 
@@ -432,8 +432,7 @@ zs_status zs_reduce_shard_multi(const zs_plan* plan, const void* workspace, void
     if (zs_status st = check_multi_plan(plan)) return st;
     Binding b;
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasContribs | zs::kHasGrad, &b)) return st;
-    return hip_status(zs::launch_multi(zs::kOpReduce, nullptr, workspace, (int)plan->chunks.size(), b.n_contribs,
-                                       b.flags, stream),
+    return hip_status(zs::launch_multi(zs::kOpReduce, nullptr, workspace, (int)plan->chunks.size(), b.n_contribs, stream),
                       "multi reduce launch");
 }
 
@@ -444,8 +443,7 @@ zs_status zs_adamw_shard_step_multi(const zs_plan* plan, const zs_adamw_hparams*
     Binding b;
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasGrad | zs::kHasState, &b)) return st;
     const zs::AdamCoef c = zs::make_coef(*hp);
-    return hip_status(zs::launch_multi(zs::kOpAdamw, &c, workspace, (int)plan->chunks.size(), b.n_contribs, b.flags,
-                                       stream),
+    return hip_status(zs::launch_multi(zs::kOpAdamw, &c, workspace, (int)plan->chunks.size(), b.n_contribs, stream),
                       "multi adamw launch");
 }
 
@@ -453,8 +451,7 @@ zs_status zs_gather_params_multi(const zs_plan* plan, const void* workspace, voi
     if (zs_status st = check_multi_plan(plan)) return st;
     Binding b;
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasParam | zs::kHasFull, &b)) return st;
-    return hip_status(zs::launch_multi(zs::kOpGather, nullptr, workspace, (int)plan->chunks.size(), b.n_contribs,
-                                       b.flags, stream),
+    return hip_status(zs::launch_multi(zs::kOpGather, nullptr, workspace, (int)plan->chunks.size(), b.n_contribs, stream),
                       "multi gather launch");
 }
 
@@ -465,8 +462,7 @@ zs_status zs_fused_shard_step_multi(const zs_plan* plan, const zs_adamw_hparams*
     Binding b;
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasContribs | zs::kHasState, &b)) return st;
     const zs::AdamCoef c = zs::make_coef(*hp);
-    return hip_status(zs::launch_multi(zs::kOpFused, &c, workspace, (int)plan->chunks.size(), b.n_contribs, b.flags,
-                                       stream),
+    return hip_status(zs::launch_multi(zs::kOpFused, &c, workspace, (int)plan->chunks.size(), b.n_contribs, stream),
                       "multi fused launch");
 }
 

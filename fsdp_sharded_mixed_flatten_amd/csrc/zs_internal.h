@@ -95,14 +95,14 @@ constexpr uint64_t kMultiMagic = 0x7A734D554C544931ull;
 // Launchers (zs_kernels.hip). They return a hipError_t value cast to int.
 int launch_reduce(const void* const* contribs, int n, void* grad, int64_t len, void* stream);
 int launch_adamw(const AdamCoef& c, const void* grad, float* master, float* m, float* v,
-                 void* param, int64_t len, void* stream);
+                 void* param, void* full_at_own, int64_t len, void* stream);
 int launch_gather(const void* param, void* full_at_own, int64_t len, void* stream);
 int launch_fused(const AdamCoef& c, const void* const* contribs, int n, float* master, float* m,
                  float* v, void* grad, void* param, void* full_at_own, int64_t len, void* stream);
 
 enum MultiOp : int32_t { kOpReduce = 0, kOpAdamw = 1, kOpGather = 2, kOpFused = 3 };
 int launch_multi(int op, const AdamCoef* c, const void* workspace, int n_chunks, int n_contribs,
-                 int flags, void* stream);
+                 void* stream);
 int copy_h2d_sync(void* dst, const void* src, int64_t bytes, void* stream);
 const char* hip_error_text(int err);
 

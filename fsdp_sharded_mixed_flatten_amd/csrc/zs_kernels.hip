@@ -1,28 +1,92 @@
 // HIP kernels of the shard-local step for CDNA4 (gfx950).
 //
-// Everything here is a pure HBM stream: per owned element the step reads
-// 2N + 14 bytes and writes 14 (fused: 2N + 12 read, 14 written), with about
-// 25 fp32 operations, so no kernel is compute-bound and none uses MFMA.
-// Design points:
-//   * 64-lane wavefronts, 256-thread blocks, one tile per block: the grid
-//     covers the shard once and the hardware dispatches blocks in order, so
-//     the resident blocks stream a compact window that advances through
-//     every array (DRAM row locality).
-//   * Kernels that mix bf16 and fp32 arrays give each lane 4 consecutive
-//     elements: fp32 arrays move as one 16-byte dwordx4 per lane, bf16 arrays
-//     as one 8-byte dwordx2; every wave-wide access is a contiguous, fully
-//     used 1 KiB / 512 B span. bf16-only kernels give each lane 8 elements
-//     (one dwordx4).
-//   * Read-once data (the N contributions) and write-once data (the gathered
-//     buffer) use nontemporal loads/stores so they do not evict anything.
-//   * The rank loop is unrolled for the common world sizes (template N); any
-//     other N up to ZS_MAX_CONTRIBS runs a runtime loop.
-//   * The element arithmetic is the IEEE fp32 sequence of the C ABI contract,
-//     compiled with -ffp-contract=off: no FMA contraction, correctly rounded
-//     division and square root (the HIP defaults), denormals kept.
+// Every kernel here is an HBM stream: per owned element the fused step reads
+// 2N + 12 bytes (N bf16 contributions, fp32 master/m/v) and writes 14 (fp32
+// master/m/v, the bf16 parameter), with ~100 fp32 instructions, far below the
+// fp32 ridge of MI355X, so nothing is compute-bound and nothing uses MFMA.
+//
+// Design points, each measured on MI355X:
+//   * One tile per block, the grid covering the shard once. Blocks dispatch in
+//     index order, so the resident blocks stream one compact window that
+//     advances through every array and DRAM rows stay open; a persistent
+//     grid-stride grid scatters its blocks over the arrays and ran 20-25%
+//     slower.
+//   * 64-thread blocks plus an occupancy throttle: each block reserves
+//     dynamic LDS it never touches, capping the resident waves per CU. With
+//     reads and writes mixed, fewer waves in flight keep fewer DRAM rows in
+//     play (+6-8% on the fused kernel).
+//   * Lanes own 4 consecutive elements where bf16 and fp32 arrays mix (fp32 as
+//     one 16-byte dwordx4, bf16 as one 8-byte dwordx2: every wave access is a
+//     contiguous, fully used 1 KiB / 512 B span) and 8 elements in bf16-only
+//     kernels (one dwordx4).
+//   * Each lane issues the loads of a group of ranks, and of the state arrays,
+//     before consuming any, so many independent loads are in flight.
+//   * Every access is nontemporal (each access class was swept; the cached
+//     variants were slower).
+//   * Writes that interleave with heavy read traffic cost several times their
+//     share of bytes, so at large N the fused entry point runs as a nearly
+//     read-only reduce followed by AdamW writing the gathered slice directly.
+//   * The element arithmetic is the IEEE fp32 sequence of the C ABI contract
+//     (no FMA contraction: built with -ffp-contract=off; IEEE division and
+//     correctly rounded square root, the HIP defaults; denormals kept), so
+//     results are bit-identical to a plain sequential implementation.
 #include <hip/hip_runtime.h>
 
 #include "zs_internal.h"
+
+// ------------------------------------------------------------------ tuning switches
+// Build-time constants (overridable with -D for sweeps). kBlockThreads and
+// kMultiU live in zs_internal.h because the host's chunk table depends on them.
+
+// Units of work per lane: 8 elements (reduce) or 4 elements (the others).
+#ifndef ZS_REDUCE_U
+#define ZS_REDUCE_U 1
+#endif
+#ifndef ZS_ADAMW_U
+#define ZS_ADAMW_U 1
+#endif
+#ifndef ZS_FUSED_U
+#define ZS_FUSED_U 1
+#endif
+// Ranks whose loads a lane issues together.
+#ifndef ZS_GROUP
+#define ZS_GROUP 8
+#endif
+// Occupancy throttle: KiB of untouched dynamic LDS per block (160 KiB per CU).
+#ifndef ZS_FUSED_LDS_KB
+#define ZS_FUSED_LDS_KB 16
+#endif
+#ifndef ZS_REDUCE_LDS_KB
+#define ZS_REDUCE_LDS_KB 8
+#endif
+#ifndef ZS_ADAMW_LDS_KB
+#define ZS_ADAMW_LDS_KB 8
+#endif
+#ifndef ZS_GATHER_LDS_KB
+#define ZS_GATHER_LDS_KB 8
+#endif
+#ifndef ZS_MULTI_LDS_KB
+#define ZS_MULTI_LDS_KB 16
+#endif
+// World size from which the fused entry point runs reduce, then AdamW +
+// gather, when the caller provides the grad buffer (0: never).
+#ifndef ZS_SPLIT_MIN_N
+#define ZS_SPLIT_MIN_N 64
+#endif
+// Cache policy per access class (1 = nontemporal): read-once inputs, the
+// read-modify-write optimizer state, write-once outputs.
+#ifndef ZS_NT_IN
+#define ZS_NT_IN 1
+#endif
+#ifndef ZS_NT_STATE_LD
+#define ZS_NT_STATE_LD 1
+#endif
+#ifndef ZS_NT_STATE_ST
+#define ZS_NT_STATE_ST 1
+#endif
+#ifndef ZS_NT_OUT
+#define ZS_NT_OUT 1
+#endif
 
 namespace zs {
 namespace {
@@ -31,7 +95,17 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBlock = kBlockThreads;  // threads per block (zs_internal.h)
+constexpr int kBlock = kBlockThreads;
+constexpr int kGroup = ZS_GROUP;
+constexpr int kReduceU = ZS_REDUCE_U;
+constexpr int kAdamwU = ZS_ADAMW_U;
+constexpr int kFusedU = ZS_FUSED_U;
+constexpr unsigned kFusedLds = ZS_FUSED_LDS_KB * 1024u;
+constexpr unsigned kReduceLds = ZS_REDUCE_LDS_KB * 1024u;
+constexpr unsigned kAdamwLds = ZS_ADAMW_LDS_KB * 1024u;
+constexpr unsigned kGatherLds = ZS_GATHER_LDS_KB * 1024u;
+constexpr unsigned kMultiLds = ZS_MULTI_LDS_KB * 1024u;
+constexpr int kSplitMinN = ZS_SPLIT_MIN_N;
 
 // ------------------------------------------------------------------ bf16
 
@@ -61,6 +135,26 @@ __device__ __forceinline__ void adamw_elem(const AdamCoef& c, float gf, float& w
     v = vn;
 }
 
+__device__ __forceinline__ void adamw_unit(const AdamCoef& c, u32x2 g, f32x4& w, f32x4& m, f32x4& v) {
+    float w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
+    float m0 = m.x, m1 = m.y, m2 = m.z, m3 = m.w;
+    float v0 = v.x, v1 = v.y, v2 = v.z, v3 = v.w;
+    adamw_elem(c, lo_bf16(g.x), w0, m0, v0);
+    adamw_elem(c, hi_bf16(g.x), w1, m1, v1);
+    adamw_elem(c, lo_bf16(g.y), w2, m2, v2);
+    adamw_elem(c, hi_bf16(g.y), w3, m3, v3);
+    w = f32x4{w0, w1, w2, w3};
+    m = f32x4{m0, m1, m2, m3};
+    v = f32x4{v0, v1, v2, v3};
+}
+
+__device__ __forceinline__ u32x2 to_bf16x4(const f32x4& w) {
+    u32x2 p;
+    p.x = pack2(w.x, w.y);
+    p.y = pack2(w.z, w.w);
+    return p;
+}
+
 // ------------------------------------------------------------------ memory helpers
 
 template <typename T>
@@ -68,21 +162,6 @@ __device__ __forceinline__ T ld_nt(const T* p) { return __builtin_nontemporal_lo
 template <typename T>
 __device__ __forceinline__ void st_nt(T* p, T x) { __builtin_nontemporal_store(x, p); }
 
-// Cache policy per access class (build-time switches, 1 = nontemporal):
-// read-once inputs (contributions, the grad/param inputs of the unfused
-// kernels), the read-modify-write optimizer state, and write-once outputs.
-#ifndef ZS_NT_IN
-#define ZS_NT_IN 1
-#endif
-#ifndef ZS_NT_STATE_LD
-#define ZS_NT_STATE_LD 1
-#endif
-#ifndef ZS_NT_STATE_ST
-#define ZS_NT_STATE_ST 1
-#endif
-#ifndef ZS_NT_OUT
-#define ZS_NT_OUT 1
-#endif
 template <typename T>
 __device__ __forceinline__ T ld_in(const T* p) {
     if constexpr (ZS_NT_IN) return ld_nt(p); else return *p;
@@ -155,15 +234,9 @@ __device__ __forceinline__ void sum_group(const void* const* p, int q0, const in
             if (ok[k]) acc_add<V>(a[k], x[g][k]);
 }
 
-// Ranks whose loads a lane issues together.
-#ifndef ZS_GROUP
-#define ZS_GROUP 8
-#endif
-constexpr int kGroup = ZS_GROUP;
-
-// Full rank sum: compile-time N in groups of min(N, GMAX); runtime N in
+// Full rank sum: compile-time N in groups of min(N, kGroup); runtime N in
 // groups of 4 plus a remainder loop.
-template <typename V, int U, int N, int GMAX>
+template <typename V, int U, int N>
 __device__ __forceinline__ void rank_sum(const void* const* p, int n_rt, const int64_t* u, const bool* ok,
                                          float (*a)[Lanes<V>::E]) {
 #pragma unroll
@@ -171,7 +244,7 @@ __device__ __forceinline__ void rank_sum(const void* const* p, int n_rt, const i
 #pragma unroll
         for (int e = 0; e < Lanes<V>::E; ++e) a[k][e] = 0.0f;
     if constexpr (N > 0) {
-        constexpr int G = N < GMAX ? N : GMAX;
+        constexpr int G = N < kGroup ? N : kGroup;
         static_assert(N % G == 0, "world sizes with compiled loops are powers of two");
 #pragma unroll
         for (int q0 = 0; q0 < N; q0 += G) sum_group<V, U, G>(p, q0, u, ok, a);
@@ -192,160 +265,49 @@ __device__ __forceinline__ float div_n(float x, float nf) {
         return x / nf;
 }
 
-// ------------------------------------------------------------------ reduce
-
-// grad[j] = bf16(avg_q contrib_q[j]); each lane owns U units of 8 elements.
-template <int N, int CAP, int U>
-__global__ __launch_bounds__(kBlock) void k_reduce(Ptrs<CAP> cp, int n_rt, float nf,
-                                                   u32x4* __restrict__ out, int64_t n8) {
-    {  // one tile of kBlock * U units per block; the grid covers the shard once
-        const int64_t base = (int64_t)blockIdx.x * kBlock * U + threadIdx.x;
-        int64_t u[U];
-        bool ok[U];
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-            u[k] = base + (int64_t)k * kBlock;
-            ok[k] = u[k] < n8;
-        }
-        float a[U][8];
-        rank_sum<u32x4, U, N, kGroup>(cp.p, n_rt, u, ok, a);
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-            if (!ok[k]) continue;
-            u32x4 o;
-            o.x = pack2(div_n<N>(a[k][0], nf), div_n<N>(a[k][1], nf));
-            o.y = pack2(div_n<N>(a[k][2], nf), div_n<N>(a[k][3], nf));
-            o.z = pack2(div_n<N>(a[k][4], nf), div_n<N>(a[k][5], nf));
-            o.w = pack2(div_n<N>(a[k][6], nf), div_n<N>(a[k][7], nf));
-            st_out(out + u[k], o);
-        }
-    }
+template <int N>
+__device__ __forceinline__ u32x2 avg_bf16x4(const float* a, float nf) {
+    u32x2 g;
+    g.x = pack2(div_n<N>(a[0], nf), div_n<N>(a[1], nf));
+    g.y = pack2(div_n<N>(a[2], nf), div_n<N>(a[3], nf));
+    return g;
 }
 
-// ------------------------------------------------------------------ AdamW
+// ------------------------------------------------------------------ tiles
+//
+// A tile is kBlock lanes x U units; a lane's units sit at base, base + kBlock,
+// ... (in units of the tile's vector type); units at or past `limit` are
+// skipped. Optional outputs are nullptr when not written (uniform per block).
 
-__device__ __forceinline__ void adamw_unit(const AdamCoef& c, u32x2 g, f32x4& w, f32x4& m, f32x4& v) {
-    float w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
-    float m0 = m.x, m1 = m.y, m2 = m.z, m3 = m.w;
-    float v0 = v.x, v1 = v.y, v2 = v.z, v3 = v.w;
-    adamw_elem(c, lo_bf16(g.x), w0, m0, v0);
-    adamw_elem(c, hi_bf16(g.x), w1, m1, v1);
-    adamw_elem(c, lo_bf16(g.y), w2, m2, v2);
-    adamw_elem(c, hi_bf16(g.y), w3, m3, v3);
-    w = f32x4{w0, w1, w2, w3};
-    m = f32x4{m0, m1, m2, m3};
-    v = f32x4{v0, v1, v2, v3};
-}
-
-__device__ __forceinline__ u32x2 to_bf16x4(const f32x4& w) {
-    u32x2 p;
-    p.x = pack2(w.x, w.y);
-    p.y = pack2(w.z, w.w);
-    return p;
-}
-
-template <int U>
-__global__ __launch_bounds__(kBlock) void k_adamw(AdamCoef c, const u32x2* __restrict__ g,
-                                                  f32x4* __restrict__ master, f32x4* __restrict__ m,
-                                                  f32x4* __restrict__ v, u32x2* __restrict__ param,
-                                                  int64_t n4) {
-    {  // one tile of kBlock * U units per block; the grid covers the shard once
-        const int64_t base = (int64_t)blockIdx.x * kBlock * U + threadIdx.x;
-        u32x2 gv[U];
-        f32x4 wv[U], mv[U], vv[U];
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-            const int64_t u = base + (int64_t)k * kBlock;
-            if (u < n4) {
-                gv[k] = ld_in(g + u);
-                wv[k] = ld_state(master + u);
-                mv[k] = ld_state(m + u);
-                vv[k] = ld_state(v + u);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-            const int64_t u = base + (int64_t)k * kBlock;
-            if (u < n4) {
-                adamw_unit(c, gv[k], wv[k], mv[k], vv[k]);
-                st_state(master + u, wv[k]);
-                st_state(m + u, mv[k]);
-                st_state(v + u, vv[k]);
-                st_out(param + u, to_bf16x4(wv[k]));
-            }
-        }
-    }
-}
-
-// ------------------------------------------------------------------ gather
-
-__global__ __launch_bounds__(kBlock) void k_gather(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
-                                                   int64_t n8) {
-    const int64_t u = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (u < n8) st_out(dst + u, ld_in(src + u));
-}
-
-// ------------------------------------------------------------------ fused
-
-// One tile of reduce + AdamW + gather: U units of 4 elements per lane, the
-// lane's units at base, base + kBlock, ...; units at or past `limit` are
-// skipped. grad, param and full are optional (nullptr: not written; the
-// test is uniform across the block).
+// reduce in units of 8 elements (bf16 only)
 template <int N, int U>
-__device__ __forceinline__ void fused_tile(const AdamCoef& c, const void* const* cp, int n_rt, float nf,
-                                           f32x4* __restrict__ master, f32x4* __restrict__ m,
-                                           f32x4* __restrict__ v, u32x2* __restrict__ grad,
-                                           u32x2* __restrict__ param, u32x2* __restrict__ full,
-                                           int64_t base, int64_t limit) {
+__device__ __forceinline__ void reduce8_tile(const void* const* cp, int n_rt, float nf, u32x4* __restrict__ out,
+                                             int64_t base, int64_t limit) {
     int64_t u[U];
     bool ok[U];
-    f32x4 wv[U], mv[U], vv[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
         u[k] = base + (int64_t)k * kBlock;
         ok[k] = u[k] < limit;
-        if (ok[k]) {
-            wv[k] = ld_state(master + u[k]);
-            mv[k] = ld_state(m + u[k]);
-            vv[k] = ld_state(v + u[k]);
-        }
     }
-    float a[U][4];
-    rank_sum<u32x2, U, N, kGroup>(cp, n_rt, u, ok, a);
+    float a[U][8];
+    rank_sum<u32x4, U, N>(cp, n_rt, u, ok, a);
 #pragma unroll
     for (int k = 0; k < U; ++k) {
         if (!ok[k]) continue;
-        u32x2 g;
-        g.x = pack2(div_n<N>(a[k][0], nf), div_n<N>(a[k][1], nf));
-        g.y = pack2(div_n<N>(a[k][2], nf), div_n<N>(a[k][3], nf));
-        adamw_unit(c, g, wv[k], mv[k], vv[k]);
-        st_state(master + u[k], wv[k]);
-        st_state(m + u[k], mv[k]);
-        st_state(v + u[k], vv[k]);
-        const u32x2 p = to_bf16x4(wv[k]);
-        if (grad) st_out(grad + u[k], g);
-        if (param) st_out(param + u[k], p);
-        if (full) st_out(full + u[k], p);
+        u32x4 o;
+        o.x = pack2(div_n<N>(a[k][0], nf), div_n<N>(a[k][1], nf));
+        o.y = pack2(div_n<N>(a[k][2], nf), div_n<N>(a[k][3], nf));
+        o.z = pack2(div_n<N>(a[k][4], nf), div_n<N>(a[k][5], nf));
+        o.w = pack2(div_n<N>(a[k][6], nf), div_n<N>(a[k][7], nf));
+        st_out(out + u[k], o);
     }
 }
 
-template <int N, int CAP, int U>
-__global__ __launch_bounds__(kBlock) void k_fused(AdamCoef c, Ptrs<CAP> cp, int n_rt, float nf,
-                                                  f32x4* __restrict__ master, f32x4* __restrict__ m,
-                                                  f32x4* __restrict__ v, u32x2* __restrict__ grad,
-                                                  u32x2* __restrict__ param, u32x2* __restrict__ full,
-                                                  int64_t n4) {
-    // one tile of kBlock * U units per block; the grid covers the shard once
-    fused_tile<N, U>(c, cp.p, n_rt, nf, master, m, v, grad, param, full,
-                     (int64_t)blockIdx.x * kBlock * U + threadIdx.x, n4);
-}
-
-// ------------------------------------------------------------------ multi-tensor
-
-// Tiles of the unfused steps in 4-element units, for the multi-tensor kernel.
+// reduce in units of 4 elements
 template <int N, int U>
-__device__ __forceinline__ void reduce_tile(const void* const* cp, int n_rt, float nf, u32x2* __restrict__ out,
-                                            int64_t base, int64_t limit) {
+__device__ __forceinline__ void reduce4_tile(const void* const* cp, int n_rt, float nf, u32x2* __restrict__ out,
+                                             int64_t base, int64_t limit) {
     int64_t u[U];
     bool ok[U];
 #pragma unroll
@@ -354,21 +316,17 @@ __device__ __forceinline__ void reduce_tile(const void* const* cp, int n_rt, flo
         ok[k] = u[k] < limit;
     }
     float a[U][4];
-    rank_sum<u32x2, U, N, kGroup>(cp, n_rt, u, ok, a);
+    rank_sum<u32x2, U, N>(cp, n_rt, u, ok, a);
 #pragma unroll
-    for (int k = 0; k < U; ++k) {
-        if (!ok[k]) continue;
-        u32x2 g;
-        g.x = pack2(div_n<N>(a[k][0], nf), div_n<N>(a[k][1], nf));
-        g.y = pack2(div_n<N>(a[k][2], nf), div_n<N>(a[k][3], nf));
-        st_out(out + u[k], g);
-    }
+    for (int k = 0; k < U; ++k)
+        if (ok[k]) st_out(out + u[k], avg_bf16x4<N>(a[k], nf));
 }
 
+// AdamW from a bf16 grad; writes the bf16 parameter to `param` and/or `full`
 template <int U>
 __device__ __forceinline__ void adamw_tile(const AdamCoef& c, const u32x2* __restrict__ g, f32x4* __restrict__ master,
                                            f32x4* __restrict__ m, f32x4* __restrict__ v, u32x2* __restrict__ param,
-                                           int64_t base, int64_t limit) {
+                                           u32x2* __restrict__ full, int64_t base, int64_t limit) {
     u32x2 gv[U];
     f32x4 wv[U], mv[U], vv[U];
 #pragma unroll
@@ -389,15 +347,17 @@ __device__ __forceinline__ void adamw_tile(const AdamCoef& c, const u32x2* __res
             st_state(master + u, wv[k]);
             st_state(m + u, mv[k]);
             st_state(v + u, vv[k]);
-            if (param) st_out(param + u, to_bf16x4(wv[k]));
+            const u32x2 p = to_bf16x4(wv[k]);
+            if (param) st_out(param + u, p);
+            if (full) st_out(full + u, p);
         }
     }
 }
 
-template <int U>
-__device__ __forceinline__ void copy_tile(const u32x2* __restrict__ src, u32x2* __restrict__ dst, int64_t base,
+template <typename V, int U>
+__device__ __forceinline__ void copy_tile(const V* __restrict__ src, V* __restrict__ dst, int64_t base,
                                           int64_t limit) {
-    u32x2 x[U];
+    V x[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
         const int64_t u = base + (int64_t)k * kBlock;
@@ -409,6 +369,80 @@ __device__ __forceinline__ void copy_tile(const u32x2* __restrict__ src, u32x2* 
         if (u < limit) st_out(dst + u, x[k]);
     }
 }
+
+// reduce + AdamW + gather write in registers
+template <int N, int U>
+__device__ __forceinline__ void fused_tile(const AdamCoef& c, const void* const* cp, int n_rt, float nf,
+                                           f32x4* __restrict__ master, f32x4* __restrict__ m,
+                                           f32x4* __restrict__ v, u32x2* __restrict__ grad,
+                                           u32x2* __restrict__ param, u32x2* __restrict__ full,
+                                           int64_t base, int64_t limit) {
+    int64_t u[U];
+    bool ok[U];
+    f32x4 wv[U], mv[U], vv[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        u[k] = base + (int64_t)k * kBlock;
+        ok[k] = u[k] < limit;
+        if (ok[k]) {
+            wv[k] = ld_state(master + u[k]);
+            mv[k] = ld_state(m + u[k]);
+            vv[k] = ld_state(v + u[k]);
+        }
+    }
+    float a[U][4];
+    rank_sum<u32x2, U, N>(cp, n_rt, u, ok, a);
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        if (!ok[k]) continue;
+        const u32x2 g = avg_bf16x4<N>(a[k], nf);
+        adamw_unit(c, g, wv[k], mv[k], vv[k]);
+        st_state(master + u[k], wv[k]);
+        st_state(m + u[k], mv[k]);
+        st_state(v + u[k], vv[k]);
+        const u32x2 p = to_bf16x4(wv[k]);
+        if (grad) st_out(grad + u[k], g);
+        if (param) st_out(param + u[k], p);
+        if (full) st_out(full + u[k], p);
+    }
+}
+
+// ------------------------------------------------------------------ flat kernels
+// One tile per block; the grid covers the shard once.
+
+__device__ __forceinline__ int64_t tile_base(int units_per_lane) {
+    return (int64_t)blockIdx.x * kBlock * units_per_lane + threadIdx.x;
+}
+
+template <int N, int CAP, int U>
+__global__ __launch_bounds__(kBlock) void k_reduce(Ptrs<CAP> cp, int n_rt, float nf, u32x4* __restrict__ out,
+                                                   int64_t n8) {
+    reduce8_tile<N, U>(cp.p, n_rt, nf, out, tile_base(U), n8);
+}
+
+template <int U>
+__global__ __launch_bounds__(kBlock) void k_adamw(AdamCoef c, const u32x2* __restrict__ g,
+                                                  f32x4* __restrict__ master, f32x4* __restrict__ m,
+                                                  f32x4* __restrict__ v, u32x2* __restrict__ param,
+                                                  u32x2* __restrict__ full, int64_t n4) {
+    adamw_tile<U>(c, g, master, m, v, param, full, tile_base(U), n4);
+}
+
+__global__ __launch_bounds__(kBlock) void k_gather(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                   int64_t n8) {
+    copy_tile<u32x4, 1>(src, dst, tile_base(1), n8);
+}
+
+template <int N, int CAP, int U>
+__global__ __launch_bounds__(kBlock) void k_fused(AdamCoef c, Ptrs<CAP> cp, int n_rt, float nf,
+                                                  f32x4* __restrict__ master, f32x4* __restrict__ m,
+                                                  f32x4* __restrict__ v, u32x2* __restrict__ grad,
+                                                  u32x2* __restrict__ param, u32x2* __restrict__ full,
+                                                  int64_t n4) {
+    fused_tile<N, U>(c, cp.p, n_rt, nf, master, m, v, grad, param, full, tile_base(U), n4);
+}
+
+// ------------------------------------------------------------------ multi-tensor kernel
 
 // One block per chunk; a chunk is one tile (kBlock lanes x kMultiU units of
 // 4 elements) of one piece. The piece supplies every pointer; the
@@ -424,16 +458,17 @@ __global__ __launch_bounds__(kBlock) void k_multi(AdamCoef c, const MultiHeader*
     const int64_t base = u0 + threadIdx.x;
     const int64_t limit = u0 + (ch.len >> 2);
     if constexpr (OP == kOpGather) {
-        copy_tile<kMultiU>(reinterpret_cast<const u32x2*>(pc.param), reinterpret_cast<u32x2*>(pc.full_own), base, limit);
+        copy_tile<u32x2, kMultiU>(reinterpret_cast<const u32x2*>(pc.param), reinterpret_cast<u32x2*>(pc.full_own),
+                                  base, limit);
     } else if constexpr (OP == kOpAdamw) {
         adamw_tile<kMultiU>(c, reinterpret_cast<const u32x2*>(pc.grad), reinterpret_cast<f32x4*>(pc.master),
                             reinterpret_cast<f32x4*>(pc.m), reinterpret_cast<f32x4*>(pc.v),
-                            (flags & kHasParam) ? reinterpret_cast<u32x2*>(pc.param) : nullptr, base, limit);
+                            (flags & kHasParam) ? reinterpret_cast<u32x2*>(pc.param) : nullptr, nullptr, base, limit);
     } else {
         const void* const* cps =
             reinterpret_cast<const void* const*>(ws + hdr->contribs_off) + (int64_t)ch.piece * (N > 0 ? N : n_rt);
         if constexpr (OP == kOpReduce) {
-            reduce_tile<N, kMultiU>(cps, n_rt, nf, reinterpret_cast<u32x2*>(pc.grad), base, limit);
+            reduce4_tile<N, kMultiU>(cps, n_rt, nf, reinterpret_cast<u32x2*>(pc.grad), base, limit);
         } else {
             fused_tile<N, kMultiU>(c, cps, n_rt, nf, reinterpret_cast<f32x4*>(pc.master), reinterpret_cast<f32x4*>(pc.m),
                                    reinterpret_cast<f32x4*>(pc.v),
@@ -446,56 +481,13 @@ __global__ __launch_bounds__(kBlock) void k_multi(AdamCoef c, const MultiHeader*
 
 // ------------------------------------------------------------------ launch helpers
 
-// Grid of a tile launch: one block per tile of kBlock * per_thread units.
-// Blocks are dispatched in index order, so the blocks resident at any moment
-// stream one compact, advancing window of each array (good DRAM row
-// locality); a persistent grid-stride grid spreads its blocks over the whole
-// array and measured ~25% slower on MI355X.
-unsigned grid_for(int64_t units, int per_thread) {
-    const int64_t per_block = (int64_t)kBlock * per_thread;
+// Blocks of a tile launch over `units` lane-units, `per_lane` units per lane.
+unsigned grid_for(int64_t units, int per_lane) {
+    const int64_t per_block = (int64_t)kBlock * per_lane;
     int64_t blocks = (units + per_block - 1) / per_block;
     if (blocks < 1) blocks = 1;
     return (unsigned)blocks;
 }
-
-// Launch shape: units of work per lane. Overridable at build time for sweeps.
-#ifndef ZS_REDUCE_U
-#define ZS_REDUCE_U 1
-#endif
-#ifndef ZS_ADAMW_U
-#define ZS_ADAMW_U 1
-#endif
-#ifndef ZS_FUSED_U
-#define ZS_FUSED_U 1
-#endif
-// Occupancy throttle: dynamic LDS (never touched by the kernels) reserved per
-// block, which caps how many blocks a CU holds at once. With the step's mix
-// of reads and writes, fewer resident waves per CU keep fewer DRAM rows in
-// play and raise achieved bandwidth (measured on MI355X: 64-thread blocks
-// with 16 KiB each, ten resident waves per CU, ~8% over unthrottled).
-#ifndef ZS_FUSED_LDS_KB
-#define ZS_FUSED_LDS_KB 16
-#endif
-#ifndef ZS_REDUCE_LDS_KB
-#define ZS_REDUCE_LDS_KB 8
-#endif
-#ifndef ZS_ADAMW_LDS_KB
-#define ZS_ADAMW_LDS_KB 8
-#endif
-#ifndef ZS_GATHER_LDS_KB
-#define ZS_GATHER_LDS_KB 8
-#endif
-#ifndef ZS_MULTI_LDS_KB
-#define ZS_MULTI_LDS_KB 16
-#endif
-constexpr unsigned kFusedLds = ZS_FUSED_LDS_KB * 1024u;
-constexpr unsigned kReduceLds = ZS_REDUCE_LDS_KB * 1024u;
-constexpr unsigned kAdamwLds = ZS_ADAMW_LDS_KB * 1024u;
-constexpr unsigned kGatherLds = ZS_GATHER_LDS_KB * 1024u;
-constexpr unsigned kMultiLds = ZS_MULTI_LDS_KB * 1024u;
-constexpr int kReduceU = ZS_REDUCE_U;
-constexpr int kAdamwU = ZS_ADAMW_U;
-constexpr int kFusedU = ZS_FUSED_U;
 
 template <int N, int CAP>
 int launch_reduce_t(const void* const* contribs, int n, void* grad, int64_t len, hipStream_t s) {
@@ -561,13 +553,14 @@ int launch_reduce(const void* const* contribs, int n, void* grad, int64_t len, v
 }
 
 int launch_adamw(const AdamCoef& c, const void* grad, float* master, float* m, float* v, void* param,
-                 int64_t len, void* stream) {
+                 void* full_at_own, int64_t len, void* stream) {
     if (len <= 0) return 0;
     const int64_t n4 = len / 4;
     hipLaunchKernelGGL((k_adamw<kAdamwU>), dim3(grid_for(n4, kAdamwU)), dim3(kBlock), kAdamwLds,
                        (hipStream_t)stream, c, reinterpret_cast<const u32x2*>(grad),
                        reinterpret_cast<f32x4*>(master), reinterpret_cast<f32x4*>(m),
-                       reinterpret_cast<f32x4*>(v), reinterpret_cast<u32x2*>(param), n4);
+                       reinterpret_cast<f32x4*>(v), reinterpret_cast<u32x2*>(param),
+                       reinterpret_cast<u32x2*>(full_at_own), n4);
     return (int)hipGetLastError();
 }
 
@@ -582,6 +575,12 @@ int launch_gather(const void* param, void* full_at_own, int64_t len, void* strea
 int launch_fused(const AdamCoef& c, const void* const* contribs, int n, float* master, float* m, float* v,
                  void* grad, void* param, void* full_at_own, int64_t len, void* stream) {
     if (len <= 0) return 0;
+    if (kSplitMinN > 0 && n >= kSplitMinN && grad) {
+        // Large N: a nearly read-only reduce, then AdamW writing the outputs.
+        // Same bytes in every buffer as the one-pass kernel.
+        if (int e = launch_reduce(contribs, n, grad, len, stream)) return e;
+        return launch_adamw(c, grad, master, m, v, param, full_at_own, len, stream);
+    }
     hipStream_t s = (hipStream_t)stream;
     switch (n) {
         case 1: return launch_fused_t<1, 1>(c, contribs, n, master, m, v, grad, param, full_at_own, len, s);
@@ -596,9 +595,7 @@ int launch_fused(const AdamCoef& c, const void* const* contribs, int n, float* m
     }
 }
 
-int launch_multi(int op, const AdamCoef* c, const void* workspace, int n_chunks, int n_contribs, int flags,
-                 void* stream) {
-    (void)flags;
+int launch_multi(int op, const AdamCoef* c, const void* workspace, int n_chunks, int n_contribs, void* stream) {
     if (n_chunks <= 0) return 0;
     const AdamCoef cc = c ? *c : AdamCoef{};
     hipStream_t s = (hipStream_t)stream;
