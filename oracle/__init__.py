@@ -48,6 +48,13 @@ def lib():
         L.ora_time_shard_step.argtypes = [_f32p, ctypes.POINTER(_u16p), _i32, _u16p, _f32p, _f32p,
                                           _f32p, _u16p, _u16p, _i64, _i32, _i64, _i32, _i32,
                                           ctypes.POINTER(ctypes.c_double)]
+        L.ora_accumulate.argtypes = [ctypes.POINTER(_u16p), _i32, _f32p, _i32, _i64, _i64]
+        L.ora_grad_sumsq.restype = ctypes.c_double
+        L.ora_grad_sumsq.argtypes = [_f32p, ctypes.c_float, _i64, _i64, ctypes.POINTER(_i32)]
+        L.ora_clip_scale.restype = ctypes.c_float
+        L.ora_clip_scale.argtypes = [ctypes.POINTER(ctypes.c_double), _i32, ctypes.c_double]
+        L.ora_adamw_f32grad.argtypes = [_f32p, _f32p, ctypes.c_float, ctypes.c_float, _i32, _f32p, _f32p,
+                                        _f32p, _u16p, _i64, _i64]
         _lib = L
     return _lib
 
@@ -176,3 +183,30 @@ def plan_step(plan, hp, contribs_by_piece, state_by_piece, full_by_tensor=None):
         adamw(hp, g, master, m, v, p)
         if full_by_tensor is not None:
             full_by_tensor[pc.tensor][pc.own_lo:pc.own_hi] = p
+
+
+# ---------------------------------------------------------------- accumulation and clipping
+
+
+def accumulate(contribs, acc, first, lo=0, hi=None):
+    """acc += f32(bf16(average of the contributions)) (acc := that value when first)."""
+    hi = acc.size if hi is None else hi
+    lib().ora_accumulate(_contrib_table(contribs), len(contribs), _p32(acc), 1 if first else 0, lo, hi)
+
+
+def grad_sumsq(acc, divisor=1.0):
+    """(sum of (acc/divisor)^2 in double, nonfinite flag)."""
+    flag = _i32(0)
+    s = lib().ora_grad_sumsq(_p32(acc), divisor, 0, acc.size, ctypes.byref(flag))
+    return s, flag.value
+
+
+def clip_scale(sumsq_per_rank, max_norm):
+    arr = (ctypes.c_double * len(sumsq_per_rank))(*sumsq_per_rank)
+    return lib().ora_clip_scale(arr, len(sumsq_per_rank), max_norm)
+
+
+def adamw_f32grad(hp, acc, divisor, scale, skip, master, m, v, p, lo=0, hi=None):
+    hi = acc.size if hi is None else hi
+    lib().ora_adamw_f32grad(_p32(hp.coef()), _p32(acc), divisor, scale, 1 if skip else 0, _p32(master),
+                            _p32(m), _p32(v), _p16(p), lo, hi)

@@ -213,3 +213,81 @@ int ora_time_shard_step(const float* c, const uint16_t* const* contribs, int32_t
     free(jobs);
     return 0;
 }
+
+/* ---------------------------------------------------------------- accumulation and clipping
+ *
+ * Gradient accumulation over G micro-batches with the gradient shard kept in
+ * fp32 ("从 Data Parallel 到 ZeRO/FSDP", section "Gradient Accumulation 会改变生命周期":
+ * each micro-step reduce-scatters and accumulates on the shard, the loss is
+ * divided by the accumulation steps, and clipping uses the global norm;
+ * section "一次 Mixed-precision Adam 为什么接近 16 Bytes/Parameter": the
+ * accumulation dtype may be fp32). Each micro-step's averaged gradient is
+ * rounded to bf16 (the reduce dtype) and added in fp32; the gradient AdamW
+ * uses is the sum divided once by G. Global-norm clipping scales it by
+ * min(1, max_norm / (||g|| + 1e-6)), ||g|| being the L2 norm over every
+ * rank's shard. A non-finite gradient anywhere skips the optimizer step. */
+
+/* acc[j] = (first ? +0 : acc[j]) + f32(bf16(average of the contributions)) */
+void ora_accumulate(const uint16_t* const* contribs, int32_t n, float* acc, int32_t first, int64_t lo,
+                    int64_t hi) {
+    const float nf = (float)n;
+    for (int64_t j = lo; j < hi; ++j) {
+        float s = 0.0f;
+        for (int32_t q = 0; q < n; ++q) s = s + ora_bf16_to_f32(contribs[q][j]);
+        float g = ora_bf16_to_f32(ora_f32_to_bf16(s / nf));
+        float base = first ? 0.0f : acc[j];
+        acc[j] = base + g;
+    }
+}
+
+/* The gradient AdamW consumes: g = acc / G, then g * scale. */
+static inline float ora_final_grad(float acc, float divisor, float scale) {
+    float g = acc / divisor;
+    return g * scale;
+}
+
+/* Sum of squares of the final gradient (acc / G) over [lo, hi) in double,
+ * element order; *nonfinite is set to 1 when any of those values is not
+ * finite. */
+double ora_grad_sumsq(const float* acc, float divisor, int64_t lo, int64_t hi, int32_t* nonfinite) {
+    double s = 0.0;
+    for (int64_t j = lo; j < hi; ++j) {
+        float g = acc[j] / divisor;
+        if (!isfinite(g)) *nonfinite = 1;
+        s += (double)g * (double)g;
+    }
+    return s;
+}
+
+/* Clip factor from the squared norms of all ranks' shards (the all-reduced
+ * sum, added in rank order), as an fp32 multiplier no larger than 1. */
+float ora_clip_scale(const double* sumsq, int32_t n_ranks, double max_norm) {
+    double total = 0.0;
+    for (int32_t r = 0; r < n_ranks; ++r) total += sumsq[r];
+    double coef = max_norm / (sqrt(total) + 1e-6);
+    return (float)(coef < 1.0 ? coef : 1.0);
+}
+
+/* AdamW from an fp32 accumulated gradient: identical to ora_adamw with the
+ * element gradient ora_final_grad(acc[j], divisor, scale) in place of the
+ * bf16 gradient; skip != 0 leaves every array unchanged. */
+void ora_adamw_f32grad(const float* c, const float* acc, float divisor, float scale, int32_t skip, float* master,
+                       float* m, float* v, uint16_t* p, int64_t lo, int64_t hi) {
+    if (skip) return;
+    const float b1 = c[0], omb1 = c[1], b2 = c[2], omb2 = c[3];
+    const float lr = c[4], eps = c[5], decay = c[6], bc1 = c[7], bc2 = c[8];
+    for (int64_t j = lo; j < hi; ++j) {
+        float gf = ora_final_grad(acc[j], divisor, scale);
+        float w = master[j] * decay;
+        float mj = b1 * m[j] + omb1 * gf;
+        float vj = b2 * v[j] + omb2 * (gf * gf);
+        float mhat = mj / bc1;
+        float vhat = vj / bc2;
+        float den = sqrtf(vhat) + eps;
+        w = w - lr * (mhat / den);
+        master[j] = w;
+        m[j] = mj;
+        v[j] = vj;
+        p[j] = ora_f32_to_bf16(w);
+    }
+}
