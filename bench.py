@@ -60,6 +60,10 @@ def parse():
     ap.add_argument("--arena-pad-kb", type=int, default=-1,
                     help="allocate the N contributions (and master/m/v) as rows of one buffer whose "
                          "rows start this many KiB apart beyond their length (-1: separate tensors)")
+    ap.add_argument("--accum", type=int, default=0,
+                    help="also time an optimizer step with this many accumulated micro-batches, global-norm "
+                         "clipping and the non-finite skip (FLAT workloads)")
+    ap.add_argument("--clip", type=float, default=1.0, help="max norm of the --accum path")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
     return ap.parse_args()
@@ -300,6 +304,37 @@ def main():
                                        "bytes_per_param": unfused_bytes_per_param(N),
                                        "launches_per_step": (S + B - 1) // B + 2,
                                        "reduce_buckets": (S + B - 1) // B}
+        if args.accum > 0:
+            G, B = args.accum, wl.bucket_elems or S
+            acc = torch.empty(S, dtype=torch.float32, device="cuda")
+            sumsq = torch.zeros(N, dtype=torch.float64, device="cuda")
+            flags = torch.zeros(N, dtype=torch.int32, device="cuda")
+            scale = torch.zeros(1, dtype=torch.float32, device="cuda")
+            skip = torch.zeros(1, dtype=torch.int32, device="cuda")
+            ws = torch.zeros(zs.zs_grad_stats_workspace_bytes(plan), dtype=torch.uint8, device="cuda")
+
+            def accum_step(t, timer):
+                e = timer.start() if timer else None
+                for k in range(G):  # each micro-step's contributions (resident inputs reused)
+                    for off in range(0, S, B):
+                        zs.zs_accumulate_shard(plan, st["contribs"], acc, off, min(B, S - off), first=(k == 0))
+                zs.zs_grad_stats(plan, acc, float(G), sumsq[0:1], flags[0:1], ws)
+                # the other ranks' squared norms arrive by an all-reduce in a
+                # multi-GPU job; copies of this rank's stand in for them here
+                sumsq[1:].copy_(sumsq[0:1].expand(N - 1))
+                flags[1:].copy_(flags[0:1].expand(N - 1))
+                zs.zs_clip_scale(sumsq, flags, args.clip, scale, skip)
+                zs.zs_adamw_shard_step_accum(plan, hp0.at(t), acc, float(G), st["master"], st["m"], st["v"],
+                                             scale=scale, skip=skip, full=st["full"])
+                if timer:
+                    timer.stop(e)
+
+            a_wall, a_dev, a_ev = time_loop(accum_step, 1, max(3, args.steps // 2))
+            a_bytes = G * (2 * N + 8) - 4 + 4 + 30  # micro-steps (first one does not read acc), stats, AdamW
+            result_paths["accum_clip"] = {"micro_steps": G, "max_norm": args.clip, "ms_per_step": a_wall,
+                                          "device_ms_per_step": a_dev, "events_ms_median": statistics.median(a_ev),
+                                          "bytes_per_param": a_bytes,
+                                          "gbps": S * a_bytes / (a_dev / 1e3) / 1e9}
     else:
         import oracle
         plan, st = per_tensor_setup(zs, synth, oracle, wl)

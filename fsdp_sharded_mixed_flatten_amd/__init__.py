@@ -86,6 +86,12 @@ def _load():
         "zs_adamw_shard_step_multi": (st, [vp, ctypes.POINTER(AdamWHParams), vp, vp]),
         "zs_gather_params_multi": (st, [vp, vp, vp]),
         "zs_fused_shard_step_multi": (st, [vp, ctypes.POINTER(AdamWHParams), vp, vp]),
+        "zs_accumulate_shard": (st, [vp, ctypes.POINTER(vp), i32, vp, i64, i64, i32, vp]),
+        "zs_grad_stats_workspace_bytes": (i64, [vp]),
+        "zs_grad_stats": (st, [vp, vp, ctypes.c_float, vp, vp, vp, i64, vp]),
+        "zs_clip_scale": (st, [vp, vp, i32, ctypes.c_double, vp, vp, vp]),
+        "zs_adamw_shard_step_accum": (st, [vp, ctypes.POINTER(AdamWHParams), vp, ctypes.c_float, vp, vp, vp, vp,
+                                           vp, vp, vp, vp]),
         "zs_last_error": (ctypes.c_char_p, []),
         "zs_version": (ctypes.c_char_p, []),
     }
@@ -102,7 +108,8 @@ EXPORTED = ("zs_shard_plan", "zs_plan_destroy", "zs_plan_padded_numel", "zs_plan
             "zs_plan_layout", "zs_plan_tensor", "zs_reduce_shard", "zs_adamw_shard_step",
             "zs_gather_params", "zs_fused_shard_step", "zs_multi_workspace_bytes", "zs_multi_bind",
             "zs_reduce_shard_multi", "zs_adamw_shard_step_multi", "zs_gather_params_multi",
-            "zs_fused_shard_step_multi", "zs_last_error", "zs_version")
+            "zs_fused_shard_step_multi", "zs_accumulate_shard", "zs_grad_stats_workspace_bytes",
+            "zs_grad_stats", "zs_clip_scale", "zs_adamw_shard_step_accum", "zs_last_error", "zs_version")
 
 
 def lib():
@@ -322,6 +329,61 @@ def zs_gather_params_multi(plan, workspace, stream=None):
 def zs_fused_shard_step_multi(plan, hp, workspace, stream=None):
     _check(_lib.zs_fused_shard_step_multi(plan.handle, ctypes.byref(hp), workspace.data_ptr(),
                                           _stream(stream)))
+
+
+# ---------------------------------------------------------------- accumulation and clipping
+
+
+def _scalar_ptr(t, dtype_name, what):
+    if t is None:
+        return None
+    import torch
+    if not (isinstance(t, torch.Tensor) and t.is_cuda and str(t.dtype).endswith(dtype_name) and t.numel() >= 1):
+        raise ValueError(f"{what} must be a CUDA {dtype_name} tensor of at least one element")
+    return t.data_ptr()
+
+
+def zs_accumulate_shard(plan, contribs, acc, off=0, length=None, first=False, stream=None):
+    S = plan.shard_numel
+    length = S - off if length is None else length
+    end = min(max(off + length, 0), S)
+    ptrs = [_ptr(c, "bf16", end, f"contribs[{q}]") for q, c in enumerate(contribs)]
+    _check(_lib.zs_accumulate_shard(plan.handle, _ptr_array(ptrs), len(ptrs), _ptr(acc, "f32", end, "acc"), off,
+                                    length, 1 if first else 0, _stream(stream)))
+
+
+def zs_grad_stats_workspace_bytes(plan):
+    return _lib.zs_grad_stats_workspace_bytes(plan.handle)
+
+
+def zs_grad_stats(plan, acc, grad_divisor, sumsq_out, nonfinite_out, workspace, stream=None):
+    """sumsq_out: CUDA float64 tensor (>= 1 element); nonfinite_out: CUDA int32
+    tensor; workspace: CUDA uint8 tensor of zs_grad_stats_workspace_bytes."""
+    _check(_lib.zs_grad_stats(plan.handle, _ptr(acc, "f32", plan.shard_numel, "acc"), grad_divisor,
+                              _scalar_ptr(sumsq_out, "float64", "sumsq_out"),
+                              _scalar_ptr(nonfinite_out, "int32", "nonfinite_out"), workspace.data_ptr(),
+                              workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def zs_clip_scale(sumsq, nonfinite, max_norm, scale_out, skip_out, stream=None):
+    """sumsq: CUDA float64 tensor of the ranks' squared norms; nonfinite: CUDA
+    int32 tensor of their flags (same length)."""
+    n = sumsq.numel()
+    if nonfinite.numel() != n:
+        raise ValueError("sumsq and nonfinite must have one entry per rank")
+    _check(_lib.zs_clip_scale(_scalar_ptr(sumsq, "float64", "sumsq"), _scalar_ptr(nonfinite, "int32", "nonfinite"),
+                              n, max_norm, _scalar_ptr(scale_out, "float32", "scale_out"),
+                              _scalar_ptr(skip_out, "int32", "skip_out"), _stream(stream)))
+
+
+def zs_adamw_shard_step_accum(plan, hp, acc, grad_divisor, master, m, v, scale=None, skip=None, param=None,
+                              full=None, stream=None):
+    S, r = plan.shard_numel, plan.rank
+    _check(_lib.zs_adamw_shard_step_accum(plan.handle, ctypes.byref(hp), _ptr(acc, "f32", S, "acc"), grad_divisor,
+                                          _scalar_ptr(scale, "float32", "scale"), _scalar_ptr(skip, "int32", "skip"),
+                                          _ptr(master, "f32", S, "master"), _ptr(m, "f32", S, "m"),
+                                          _ptr(v, "f32", S, "v"), _ptr(param, "bf16", S, "param"),
+                                          _ptr(full, "bf16", (r + 1) * S, "full"), _stream(stream)))
 
 
 def zs_last_error():

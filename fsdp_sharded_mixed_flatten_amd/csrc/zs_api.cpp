@@ -298,6 +298,83 @@ zs_status zs_fused_shard_step(const zs_plan* plan, const zs_adamw_hparams* hp, c
                       "fused launch");
 }
 
+// ------------------------------------------------------------------ accumulation and clipping
+
+zs_status zs_accumulate_shard(const zs_plan* plan, const void* const* contribs, int32_t n_contribs, float* acc_f32,
+                              int64_t off, int64_t len, int32_t first, void* stream) {
+    if (zs_status st = check_plan(plan)) return st;
+    if (zs_status st = check_contribs(plan, contribs, n_contribs)) return st;
+    if (zs_status st = check_ptr(acc_f32, "acc_f32")) return st;
+    if (off < 0 || len < 0 || off % 8 || len % 8 || off > plan->S || len > plan->S - off)
+        return fail(ZS_ERANGE, "bucket [%lld, %lld) must be multiples of 8 inside the shard [0, %lld)",
+                    (long long)off, (long long)(off + len), (long long)plan->S);
+    if (len == 0) return ZS_OK;
+    const void* shifted[ZS_MAX_CONTRIBS];
+    for (int32_t q = 0; q < n_contribs; ++q) shifted[q] = static_cast<const char*>(contribs[q]) + 2 * off;
+    return hip_status(zs::launch_accumulate(shifted, n_contribs, acc_f32 + off, first ? 1 : 0, len, stream),
+                      "accumulate launch");
+}
+
+int64_t zs_grad_stats_workspace_bytes(const zs_plan* plan) {
+    if (!plan) return -1;
+    const int64_t nb = (plan->S + zs::kStatsChunk - 1) / zs::kStatsChunk;
+    return roundup(nb * 8, 256) + roundup(nb * 4, 256) + 256;
+}
+
+zs_status zs_grad_stats(const zs_plan* plan, const float* acc_f32, float grad_divisor, double* sumsq_out,
+                        int32_t* nonfinite_out, void* workspace, int64_t workspace_bytes, void* stream) {
+    if (zs_status st = check_plan(plan)) return st;
+    if (zs_status st = check_ptr(acc_f32, "acc_f32")) return st;
+    if (!std::isfinite(grad_divisor) || grad_divisor == 0.0f)
+        return fail(ZS_EINVAL, "grad_divisor = %g must be finite and nonzero", (double)grad_divisor);
+    if (!sumsq_out || !nonfinite_out) return fail(ZS_EINVAL, "sumsq_out and nonfinite_out must not be NULL");
+    if ((reinterpret_cast<uintptr_t>(sumsq_out) & 7) || (reinterpret_cast<uintptr_t>(nonfinite_out) & 3))
+        return fail(ZS_EALIGN, "sumsq_out must be 8-byte and nonfinite_out 4-byte aligned");
+    if (zs_status st = check_ptr(workspace, "workspace")) return st;
+    const int64_t need = zs_grad_stats_workspace_bytes(plan);
+    if (workspace_bytes < need)
+        return fail(ZS_ENOMEM, "workspace holds %lld bytes, zs_grad_stats needs %lld", (long long)workspace_bytes,
+                    (long long)need);
+    return hip_status(zs::launch_grad_stats(acc_f32, grad_divisor, sumsq_out, nonfinite_out, workspace, plan->S, stream),
+                      "grad stats launch");
+}
+
+zs_status zs_clip_scale(const double* sumsq, const int32_t* nonfinite, int32_t n_ranks, double max_norm,
+                        float* scale_out, int32_t* skip_out, void* stream) {
+    if (!sumsq || !nonfinite || !scale_out || !skip_out) return fail(ZS_EINVAL, "a pointer argument is NULL");
+    if ((reinterpret_cast<uintptr_t>(sumsq) & 7) || (reinterpret_cast<uintptr_t>(nonfinite) & 3) ||
+        (reinterpret_cast<uintptr_t>(scale_out) & 3) || (reinterpret_cast<uintptr_t>(skip_out) & 3))
+        return fail(ZS_EALIGN, "sumsq needs 8-byte, the others 4-byte alignment");
+    if (n_ranks < 1) return fail(ZS_EINVAL, "n_ranks = %d must be >= 1", n_ranks);
+    if (!std::isfinite(max_norm) || max_norm <= 0.0) return fail(ZS_EINVAL, "max_norm = %g must be positive", max_norm);
+    return hip_status(zs::launch_clip_scale(sumsq, nonfinite, n_ranks, max_norm, scale_out, skip_out, stream),
+                      "clip scale launch");
+}
+
+zs_status zs_adamw_shard_step_accum(const zs_plan* plan, const zs_adamw_hparams* hp, const float* acc_f32,
+                                    float grad_divisor, const float* scale, const int32_t* skip, float* master,
+                                    float* m, float* v, void* param_bf16, void* full_bf16, void* stream) {
+    if (zs_status st = check_plan(plan)) return st;
+    if (zs_status st = check_hp(hp)) return st;
+    if (zs_status st = check_ptr(acc_f32, "acc_f32")) return st;
+    if (!std::isfinite(grad_divisor) || grad_divisor == 0.0f)
+        return fail(ZS_EINVAL, "grad_divisor = %g must be finite and nonzero", (double)grad_divisor);
+    if ((scale && (reinterpret_cast<uintptr_t>(scale) & 3)) || (skip && (reinterpret_cast<uintptr_t>(skip) & 3)))
+        return fail(ZS_EALIGN, "scale and skip must be 4-byte aligned");
+    if (zs_status st = check_ptr(master, "master")) return st;
+    if (zs_status st = check_ptr(m, "m")) return st;
+    if (zs_status st = check_ptr(v, "v")) return st;
+    if (zs_status st = check_opt_ptr(param_bf16, "param_bf16")) return st;
+    if (zs_status st = check_opt_ptr(full_bf16, "full_bf16")) return st;
+    if (full_bf16 && plan->layout != ZS_LAYOUT_FLAT)
+        return fail(ZS_EINVAL, "a gather into full_bf16 needs a FLAT plan");
+    if (plan->S == 0) return ZS_OK;
+    char* own = full_bf16 ? static_cast<char*>(full_bf16) + 2 * (int64_t)plan->rank * plan->S : nullptr;
+    return hip_status(zs::launch_adamw_accum(zs::make_coef(*hp), acc_f32, grad_divisor, scale, skip, master, m, v,
+                                             param_bf16, own, plan->S, stream),
+                      "adamw accum launch");
+}
+
 // ------------------------------------------------------------------ multi-tensor
 
 namespace {

@@ -100,6 +100,18 @@ int launch_gather(const void* param, void* full_at_own, int64_t len, void* strea
 int launch_fused(const AdamCoef& c, const void* const* contribs, int n, float* master, float* m,
                  float* v, void* grad, void* param, void* full_at_own, int64_t len, void* stream);
 
+// Elements one block of the stats kernel reduces (kBlockThreads lanes x 4
+// elements x 16 trips).
+constexpr int64_t kStatsChunk = (int64_t)kBlockThreads * 4 * 16;
+
+int launch_accumulate(const void* const* contribs, int n, float* acc, int first, int64_t len, void* stream);
+int launch_grad_stats(const float* acc, float divisor, double* sumsq_out, int32_t* nonfinite_out, void* workspace,
+                      int64_t len, void* stream);
+int launch_clip_scale(const double* sumsq, const int32_t* nonfinite, int n_ranks, double max_norm, float* scale_out,
+                      int32_t* skip_out, void* stream);
+int launch_adamw_accum(const AdamCoef& c, const float* acc, float divisor, const float* scale, const int32_t* skip,
+                       float* master, float* m, float* v, void* param, void* full_at_own, int64_t len, void* stream);
+
 enum MultiOp : int32_t { kOpReduce = 0, kOpAdamw = 1, kOpGather = 2, kOpFused = 3 };
 int launch_multi(int op, const AdamCoef* c, const void* workspace, int n_chunks, int n_contribs,
                  void* stream);

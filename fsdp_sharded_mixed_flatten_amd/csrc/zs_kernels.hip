@@ -479,6 +479,190 @@ __global__ __launch_bounds__(kBlock) void k_multi(AdamCoef c, const MultiHeader*
     }
 }
 
+// ------------------------------------------------------------------ accumulation and clipping
+
+// One micro-step: acc += f32(bf16(average)) in units of 4 elements; FIRST
+// starts from +0 instead of reading acc.
+template <int N, int U, bool FIRST>
+__device__ __forceinline__ void accum_tile(const void* const* cp, int n_rt, float nf, f32x4* __restrict__ acc,
+                                           int64_t base, int64_t limit) {
+    int64_t u[U];
+    bool ok[U];
+    f32x4 av[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        u[k] = base + (int64_t)k * kBlock;
+        ok[k] = u[k] < limit;
+        av[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (!FIRST && ok[k]) av[k] = ld_state(acc + u[k]);
+    }
+    float a[U][4];
+    rank_sum<u32x2, U, N>(cp, n_rt, u, ok, a);
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        if (!ok[k]) continue;
+        const u32x2 g = avg_bf16x4<N>(a[k], nf);
+        f32x4 r;
+        r.x = av[k].x + lo_bf16(g.x);
+        r.y = av[k].y + hi_bf16(g.x);
+        r.z = av[k].z + lo_bf16(g.y);
+        r.w = av[k].w + hi_bf16(g.y);
+        st_state(acc + u[k], r);
+    }
+}
+
+template <int N, int CAP, bool FIRST>
+__global__ __launch_bounds__(kBlock) void k_accum(Ptrs<CAP> cp, int n_rt, float nf, f32x4* __restrict__ acc,
+                                                  int64_t n4) {
+    accum_tile<N, kFusedU, FIRST>(cp.p, n_rt, nf, acc, tile_base(kFusedU), n4);
+}
+
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+__device__ __forceinline__ int wave_or(int x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x |= __shfl_xor(x, off, 64);
+    return x;
+}
+
+// Block sum over a fixed partition: lane sums, then a wave tree, then (for
+// blocks of several waves) the wave sums in order.
+__device__ __forceinline__ void block_reduce(double& s, int& bad) {
+    s = wave_sum(s);
+    bad = wave_or(bad);
+    if constexpr (kBlock > 64) {
+        __shared__ double ws[kBlock / 64];
+        __shared__ int wb[kBlock / 64];
+        const int w = threadIdx.x / 64;
+        if ((threadIdx.x & 63) == 0) {
+            ws[w] = s;
+            wb[w] = bad;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            s = 0.0;
+            bad = 0;
+            for (int i = 0; i < kBlock / 64; ++i) {
+                s += ws[i];
+                bad |= wb[i];
+            }
+        }
+    }
+}
+
+// Stage 1: block b reduces elements [b*kStatsChunk, (b+1)*kStatsChunk) of the
+// final gradient acc/divisor: partial sum of squares (double) and a flag.
+__global__ __launch_bounds__(kBlock) void k_stats(const f32x4* __restrict__ acc, float divisor, int64_t n4,
+                                                  double* __restrict__ part, int32_t* __restrict__ flags) {
+    const int64_t u0 = (int64_t)blockIdx.x * (kStatsChunk / 4);
+    const int64_t u1 = u0 + kStatsChunk / 4 < n4 ? u0 + kStatsChunk / 4 : n4;
+    double s = 0.0;
+    int bad = 0;
+    for (int64_t u = u0 + threadIdx.x; u < u1; u += kBlock) {
+        const f32x4 x = ld_in(acc + u);
+        const float g[4] = {x.x / divisor, x.y / divisor, x.z / divisor, x.w / divisor};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            bad |= !__builtin_isfinite(g[e]);
+            s = s + (double)g[e] * (double)g[e];
+        }
+    }
+    block_reduce(s, bad);
+    if (threadIdx.x == 0) {
+        part[blockIdx.x] = s;
+        flags[blockIdx.x] = bad;
+    }
+}
+
+// Stage 2 (one block): the partials in a fixed order.
+__global__ __launch_bounds__(kBlock) void k_stats_final(const double* __restrict__ part,
+                                                        const int32_t* __restrict__ flags, int64_t nb,
+                                                        double* __restrict__ sumsq_out,
+                                                        int32_t* __restrict__ nonfinite_out) {
+    double s = 0.0;
+    int bad = 0;
+    for (int64_t i = threadIdx.x; i < nb; i += kBlock) {
+        s = s + part[i];
+        bad |= flags[i];
+    }
+    block_reduce(s, bad);
+    if (threadIdx.x == 0) {
+        *sumsq_out = s;
+        *nonfinite_out = bad ? 1 : 0;
+    }
+}
+
+// One thread: the all-reduced norm (ranks added in order) to an fp32 factor.
+__global__ void k_clip_scale(const double* __restrict__ sumsq, const int32_t* __restrict__ nonfinite, int n,
+                             double max_norm, float* __restrict__ scale_out, int32_t* __restrict__ skip_out) {
+    if (blockIdx.x != 0 || threadIdx.x != 0) return;
+    double total = 0.0;
+    int bad = 0;
+    for (int r = 0; r < n; ++r) {
+        total = total + sumsq[r];
+        bad |= nonfinite[r];
+    }
+    const double coef = max_norm / (sqrt(total) + 1e-6);
+    *scale_out = (float)(coef < 1.0 ? coef : 1.0);
+    *skip_out = bad ? 1 : 0;
+}
+
+// AdamW from the fp32 accumulator: element gradient (acc / divisor) * scale.
+template <int U>
+__device__ __forceinline__ void adamw_accum_tile(const AdamCoef& c, const f32x4* __restrict__ acc, float divisor,
+                                                 float scale, f32x4* __restrict__ master, f32x4* __restrict__ m,
+                                                 f32x4* __restrict__ v, u32x2* __restrict__ param,
+                                                 u32x2* __restrict__ full, int64_t base, int64_t limit) {
+    f32x4 av[U], wv[U], mv[U], vv[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const int64_t u = base + (int64_t)k * kBlock;
+        if (u < limit) {
+            av[k] = ld_in(acc + u);
+            wv[k] = ld_state(master + u);
+            mv[k] = ld_state(m + u);
+            vv[k] = ld_state(v + u);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const int64_t u = base + (int64_t)k * kBlock;
+        if (u >= limit) continue;
+        float w[4] = {wv[k].x, wv[k].y, wv[k].z, wv[k].w};
+        float mm[4] = {mv[k].x, mv[k].y, mv[k].z, mv[k].w};
+        float vv4[4] = {vv[k].x, vv[k].y, vv[k].z, vv[k].w};
+        const float ac[4] = {av[k].x, av[k].y, av[k].z, av[k].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float g = (ac[e] / divisor) * scale;
+            adamw_elem(c, g, w[e], mm[e], vv4[e]);
+        }
+        const f32x4 wn{w[0], w[1], w[2], w[3]};
+        st_state(master + u, wn);
+        st_state(m + u, f32x4{mm[0], mm[1], mm[2], mm[3]});
+        st_state(v + u, f32x4{vv4[0], vv4[1], vv4[2], vv4[3]});
+        const u32x2 p = to_bf16x4(wn);
+        if (param) st_out(param + u, p);
+        if (full) st_out(full + u, p);
+    }
+}
+
+template <int U>
+__global__ __launch_bounds__(kBlock) void k_adamw_accum(AdamCoef c, const f32x4* __restrict__ acc, float divisor,
+                                                        const float* __restrict__ scale_p,
+                                                        const int32_t* __restrict__ skip_p,
+                                                        f32x4* __restrict__ master, f32x4* __restrict__ m,
+                                                        f32x4* __restrict__ v, u32x2* __restrict__ param,
+                                                        u32x2* __restrict__ full, int64_t n4) {
+    if (skip_p && *skip_p) return;  // uniform: the whole grid skips the step
+    const float scale = scale_p ? *scale_p : 1.0f;
+    adamw_accum_tile<U>(c, acc, divisor, scale, master, m, v, param, full, tile_base(U), n4);
+}
+
 // ------------------------------------------------------------------ launch helpers
 
 // Blocks of a tile launch over `units` lane-units, `per_lane` units per lane.
@@ -531,6 +715,20 @@ int launch_multi_op(const AdamCoef& c, const void* ws, int n_chunks, int n, hipS
         case 64: return launch_multi_t<OP, 64>(c, ws, n_chunks, n, s);
         default: return launch_multi_t<OP, 0>(c, ws, n_chunks, n, s);
     }
+}
+
+template <int N, int CAP>
+int launch_accum_t(const void* const* contribs, int n, float* acc, int first, int64_t len, hipStream_t s) {
+    Ptrs<CAP> cp{};
+    for (int q = 0; q < n; ++q) cp.p[q] = contribs[q];
+    const int64_t n4 = len / 4;
+    if (first)
+        hipLaunchKernelGGL((k_accum<N, CAP, true>), dim3(grid_for(n4, kFusedU)), dim3(kBlock), kFusedLds, s, cp, n,
+                           (float)n, reinterpret_cast<f32x4*>(acc), n4);
+    else
+        hipLaunchKernelGGL((k_accum<N, CAP, false>), dim3(grid_for(n4, kFusedU)), dim3(kBlock), kFusedLds, s, cp, n,
+                           (float)n, reinterpret_cast<f32x4*>(acc), n4);
+    return (int)hipGetLastError();
 }
 
 }  // namespace
@@ -605,6 +803,53 @@ int launch_multi(int op, const AdamCoef* c, const void* workspace, int n_chunks,
         case kOpGather: return launch_multi_t<kOpGather, 1>(cc, workspace, n_chunks, 1, s);
         default: return launch_multi_op<kOpFused>(cc, workspace, n_chunks, n_contribs, s);
     }
+}
+
+int launch_accumulate(const void* const* contribs, int n, float* acc, int first, int64_t len, void* stream) {
+    if (len <= 0) return 0;
+    hipStream_t s = (hipStream_t)stream;
+    switch (n) {
+        case 1: return launch_accum_t<1, 1>(contribs, n, acc, first, len, s);
+        case 2: return launch_accum_t<2, 2>(contribs, n, acc, first, len, s);
+        case 4: return launch_accum_t<4, 4>(contribs, n, acc, first, len, s);
+        case 8: return launch_accum_t<8, 8>(contribs, n, acc, first, len, s);
+        case 16: return launch_accum_t<16, 16>(contribs, n, acc, first, len, s);
+        case 32: return launch_accum_t<32, 32>(contribs, n, acc, first, len, s);
+        case 64: return launch_accum_t<64, 64>(contribs, n, acc, first, len, s);
+        default: return launch_accum_t<0, ZS_MAX_CONTRIBS>(contribs, n, acc, first, len, s);
+    }
+}
+
+// The workspace holds nb doubles, then (256-byte aligned) nb int32 flags.
+int launch_grad_stats(const float* acc, float divisor, double* sumsq_out, int32_t* nonfinite_out, void* workspace,
+                      int64_t len, void* stream) {
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t nb = (len + kStatsChunk - 1) / kStatsChunk;
+    double* part = reinterpret_cast<double*>(workspace);
+    int32_t* flags = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + ((nb * 8 + 255) / 256) * 256);
+    if (nb > 0)
+        hipLaunchKernelGGL(k_stats, dim3((unsigned)nb), dim3(kBlock), 0, s, reinterpret_cast<const f32x4*>(acc),
+                           divisor, len / 4, part, flags);
+    hipLaunchKernelGGL(k_stats_final, dim3(1), dim3(kBlock), 0, s, part, flags, nb, sumsq_out, nonfinite_out);
+    return (int)hipGetLastError();
+}
+
+int launch_clip_scale(const double* sumsq, const int32_t* nonfinite, int n_ranks, double max_norm, float* scale_out,
+                      int32_t* skip_out, void* stream) {
+    hipLaunchKernelGGL(k_clip_scale, dim3(1), dim3(64), 0, (hipStream_t)stream, sumsq, nonfinite, n_ranks, max_norm,
+                       scale_out, skip_out);
+    return (int)hipGetLastError();
+}
+
+int launch_adamw_accum(const AdamCoef& c, const float* acc, float divisor, const float* scale, const int32_t* skip,
+                       float* master, float* m, float* v, void* param, void* full_at_own, int64_t len, void* stream) {
+    if (len <= 0) return 0;
+    const int64_t n4 = len / 4;
+    hipLaunchKernelGGL((k_adamw_accum<kAdamwU>), dim3(grid_for(n4, kAdamwU)), dim3(kBlock), kAdamwLds,
+                       (hipStream_t)stream, c, reinterpret_cast<const f32x4*>(acc), divisor, scale, skip,
+                       reinterpret_cast<f32x4*>(master), reinterpret_cast<f32x4*>(m), reinterpret_cast<f32x4*>(v),
+                       reinterpret_cast<u32x2*>(param), reinterpret_cast<u32x2*>(full_at_own), n4);
+    return (int)hipGetLastError();
 }
 
 int copy_h2d_sync(void* dst, const void* src, int64_t bytes, void* stream) {

@@ -217,6 +217,51 @@ zs_status zs_gather_params_multi(const zs_plan* plan, const void* workspace, voi
 zs_status zs_fused_shard_step_multi(const zs_plan* plan, const zs_adamw_hparams* hp,
                                     const void* workspace, void* stream);
 
+/* ------------------------------------------------------------------ accumulation and clipping
+ * Gradient accumulation over G micro-batches with an fp32 gradient shard,
+ * global-norm clipping and a non-finite skip ("从 Data Parallel 到
+ * ZeRO/FSDP", section "Gradient Accumulation 会改变生命周期": every micro-step
+ * reduce-scatters and accumulates on the shard, the loss is divided by G,
+ * clipping uses the norm over all ranks, the overflow decision is shared).
+ * The per-rank squared norms are combined by the caller (an all-reduce of
+ * one double per rank in a multi-GPU job). Scale and skip stay on the device,
+ * so the optimizer step needs no host synchronization. */
+
+/* One micro-step over the bucket [off, off+len) of the shard:
+ * acc_f32[j] = (first ? +0 : acc_f32[j]) + f32(bf16(average of the N
+ * contributions)), the average computed as in zs_reduce_shard. Same argument
+ * rules as zs_reduce_shard. */
+zs_status zs_accumulate_shard(const zs_plan* plan, const void* const* contribs, int32_t n_contribs,
+                              float* acc_f32, int64_t off, int64_t len, int32_t first, void* stream);
+
+/* Device workspace bytes zs_grad_stats needs for this plan. */
+int64_t zs_grad_stats_workspace_bytes(const zs_plan* plan);
+
+/* Over the shard's final gradient g = acc_f32 / grad_divisor (fp32
+ * division): *sumsq_out = sum of g^2 in double (a fixed-order reduction, so
+ * repeated calls give identical bits) and *nonfinite_out = 1 if any g is NaN
+ * or infinite, else 0. sumsq_out (8-byte aligned) and nonfinite_out (4-byte
+ * aligned) are device pointers; both are always written. grad_divisor must
+ * be finite and nonzero. */
+zs_status zs_grad_stats(const zs_plan* plan, const float* acc_f32, float grad_divisor, double* sumsq_out,
+                        int32_t* nonfinite_out, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* From the squared norms of all n_ranks shards (device array, added in rank
+ * order) and their flags (device array): *scale_out = (float) min(1,
+ * max_norm / (sqrt(sum) + 1e-6)) and *skip_out = 1 if any flag is set.
+ * max_norm must be finite and positive; n_ranks >= 1. */
+zs_status zs_clip_scale(const double* sumsq, const int32_t* nonfinite, int32_t n_ranks, double max_norm,
+                        float* scale_out, int32_t* skip_out, void* stream);
+
+/* AdamW from the fp32 accumulator: element gradient (acc_f32[j] /
+ * grad_divisor) * *scale (scale NULL: 1), then the update of
+ * zs_adamw_shard_step. If skip is non-NULL and *skip != 0 nothing is
+ * written. param_bf16 and full_bf16 are optional outputs (full_bf16: FLAT
+ * plans, written at [r*S, (r+1)*S)). */
+zs_status zs_adamw_shard_step_accum(const zs_plan* plan, const zs_adamw_hparams* hp, const float* acc_f32,
+                                    float grad_divisor, const float* scale, const int32_t* skip, float* master,
+                                    float* m, float* v, void* param_bf16, void* full_bf16, void* stream);
+
 /* ------------------------------------------------------------------ misc */
 
 /* Thread-local text describing the last non-OK status of this thread. */
