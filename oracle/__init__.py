@@ -167,20 +167,21 @@ def time_shard_step(hp, contribs, g, master, m, v, p, full, nthreads, reps):
 # ---------------------------------------------------------------- whole plans
 
 
-def plan_step(plan, hp, contribs_by_piece, state_by_piece, full_by_tensor=None):
+def plan_step(plan, hp, contribs_by_piece, state_by_piece, full_by_tensor=None, hp_of_piece=None):
     """One shard step over every owned piece of a PER_TENSOR or FLAT plan.
 
     contribs_by_piece[i] is the list of N bf16 arrays of piece i (length = piece
     length); state_by_piece[i] = (g, master, m, v, p) arrays of piece i; the
     gathered tensor i (padded, T_i) receives the piece at own_lo when
-    full_by_tensor is given.
+    full_by_tensor is given. hp_of_piece optionally gives each piece its own
+    hyperparameters (parameter groups).
     """
     for k, pc in enumerate(plan.pieces):
         g, master, m, v, p = state_by_piece[k]
         if g.size == 0:
             continue
         reduce(contribs_by_piece[k], out=g)
-        adamw(hp, g, master, m, v, p)
+        adamw(hp if hp_of_piece is None else hp_of_piece[k], g, master, m, v, p)
         if full_by_tensor is not None:
             full_by_tensor[pc.tensor][pc.own_lo:pc.own_hi] = p
 

@@ -93,7 +93,11 @@ def plan_flat(numels, world, rank, align=1):
     return OraclePlan("flat", world, rank, align, list(numels), offs, [], T, S, pieces)
 
 
-def plan_per_tensor(numels, world, rank):
+def plan_per_tensor(numels, world, rank, persist_below=0):
+    """PER_TENSOR plan. Tensors with fewer than ``persist_below`` elements are
+    not sharded: every rank holds and updates the whole tensor, padded to one
+    16-byte vector ("ZeRO vs FSDP..." section 7: small parameters such as
+    norms stay replicated under a persistence threshold)."""
     if world < 1 or not (0 <= rank < world):
         raise ValueError("bad world/rank")
     padded, offs, pieces = [], [], []
@@ -102,6 +106,14 @@ def plan_per_tensor(numels, world, rank):
     for i, n in enumerate(numels):
         if n < 0:
             raise ValueError("negative numel")
+        if n < persist_below:
+            Ti = roundup(n, SHARD_GRANULE)
+            padded.append(Ti)
+            offs.append(full_acc)
+            pieces.append(OraclePiece(i, 0, Ti, 0, n, shard_acc, full_acc))
+            shard_acc += Ti
+            full_acc += Ti
+            continue
         Ti = roundup(n, world * SHARD_GRANULE)
         Si = Ti // world
         padded.append(Ti)
