@@ -22,6 +22,7 @@ LIB_PATH = os.environ.get("ZS_LIB") or os.path.join(_HERE, "libzs.so")
 ZS_OK, ZS_EINVAL, ZS_EALIGN, ZS_ERANGE, ZS_EHIP, ZS_ENOMEM = 0, -1, -2, -3, -4, -5
 ZS_LAYOUT_FLAT, ZS_LAYOUT_PER_TENSOR = 0, 1
 ZS_MAX_CONTRIBS = 256
+ZS_MAX_GROUPS = 8
 
 _STATUS_NAMES = {0: "ZS_OK", -1: "ZS_EINVAL", -2: "ZS_EALIGN", -3: "ZS_ERANGE", -4: "ZS_EHIP",
                  -5: "ZS_ENOMEM"}
@@ -52,6 +53,11 @@ class TensorInfo(ctypes.Structure):
                 ("own_hi", ctypes.c_int64), ("shard_off", ctypes.c_int64)]
 
 
+class PlanOptions(ctypes.Structure):
+    _fields_ = [("layout", ctypes.c_int32), ("tensor_align_elems", ctypes.c_int32),
+                ("persist_below_elems", ctypes.c_int64), ("groups", ctypes.POINTER(ctypes.c_int32))]
+
+
 class PiecePtrs(ctypes.Structure):
     _fields_ = [("grad", ctypes.c_void_p), ("master", ctypes.c_void_p), ("m", ctypes.c_void_p),
                 ("v", ctypes.c_void_p), ("param", ctypes.c_void_p), ("full", ctypes.c_void_p)]
@@ -66,6 +72,10 @@ def _load():
     st = ctypes.c_int
     sigs = {
         "zs_shard_plan": (st, [ctypes.POINTER(i64), i32, i32, i32, i32, i32, ctypes.POINTER(vp)]),
+        "zs_shard_plan_ex": (st, [ctypes.POINTER(i64), i32, i32, i32, ctypes.POINTER(PlanOptions),
+                                  ctypes.POINTER(vp)]),
+        "zs_plan_tensor_group": (i32, [vp, i32]),
+        "zs_plan_tensor_replicated": (i32, [vp, i32]),
         "zs_plan_destroy": (None, [vp]),
         "zs_plan_padded_numel": (i64, [vp]),
         "zs_plan_shard_numel": (i64, [vp]),
@@ -86,6 +96,8 @@ def _load():
         "zs_adamw_shard_step_multi": (st, [vp, ctypes.POINTER(AdamWHParams), vp, vp]),
         "zs_gather_params_multi": (st, [vp, vp, vp]),
         "zs_fused_shard_step_multi": (st, [vp, ctypes.POINTER(AdamWHParams), vp, vp]),
+        "zs_adamw_shard_step_multi_groups": (st, [vp, ctypes.POINTER(AdamWHParams), i32, vp, vp]),
+        "zs_fused_shard_step_multi_groups": (st, [vp, ctypes.POINTER(AdamWHParams), i32, vp, vp]),
         "zs_accumulate_shard": (st, [vp, ctypes.POINTER(vp), i32, vp, i64, i64, i32, vp]),
         "zs_grad_stats_workspace_bytes": (i64, [vp]),
         "zs_grad_stats": (st, [vp, vp, ctypes.c_float, vp, vp, vp, i64, vp]),
@@ -103,12 +115,14 @@ def _load():
 
 
 _lib = _load()
-EXPORTED = ("zs_shard_plan", "zs_plan_destroy", "zs_plan_padded_numel", "zs_plan_shard_numel",
+EXPORTED = ("zs_shard_plan", "zs_shard_plan_ex", "zs_plan_tensor_group", "zs_plan_tensor_replicated",
+            "zs_plan_destroy", "zs_plan_padded_numel", "zs_plan_shard_numel",
             "zs_plan_persistent_bytes", "zs_plan_num_tensors", "zs_plan_world_size", "zs_plan_rank",
             "zs_plan_layout", "zs_plan_tensor", "zs_reduce_shard", "zs_adamw_shard_step",
             "zs_gather_params", "zs_fused_shard_step", "zs_multi_workspace_bytes", "zs_multi_bind",
             "zs_reduce_shard_multi", "zs_adamw_shard_step_multi", "zs_gather_params_multi",
-            "zs_fused_shard_step_multi", "zs_accumulate_shard", "zs_grad_stats_workspace_bytes",
+            "zs_fused_shard_step_multi", "zs_adamw_shard_step_multi_groups",
+            "zs_fused_shard_step_multi_groups", "zs_accumulate_shard", "zs_grad_stats_workspace_bytes",
             "zs_grad_stats", "zs_clip_scale", "zs_adamw_shard_step_accum", "zs_last_error", "zs_version")
 
 
@@ -223,12 +237,38 @@ class Plan:
         _check(_lib.zs_plan_tensor(self.handle, i, ctypes.byref(info)))
         return info
 
+    def tensor_group(self, i):
+        g = _lib.zs_plan_tensor_group(self.handle, i)
+        if g < 0:
+            raise IndexError(f"tensor {i} is not in the plan")
+        return g
+
+    def tensor_replicated(self, i):
+        r = _lib.zs_plan_tensor_replicated(self.handle, i)
+        if r < 0:
+            raise IndexError(f"tensor {i} is not in the plan")
+        return bool(r)
+
 
 def zs_shard_plan(numels, world_size, rank, tensor_align_elems=1, layout=ZS_LAYOUT_FLAT):
     arr = (ctypes.c_int64 * max(len(numels), 1))(*numels)
     out = ctypes.c_void_p()
     _check(_lib.zs_shard_plan(arr, len(numels), world_size, rank, tensor_align_elems, layout,
                               ctypes.byref(out)))
+    return Plan(out.value)
+
+
+def zs_shard_plan_ex(numels, world_size, rank, layout=ZS_LAYOUT_PER_TENSOR, tensor_align_elems=1,
+                     persist_below_elems=0, groups=None):
+    arr = (ctypes.c_int64 * max(len(numels), 1))(*numels)
+    opt = PlanOptions(layout, tensor_align_elems, persist_below_elems, None)
+    if groups is not None:
+        if len(groups) != len(numels):
+            raise ValueError(f"groups has {len(groups)} entries for {len(numels)} tensors")
+        garr = (ctypes.c_int32 * max(len(groups), 1))(*groups)
+        opt.groups = ctypes.cast(garr, ctypes.POINTER(ctypes.c_int32))
+    out = ctypes.c_void_p()
+    _check(_lib.zs_shard_plan_ex(arr, len(numels), world_size, rank, ctypes.byref(opt), ctypes.byref(out)))
     return Plan(out.value)
 
 
@@ -329,6 +369,22 @@ def zs_gather_params_multi(plan, workspace, stream=None):
 def zs_fused_shard_step_multi(plan, hp, workspace, stream=None):
     _check(_lib.zs_fused_shard_step_multi(plan.handle, ctypes.byref(hp), workspace.data_ptr(),
                                           _stream(stream)))
+
+
+def _hp_array(hps):
+    if not hps:
+        raise ValueError("at least one set of hyperparameters is needed")
+    return (AdamWHParams * len(hps))(*hps), len(hps)
+
+
+def zs_adamw_shard_step_multi_groups(plan, hps, workspace, stream=None):
+    arr, n = _hp_array(hps)
+    _check(_lib.zs_adamw_shard_step_multi_groups(plan.handle, arr, n, workspace.data_ptr(), _stream(stream)))
+
+
+def zs_fused_shard_step_multi_groups(plan, hps, workspace, stream=None):
+    arr, n = _hp_array(hps)
+    _check(_lib.zs_fused_shard_step_multi_groups(plan.handle, arr, n, workspace.data_ptr(), _stream(stream)))
 
 
 # ---------------------------------------------------------------- accumulation and clipping

@@ -113,9 +113,12 @@ const char* zs_version(void) { return "0.1.0"; }
 
 // ------------------------------------------------------------------ plan
 
-zs_status zs_shard_plan(const int64_t* numels, int32_t n_tensors, int32_t world_size, int32_t rank,
-                        int32_t tensor_align_elems, int32_t layout, zs_plan** out) {
+zs_status zs_shard_plan_ex(const int64_t* numels, int32_t n_tensors, int32_t world_size, int32_t rank,
+                           const zs_plan_options* opt, zs_plan** out) {
     if (!out) return fail(ZS_EINVAL, "out is NULL");
+    if (!opt) return fail(ZS_EINVAL, "options is NULL");
+    const int32_t layout = opt->layout;
+    const int32_t tensor_align_elems = opt->tensor_align_elems;
     if (n_tensors < 0) return fail(ZS_EINVAL, "n_tensors = %d is negative", n_tensors);
     if (n_tensors > 0 && !numels) return fail(ZS_EINVAL, "numels is NULL");
     if (world_size < 1) return fail(ZS_EINVAL, "world_size = %d must be >= 1", world_size);
@@ -125,9 +128,15 @@ zs_status zs_shard_plan(const int64_t* numels, int32_t n_tensors, int32_t world_
         return fail(ZS_EINVAL, "unknown layout %d", layout);
     if (layout == ZS_LAYOUT_FLAT && tensor_align_elems < 1)
         return fail(ZS_EINVAL, "tensor_align_elems = %d must be >= 1", tensor_align_elems);
-    for (int32_t i = 0; i < n_tensors; ++i)
+    if (opt->persist_below_elems < 0) return fail(ZS_EINVAL, "persist_below_elems is negative");
+    if (layout == ZS_LAYOUT_FLAT && (opt->persist_below_elems > 0 || opt->groups))
+        return fail(ZS_EINVAL, "a persistence threshold and groups need a PER_TENSOR plan");
+    for (int32_t i = 0; i < n_tensors; ++i) {
         if (numels[i] < 0 || numels[i] > kMaxElems)
             return fail(ZS_EINVAL, "numels[%d] = %lld out of range", i, (long long)numels[i]);
+        if (opt->groups && (opt->groups[i] < 0 || opt->groups[i] >= ZS_MAX_GROUPS))
+            return fail(ZS_EINVAL, "groups[%d] = %d outside [0, %d)", i, opt->groups[i], ZS_MAX_GROUPS);
+    }
 
     zs_plan* p = new (std::nothrow) zs_plan();
     if (!p) return fail(ZS_ENOMEM, "out of host memory");
@@ -170,10 +179,19 @@ zs_status zs_shard_plan(const int64_t* numels, int32_t n_tensors, int32_t world_
             for (int32_t i = 0; i < n_tensors; ++i) {
                 zs::TensorEntry& t = p->tensors[(size_t)i];
                 t.numel = numels[i];
-                t.padded = roundup(t.numel, granule);
+                t.group = opt->groups ? opt->groups[i] : 0;
+                t.replicated = t.numel < opt->persist_below_elems ? 1 : 0;
                 t.flat_off = full;
-                const int64_t Si = t.padded / world_size;
-                t.own_lo = (int64_t)rank * Si;
+                int64_t Si;
+                if (t.replicated) {
+                    t.padded = roundup(t.numel, 8);
+                    Si = t.padded;
+                    t.own_lo = 0;
+                } else {
+                    t.padded = roundup(t.numel, granule);
+                    Si = t.padded / world_size;
+                    t.own_lo = (int64_t)rank * Si;
+                }
                 t.own_hi = t.own_lo + Si;
                 t.shard_off = shard;
                 full += t.padded;
@@ -198,6 +216,26 @@ zs_status zs_shard_plan(const int64_t* numels, int32_t n_tensors, int32_t world_
     }
     *out = p;
     return ZS_OK;
+}
+
+zs_status zs_shard_plan(const int64_t* numels, int32_t n_tensors, int32_t world_size, int32_t rank,
+                        int32_t tensor_align_elems, int32_t layout, zs_plan** out) {
+    zs_plan_options o;
+    o.layout = layout;
+    o.tensor_align_elems = tensor_align_elems;
+    o.persist_below_elems = 0;
+    o.groups = nullptr;
+    return zs_shard_plan_ex(numels, n_tensors, world_size, rank, &o, out);
+}
+
+int32_t zs_plan_tensor_group(const zs_plan* p, int32_t i) {
+    if (!p || i < 0 || i >= (int32_t)p->tensors.size()) return -1;
+    return p->tensors[(size_t)i].group;
+}
+
+int32_t zs_plan_tensor_replicated(const zs_plan* p, int32_t i) {
+    if (!p || i < 0 || i >= (int32_t)p->tensors.size()) return -1;
+    return p->tensors[(size_t)i].replicated;
 }
 
 void zs_plan_destroy(zs_plan* plan) {
@@ -495,6 +533,8 @@ zs_status zs_multi_bind(const zs_plan* plan, const zs_piece_ptrs* pieces, const 
         pd[i].param = pc.param;
         pd[i].full_own = pc.full ? static_cast<char*>(pc.full) + 2 * t.own_lo : nullptr;
         pd[i].len = t.own_hi - t.own_lo;
+        pd[i].group = t.group;
+        pd[i].pad_ = 0;
         for (int32_t q = 0; q < n_contribs; ++q) cd[(int64_t)i * n_contribs + q] = contribs[(int64_t)q * n + i];
     }
     std::memcpy(host.data() + L.chunks_off, plan->chunks.data(), plan->chunks.size() * sizeof(zs::Chunk));
@@ -519,8 +559,9 @@ zs_status zs_adamw_shard_step_multi(const zs_plan* plan, const zs_adamw_hparams*
     if (zs_status st = check_hp(hp)) return st;
     Binding b;
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasGrad | zs::kHasState, &b)) return st;
-    const zs::AdamCoef c = zs::make_coef(*hp);
-    return hip_status(zs::launch_multi(zs::kOpAdamw, &c, workspace, (int)plan->chunks.size(), b.n_contribs, stream),
+    zs::CoefTable ct;
+    for (auto& e : ct.c) e = zs::make_coef(*hp);
+    return hip_status(zs::launch_multi(zs::kOpAdamw, &ct, workspace, (int)plan->chunks.size(), b.n_contribs, stream),
                       "multi adamw launch");
 }
 
@@ -538,8 +579,49 @@ zs_status zs_fused_shard_step_multi(const zs_plan* plan, const zs_adamw_hparams*
     if (zs_status st = check_hp(hp)) return st;
     Binding b;
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasContribs | zs::kHasState, &b)) return st;
-    const zs::AdamCoef c = zs::make_coef(*hp);
-    return hip_status(zs::launch_multi(zs::kOpFused, &c, workspace, (int)plan->chunks.size(), b.n_contribs, stream),
+    zs::CoefTable ct;
+    for (auto& e : ct.c) e = zs::make_coef(*hp);
+    return hip_status(zs::launch_multi(zs::kOpFused, &ct, workspace, (int)plan->chunks.size(), b.n_contribs, stream),
+                      "multi fused launch");
+}
+
+namespace {
+
+zs_status group_table(const zs_plan* plan, const zs_adamw_hparams* hps, int32_t n_groups, zs::CoefTable* ct) {
+    if (!hps) return fail(ZS_EINVAL, "hparams array is NULL");
+    if (n_groups < 1 || n_groups > ZS_MAX_GROUPS)
+        return fail(ZS_EINVAL, "n_groups = %d outside [1, %d]", n_groups, ZS_MAX_GROUPS);
+    for (const auto& t : plan->tensors)
+        if (t.group >= n_groups)
+            return fail(ZS_EINVAL, "the plan uses group %d but only %d sets of hyperparameters were given", t.group,
+                        n_groups);
+    for (int32_t g = 0; g < n_groups; ++g)
+        if (zs_status st = check_hp(&hps[g])) return st;
+    for (int32_t g = 0; g < ZS_MAX_GROUPS; ++g) ct->c[g] = zs::make_coef(hps[g < n_groups ? g : 0]);
+    return ZS_OK;
+}
+
+}  // namespace
+
+zs_status zs_adamw_shard_step_multi_groups(const zs_plan* plan, const zs_adamw_hparams* hps, int32_t n_groups,
+                                           const void* workspace, void* stream) {
+    if (zs_status st = check_multi_plan(plan)) return st;
+    zs::CoefTable ct;
+    if (zs_status st = group_table(plan, hps, n_groups, &ct)) return st;
+    Binding b;
+    if (zs_status st = lookup_binding(plan, workspace, zs::kHasGrad | zs::kHasState, &b)) return st;
+    return hip_status(zs::launch_multi(zs::kOpAdamw, &ct, workspace, (int)plan->chunks.size(), b.n_contribs, stream),
+                      "multi adamw launch");
+}
+
+zs_status zs_fused_shard_step_multi_groups(const zs_plan* plan, const zs_adamw_hparams* hps, int32_t n_groups,
+                                           const void* workspace, void* stream) {
+    if (zs_status st = check_multi_plan(plan)) return st;
+    zs::CoefTable ct;
+    if (zs_status st = group_table(plan, hps, n_groups, &ct)) return st;
+    Binding b;
+    if (zs_status st = lookup_binding(plan, workspace, zs::kHasContribs | zs::kHasState, &b)) return st;
+    return hip_status(zs::launch_multi(zs::kOpFused, &ct, workspace, (int)plan->chunks.size(), b.n_contribs, stream),
                       "multi fused launch");
 }
 

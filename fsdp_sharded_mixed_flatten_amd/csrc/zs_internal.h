@@ -17,7 +17,14 @@ struct AdamCoef {
 
 AdamCoef make_coef(const zs_adamw_hparams& hp);
 
+// Per-group AdamW scalars, passed by value to the multi-tensor kernel.
+struct CoefTable {
+    AdamCoef c[ZS_MAX_GROUPS];
+};
+
 struct TensorEntry {
+    int32_t group = 0;       // hyperparameter group
+    int32_t replicated = 0;  // 1: held whole by every rank (persistence threshold)
     int64_t numel;
     int64_t flat_off;  // FLAT: start in the flat buffer; PER_TENSOR: packed start of padded tensor
     int64_t padded;    // PER_TENSOR: T_i; FLAT: numel
@@ -80,6 +87,8 @@ struct PieceDev {
     void* param;
     void* full_own;  // gathered tensor + r*S_i (already offset)
     int64_t len;     // S_i
+    int32_t group;   // index into the kernel's coefficient table
+    int32_t pad_;
 };
 
 enum MultiFlags : int32_t {
@@ -113,7 +122,7 @@ int launch_adamw_accum(const AdamCoef& c, const float* acc, float divisor, const
                        float* master, float* m, float* v, void* param, void* full_at_own, int64_t len, void* stream);
 
 enum MultiOp : int32_t { kOpReduce = 0, kOpAdamw = 1, kOpGather = 2, kOpFused = 3 };
-int launch_multi(int op, const AdamCoef* c, const void* workspace, int n_chunks, int n_contribs,
+int launch_multi(int op, const CoefTable* c, const void* workspace, int n_chunks, int n_contribs,
                  void* stream);
 int copy_h2d_sync(void* dst, const void* src, int64_t bytes, void* stream);
 const char* hip_error_text(int err);

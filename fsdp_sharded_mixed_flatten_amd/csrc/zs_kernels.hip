@@ -448,11 +448,12 @@ __global__ __launch_bounds__(kBlock) void k_fused(AdamCoef c, Ptrs<CAP> cp, int 
 // 4 elements) of one piece. The piece supplies every pointer; the
 // contributions of piece i are cps[i * N .. i * N + N).
 template <int OP, int N>
-__global__ __launch_bounds__(kBlock) void k_multi(AdamCoef c, const MultiHeader* __restrict__ hdr,
+__global__ __launch_bounds__(kBlock) void k_multi(CoefTable ct, const MultiHeader* __restrict__ hdr,
                                                   int n_rt, float nf) {
     const char* ws = reinterpret_cast<const char*>(hdr);
     const Chunk ch = reinterpret_cast<const Chunk*>(ws + hdr->chunks_off)[blockIdx.x];
     const PieceDev pc = reinterpret_cast<const PieceDev*>(ws + hdr->pieces_off)[ch.piece];
+    const AdamCoef c = ct.c[pc.group];
     const int flags = hdr->flags;
     const int64_t u0 = ch.start >> 2;  // chunk start and length are multiples of 8
     const int64_t base = u0 + threadIdx.x;
@@ -697,14 +698,14 @@ int launch_fused_t(const AdamCoef& c, const void* const* contribs, int n, float*
 }
 
 template <int OP, int N>
-int launch_multi_t(const AdamCoef& c, const void* ws, int n_chunks, int n, hipStream_t s) {
+int launch_multi_t(const CoefTable& c, const void* ws, int n_chunks, int n, hipStream_t s) {
     hipLaunchKernelGGL((k_multi<OP, N>), dim3((unsigned)n_chunks), dim3(kBlock), kMultiLds, s, c,
                        reinterpret_cast<const MultiHeader*>(ws), n, (float)n);
     return (int)hipGetLastError();
 }
 
 template <int OP>
-int launch_multi_op(const AdamCoef& c, const void* ws, int n_chunks, int n, hipStream_t s) {
+int launch_multi_op(const CoefTable& c, const void* ws, int n_chunks, int n, hipStream_t s) {
     switch (n) {
         case 1: return launch_multi_t<OP, 1>(c, ws, n_chunks, n, s);
         case 2: return launch_multi_t<OP, 2>(c, ws, n_chunks, n, s);
@@ -793,9 +794,9 @@ int launch_fused(const AdamCoef& c, const void* const* contribs, int n, float* m
     }
 }
 
-int launch_multi(int op, const AdamCoef* c, const void* workspace, int n_chunks, int n_contribs, void* stream) {
+int launch_multi(int op, const CoefTable* c, const void* workspace, int n_chunks, int n_contribs, void* stream) {
     if (n_chunks <= 0) return 0;
-    const AdamCoef cc = c ? *c : AdamCoef{};
+    const CoefTable cc = c ? *c : CoefTable{};
     hipStream_t s = (hipStream_t)stream;
     switch (op) {
         case kOpReduce: return launch_multi_op<kOpReduce>(cc, workspace, n_chunks, n_contribs, s);

@@ -62,6 +62,8 @@ extern "C" {
 
 /* Largest number of gradient contributions (world size) one call accepts. */
 #define ZS_MAX_CONTRIBS 256
+/* Hyperparameter groups a PER_TENSOR plan can hold. */
+#define ZS_MAX_GROUPS 8
 
 typedef enum zs_status {
     ZS_OK = 0,
@@ -127,6 +129,35 @@ typedef struct zs_tensor_info {
 zs_status zs_shard_plan(const int64_t* numels, int32_t n_tensors, int32_t world_size, int32_t rank,
                         int32_t tensor_align_elems, int32_t layout, zs_plan** out);
 void zs_plan_destroy(zs_plan* plan);
+
+/* Plan options beyond zs_shard_plan's arguments. */
+typedef struct zs_plan_options {
+    int32_t layout;             /* ZS_LAYOUT_FLAT or ZS_LAYOUT_PER_TENSOR */
+    int32_t tensor_align_elems; /* FLAT: tensor-start alignment (>= 1); ignored otherwise */
+    /* PER_TENSOR only: a tensor with fewer elements than this is not sharded
+     * but replicated -- every rank holds the whole tensor, padded to a
+     * multiple of 8, reduces all of it and updates it, and its gathered copy
+     * is written whole ("ZeRO vs FSDP...", section 7: a persistence threshold
+     * keeps small parameters such as norms replicated). 0: shard everything. */
+    int64_t persist_below_elems;
+    /* PER_TENSOR only: hyperparameter group of each tensor, each in
+     * [0, ZS_MAX_GROUPS), or NULL (every tensor in group 0). The *_groups
+     * multi-tensor calls take one zs_adamw_hparams per group (e.g. no weight
+     * decay for norms and biases). */
+    const int32_t* groups;
+} zs_plan_options;
+
+/* zs_shard_plan with options; zs_shard_plan(numels, n, N, r, align, layout, out)
+ * equals this call with {layout, align, 0, NULL}. A replicated tensor i has
+ * padded_numel = roundup(numel, 8), own range [0, padded_numel) and a
+ * gathered copy of padded_numel elements; the ledger counts it in full. */
+zs_status zs_shard_plan_ex(const int64_t* numels, int32_t n_tensors, int32_t world_size, int32_t rank,
+                           const zs_plan_options* options, zs_plan** out);
+/* zs_plan_tensor_group: the hyperparameter group of tensor i.
+ * zs_plan_tensor_replicated: 1 if tensor i is replicated, 0 if sharded.
+ * Both give -1 on a NULL plan or an index out of range. */
+int32_t zs_plan_tensor_group(const zs_plan* plan, int32_t i);
+int32_t zs_plan_tensor_replicated(const zs_plan* plan, int32_t i);
 
 /* Queries (host only; a NULL plan gives -1). */
 int64_t zs_plan_padded_numel(const zs_plan* plan);     /* T */
@@ -216,6 +247,14 @@ zs_status zs_gather_params_multi(const zs_plan* plan, const void* workspace, voi
  * and full only where those fields were bound non-NULL. */
 zs_status zs_fused_shard_step_multi(const zs_plan* plan, const zs_adamw_hparams* hp,
                                     const void* workspace, void* stream);
+/* As zs_adamw_shard_step_multi / zs_fused_shard_step_multi with one set of
+ * hyperparameters per group: piece i uses hps[group of tensor i]. n_groups
+ * must exceed every group id of the plan (<= ZS_MAX_GROUPS). The calls
+ * without _groups apply their single hp to every group. */
+zs_status zs_adamw_shard_step_multi_groups(const zs_plan* plan, const zs_adamw_hparams* hps, int32_t n_groups,
+                                           const void* workspace, void* stream);
+zs_status zs_fused_shard_step_multi_groups(const zs_plan* plan, const zs_adamw_hparams* hps, int32_t n_groups,
+                                           const void* workspace, void* stream);
 
 /* ------------------------------------------------------------------ accumulation and clipping
  * Gradient accumulation over G micro-batches with an fp32 gradient shard,

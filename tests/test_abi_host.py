@@ -82,6 +82,72 @@ def test_plan_matches_oracle_random(zs, seed):
     _compare_plan(zs, numels, world, rank, align, zs.ZS_LAYOUT_PER_TENSOR)
 
 
+@pytest.mark.parametrize("seed", range(30))
+def test_plan_ex_matches_oracle_random(zs, seed):
+    """Persistence threshold and groups against the oracle's per-tensor plan."""
+    rnd = random.Random(1000 + seed)
+    numels = [rnd.choice([0, 1, 5, 8, 9, 64, 100, 768, 4093, 65536, 100_003]) for _ in range(rnd.randint(0, 15))]
+    world = rnd.choice([1, 2, 3, 4, 5, 7, 8, 16, 64, 100, 256])
+    rank = rnd.randrange(world)
+    persist = rnd.choice([0, 1, 9, 100, 769, 70_000, 1 << 40])
+    groups = [rnd.randrange(zs.ZS_MAX_GROUPS) for _ in numels]
+    p = zs.zs_shard_plan_ex(numels, world, rank, persist_below_elems=persist, groups=groups)
+    o = plan_per_tensor(numels, world, rank, persist)
+    assert (p.padded_numel, p.shard_numel, p.persistent_bytes) == (o.T, o.S, o.persistent_bytes)
+    for i, pc in enumerate(o.pieces):
+        info = p.tensor(i)
+        assert (info.flat_off, info.padded_numel) == (o.offsets[i], o.padded[i])
+        assert (info.own_lo, info.own_hi, info.shard_off) == (pc.own_lo, pc.own_hi, pc.shard_off)
+        assert info.flat_off + info.own_lo == pc.full_off
+        assert p.tensor_group(i) == groups[i]
+        assert p.tensor_replicated(i) == (numels[i] < persist)
+
+
+def test_plan_ex_defaults_equal_plan(zs):
+    numels = shapes.tiny()
+    a = zs.zs_shard_plan(numels, 8, 3, 1, zs.ZS_LAYOUT_PER_TENSOR)
+    b = zs.zs_shard_plan_ex(numels, 8, 3)
+    for i in range(len(numels)):
+        x, y = a.tensor(i), b.tensor(i)
+        assert [getattr(x, f) for f, _ in x._fields_] == [getattr(y, f) for f, _ in y._fields_]
+        assert b.tensor_group(i) == 0 and not b.tensor_replicated(i)
+    c = zs.zs_shard_plan_ex(numels, 8, 3, layout=zs.ZS_LAYOUT_FLAT, tensor_align_elems=64)
+    d = zs.zs_shard_plan(numels, 8, 3, 64, zs.ZS_LAYOUT_FLAT)
+    assert (c.padded_numel, c.shard_numel) == (d.padded_numel, d.shard_numel)
+    with pytest.raises(IndexError):
+        b.tensor_group(len(numels))
+
+
+def test_plan_ex_rejects_bad_options(zs):
+    bad = [dict(layout=zs.ZS_LAYOUT_FLAT, persist_below_elems=10), dict(layout=zs.ZS_LAYOUT_FLAT, groups=[0, 0]),
+           dict(groups=[0, zs.ZS_MAX_GROUPS]), dict(groups=[-1, 0]), dict(persist_below_elems=-1),
+           dict(layout=5)]
+    for kw in bad:
+        with pytest.raises(zs.ZsError) as e:
+            zs.zs_shard_plan_ex([10, 20], 4, 1, **kw)
+        assert e.value.status == zs.ZS_EINVAL and e.value.message
+    with pytest.raises(ValueError):
+        zs.zs_shard_plan_ex([10, 20], 4, 1, groups=[0])
+
+
+def test_group_calls_validate_without_device(zs):
+    L = zs.lib()
+    plan = zs.zs_shard_plan_ex([1000, 10], 4, 1, persist_below_elems=64, groups=[0, 2])
+    flat = zs.zs_shard_plan([1000], 4, 1)
+    hp3 = (zs.AdamWHParams * 3)(zs.AdamWHParams(), zs.AdamWHParams(), zs.AdamWHParams())
+    for fn in (L.zs_adamw_shard_step_multi_groups, L.zs_fused_shard_step_multi_groups):
+        assert fn(plan.handle, hp3, 2, FAKE, None) == zs.ZS_EINVAL  # group 2 has no hyperparameters
+        assert fn(plan.handle, hp3, 0, FAKE, None) == zs.ZS_EINVAL
+        assert fn(plan.handle, hp3, zs.ZS_MAX_GROUPS + 1, FAKE, None) == zs.ZS_EINVAL
+        assert fn(plan.handle, None, 3, FAKE, None) == zs.ZS_EINVAL
+        assert fn(flat.handle, hp3, 3, FAKE, None) == zs.ZS_EINVAL  # FLAT plans have no multi-tensor form
+        hp3[1] = zs.AdamWHParams(step=0)
+        assert fn(plan.handle, hp3, 3, FAKE, None) == zs.ZS_EINVAL
+        hp3[1] = zs.AdamWHParams()
+        assert fn(plan.handle, hp3, 3, FAKE, None) == zs.ZS_EINVAL  # workspace never bound
+        assert b"never bound" in L.zs_last_error()
+
+
 def test_plan_rejects_bad_arguments(zs):
     for args in (([10], 0, 0, 1, 0), ([10], 4, 4, 1, 0), ([10], 4, -1, 1, 0), ([10], 4, 0, 0, 0),
                  ([-1], 4, 0, 1, 0), ([10], 4, 0, 1, 7)):

@@ -291,11 +291,19 @@ def _small_model(H=256, I=688, V=1000, L=2):
 
 
 class MultiRun:
-    def __init__(self, zs, numels, world, rank, steps, seed, hp):
+    """PER_TENSOR multi-tensor step against the oracle. With ``hps`` (one set
+    of hyperparameters per group) the *_groups calls run and piece i uses
+    hps[groups[i]]; ``persist_below`` replicates the small tensors."""
+
+    def __init__(self, zs, numels, world, rank, steps, seed, hp, persist_below=0, groups=None, hps=None):
         import torch
         self.zs, self.hp, self.world, self.rank = zs, hp, world, rank
-        self.plan = zs.zs_shard_plan(numels, world, rank, 1, zs.ZS_LAYOUT_PER_TENSOR)
-        self.oplan = oracle.plan_per_tensor(numels, world, rank)
+        self.groups, self.hps = groups, hps
+        if persist_below or groups is not None:
+            self.plan = zs.zs_shard_plan_ex(numels, world, rank, persist_below_elems=persist_below, groups=groups)
+        else:
+            self.plan = zs.zs_shard_plan(numels, world, rank, 1, zs.ZS_LAYOUT_PER_TENSOR)
+        self.oplan = oracle.plan_per_tensor(numels, world, rank, persist_below)
         self.pieces = []
         self.o = []
         self.contribs = {}
@@ -324,14 +332,24 @@ class MultiRun:
     def step(self, t, fused):
         zs = self.zs
         hp = self.hp.at(t)
-        if fused:
+        hps = None if self.hps is None else [x.at(t) for x in self.hps]
+        if fused and hps is None:
             zs.zs_fused_shard_step_multi(self.plan, hp, self.ws[t])
+        elif fused:
+            zs.zs_fused_shard_step_multi_groups(self.plan, hps, self.ws[t])
         else:
             zs.zs_reduce_shard_multi(self.plan, self.ws[t])
-            zs.zs_adamw_shard_step_multi(self.plan, hp, self.ws[t])
+            if hps is None:
+                zs.zs_adamw_shard_step_multi(self.plan, hp, self.ws[t])
+            else:
+                zs.zs_adamw_shard_step_multi_groups(self.plan, hps, self.ws[t])
             zs.zs_gather_params_multi(self.plan, self.ws[t])
-        h = oracle.HParams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, t)
+
+        def ohp(x):
+            return oracle.HParams(x.lr, x.beta1, x.beta2, x.eps, x.weight_decay, t)
+
         for i, pc in enumerate(self.oplan.pieces):
+            h = ohp(hp) if hps is None else ohp(hps[self.groups[pc.tensor] if self.groups else 0])
             o = self.o[i]
             if o["g"].size == 0:
                 continue
@@ -366,6 +384,38 @@ def test_multi_tensor_runtime_world(zs):
     run = MultiRun(zs, _small_model(H=128, I=344, V=300, L=1), 5, 4, 1, 78, _hp(zs))
     run.step(1, True)
     run.check()
+
+
+def _norm_groups(numels, H):
+    """Group 1 (no weight decay, other lr) for vectors such as norm weights, group 0 otherwise."""
+    return [1 if n <= H or n in (1000, 3) else 0 for n in numels]
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_multi_tensor_persistence_and_groups(zs, fused):
+    """Tensors below the threshold are replicated (whole tensor reduced and
+    updated on every rank); norms and odd sizes use a second hyperparameter
+    group without weight decay."""
+    numels = _small_model()
+    groups = _norm_groups(numels, 256)
+    hps = [_hp(zs), zs.AdamWHParams(lr=3e-4, beta1=0.8, beta2=0.99, eps=1e-6, weight_decay=0.0)]
+    run = MultiRun(zs, numels, 8, 5, 3, 91, _hp(zs), persist_below=2048, groups=groups, hps=hps)
+    assert any(run.plan.tensor_replicated(i) for i in range(len(numels)))
+    assert any(not run.plan.tensor_replicated(i) for i in range(len(numels)))
+    for t in (1, 2, 3):
+        run.step(t, fused)
+        run.check()
+
+
+def test_multi_tensor_groups_all_replicated(zs):
+    """Every tensor below the threshold: the step is plain data parallelism on each rank."""
+    numels = [100, 7, 2000, 3, 9]
+    hps = [_hp(zs), zs.AdamWHParams(lr=1e-3, weight_decay=0.0)]
+    run = MultiRun(zs, numels, 4, 0, 2, 92, _hp(zs), persist_below=1 << 20, groups=[0, 1, 0, 1, 1], hps=hps)
+    assert run.plan.shard_numel == sum((n + 7) // 8 * 8 for n in numels)
+    for t in (1, 2):
+        run.step(t, True)
+        run.check()
 
 
 def test_generator_gpu_equals_host(zs):
