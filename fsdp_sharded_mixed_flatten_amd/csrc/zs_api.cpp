@@ -60,10 +60,10 @@ zs_status check_hp(const zs_adamw_hparams* hp) {
 
 zs_status check_contribs(const zs_plan* plan, const void* const* contribs, int32_t n) {
     if (!contribs) return fail(ZS_EINVAL, "contribs is NULL");
-    if (n != plan->world)
-        return fail(ZS_EINVAL, "n_contribs = %d but the plan's world size is %d", n, plan->world);
     if (n < 1 || n > ZS_MAX_CONTRIBS)
         return fail(ZS_EINVAL, "n_contribs = %d outside [1, %d]", n, ZS_MAX_CONTRIBS);
+    if (n % plan->world != 0)
+        return fail(ZS_EINVAL, "n_contribs = %d is not a multiple of the plan's world size %d", n, plan->world);
     for (int32_t q = 0; q < n; ++q) {
         if (!contribs[q]) return fail(ZS_EINVAL, "contribs[%d] is NULL (no contribution from rank %d)", q, q);
         if (!aligned16(contribs[q])) return fail(ZS_EALIGN, "contribs[%d] is not 16-byte aligned", q);
@@ -464,8 +464,9 @@ zs_status zs_multi_bind(const zs_plan* plan, const zs_piece_ptrs* pieces, const 
     if (zs_status st = check_multi_plan(plan)) return st;
     if (!pieces && !plan->tensors.empty()) return fail(ZS_EINVAL, "pieces is NULL");
     if (zs_status st = check_ptr(workspace, "workspace")) return st;
-    if (n_contribs != 0 && n_contribs != plan->world)
-        return fail(ZS_EINVAL, "n_contribs = %d must be 0 or the world size %d", n_contribs, plan->world);
+    if (n_contribs < 0 || n_contribs > ZS_MAX_CONTRIBS || n_contribs % plan->world != 0)
+        return fail(ZS_EINVAL, "n_contribs = %d must be 0 or a multiple of the world size %d, at most %d",
+                    n_contribs, plan->world, ZS_MAX_CONTRIBS);
     if (n_contribs > 0 && !contribs) return fail(ZS_EINVAL, "contribs is NULL");
     const MultiLayout L = multi_layout(plan, n_contribs);
     if (workspace_bytes < L.total)

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-/* Largest number of gradient contributions (world size) one call accepts. */
+/* Largest number of gradient contributions one call accepts. */
 #define ZS_MAX_CONTRIBS 256
 /* Hyperparameter groups a PER_TENSOR plan can hold. */
 #define ZS_MAX_GROUPS 8
@@ -173,9 +173,14 @@ zs_status zs_plan_tensor(const zs_plan* plan, int32_t i, zs_tensor_info* out);
  * In these calls the rank's shard is one packed buffer of S elements.
  * contribs is a HOST array of n_contribs device pointers; contribs[q] is rank
  * q's bf16 gradient for this rank's shard, S elements, element j belonging
- * to global index r*S + j (FLAT). n_contribs must equal the plan's world
- * size, 1 <= N <= ZS_MAX_CONTRIBS. full_bf16 is the gathered parameter
- * buffer of T elements; only [r*S, (r+1)*S) is written. */
+ * to global index r*S + j (FLAT). n_contribs is the plan's world size N, or
+ * N*R for hybrid sharding (shards cut N ways inside a group, R groups
+ * replicating them: HYBRID_SHARD in "ZeRO vs FSDP...", section 3.1, and
+ * "FSDP2's parameter lifecycle...", section "Hybrid sharding"): the
+ * gradient is then averaged over all N*R data-parallel ranks, in the order
+ * the array gives, exactly as one flat group of N*R ranks would average it.
+ * n_contribs <= ZS_MAX_CONTRIBS. full_bf16 is the gathered parameter buffer
+ * of T elements; only [r*S, (r+1)*S) is written. */
 
 /* Averaged reduce of the bucket [off, off+len) of the shard (reduce-scatter
  * bucketed as gradients become ready: "从 Data Parallel 到 ZeRO/FSDP", section
@@ -235,7 +240,8 @@ int64_t zs_multi_workspace_bytes(const zs_plan* plan, int32_t n_contribs);
 /* pieces: host array of zs_plan_num_tensors(plan) records. contribs: host
  * array of n_contribs * num_tensors device pointers, contribs[q*n_tensors+i]
  * = rank q's bf16 gradient piece of tensor i (S_i elements), or NULL when
- * n_contribs == 0 (no reduce possible on this binding). */
+ * n_contribs == 0 (no reduce possible on this binding). As in the flat
+ * calls, n_contribs is the world size or a multiple of it (hybrid). */
 zs_status zs_multi_bind(const zs_plan* plan, const zs_piece_ptrs* pieces, const void* const* contribs,
                         int32_t n_contribs, void* workspace, int64_t workspace_bytes, void* stream);
 

@@ -179,6 +179,11 @@ def test_validation_without_device(zs):
 
     # wrong number of contributions, NULL contribution, misaligned contribution
     assert st(L.zs_reduce_shard, h, good, 3, FAKE, 0, 8, None) == zs.ZS_EINVAL
+    good12 = (vp * 12)(*[FAKE + 4096 * k for k in range(12)])
+    assert st(L.zs_reduce_shard, h, good12, 6, FAKE, 0, 8, None) == zs.ZS_EINVAL  # not a multiple of N
+    assert "multiple" in zs.zs_last_error()
+    assert st(L.zs_reduce_shard, h, good12, 12, FAKE, 8, 0, None) == zs.ZS_OK  # hybrid: 3 groups of 4
+    assert st(L.zs_reduce_shard, h, good12, 0, FAKE, 8, 0, None) == zs.ZS_EINVAL
     bad = (vp * 4)(FAKE, None, FAKE, FAKE)
     assert st(L.zs_reduce_shard, h, bad, 4, FAKE, 0, 8, None) == zs.ZS_EINVAL
     assert "contribs[1]" in zs.zs_last_error()

@@ -31,7 +31,7 @@ def zs():
     return m
 
 
-def _flat_inputs(numels, world, align, steps, seed, zero_prob=0.0, tail_prob=0.0):
+def _flat_inputs(numels, world, align, steps, seed, zero_prob=0.0, tail_prob=0.0, replicas=1):
     plan = oracle.plan_flat(numels, world, 0, align)
     T = plan.T
     pad = np.frombuffer(bytes(plan.padding_mask_full()), dtype=np.uint8).astype(bool)
@@ -40,7 +40,7 @@ def _flat_inputs(numels, world, align, steps, seed, zero_prob=0.0, tail_prob=0.0
     contribs = {}
     for t in range(1, steps + 1):
         cs = []
-        for q in range(world):
+        for q in range(world * replicas):
             c = synth.cpu_bf16(T, 0, synth.spec(seed, synth.STREAM_CONTRIB + q, t, 1e-3, 2**62, 0.1,
                                                 tail_prob, zero_prob))
             c[pad] = 0
@@ -53,13 +53,13 @@ class FlatRun:
     """Oracle and GPU state of one rank over several steps of a FLAT plan."""
 
     def __init__(self, zs, numels, world, rank, align, steps, seed, hp, bucket=0, fused=False,
-                 zero_prob=0.0, tail_prob=0.0):
+                 zero_prob=0.0, tail_prob=0.0, replicas=1):
         import torch
         self.zs = zs
         self.plan = zs.zs_shard_plan(numels, world, rank, align, zs.ZS_LAYOUT_FLAT)
         T, S = self.plan.padded_numel, self.plan.shard_numel
         self.T, self.S, self.rank, self.world = T, S, rank, world
-        T2, master, contribs = _flat_inputs(numels, world, align, steps, seed, zero_prob, tail_prob)
+        T2, master, contribs = _flat_inputs(numels, world, align, steps, seed, zero_prob, tail_prob, replicas)
         assert T2 == T
         lo = rank * S
         self.mine = {t: [c[lo:lo + S].copy() for c in cs] for t, cs in contribs.items()}
@@ -295,9 +295,11 @@ class MultiRun:
     of hyperparameters per group) the *_groups calls run and piece i uses
     hps[groups[i]]; ``persist_below`` replicates the small tensors."""
 
-    def __init__(self, zs, numels, world, rank, steps, seed, hp, persist_below=0, groups=None, hps=None):
+    def __init__(self, zs, numels, world, rank, steps, seed, hp, persist_below=0, groups=None, hps=None,
+                 replicas=1):
         import torch
         self.zs, self.hp, self.world, self.rank = zs, hp, world, rank
+        self.n_contribs = world * replicas
         self.groups, self.hps = groups, hps
         if persist_below or groups is not None:
             self.plan = zs.zs_shard_plan_ex(numels, world, rank, persist_below_elems=persist_below, groups=groups)
@@ -320,11 +322,11 @@ class MultiRun:
                                     param=torch.zeros(Si, dtype=torch.int16, device="cuda"),
                                     full=dev16(np.full(self.oplan.padded[i], SENT, np.uint16))))
             for t in range(1, steps + 1):
-                for q in range(world):
+                for q in range(self.n_contribs):
                     c = synth.cpu_bf16(Si, base, synth.spec(seed, synth.STREAM_CONTRIB + q, t, 1e-3, valid))
-                    self.contribs.setdefault(t, [[None] * len(numels) for _ in range(world)])[q][i] = c
+                    self.contribs.setdefault(t, [[None] * len(numels) for _ in range(self.n_contribs)])[q][i] = c
         self.dcontribs = {t: [[dev16(c) for c in row] for row in cs] for t, cs in self.contribs.items()}
-        nbytes = zs.zs_multi_workspace_bytes(self.plan, world)
+        nbytes = zs.zs_multi_workspace_bytes(self.plan, self.n_contribs)
         self.ws = {t: torch.zeros(nbytes, dtype=torch.uint8, device="cuda") for t in self.contribs}
         for t in self.contribs:
             zs.zs_multi_bind(self.plan, self.pieces, self.dcontribs[t], self.ws[t])
@@ -353,7 +355,7 @@ class MultiRun:
             o = self.o[i]
             if o["g"].size == 0:
                 continue
-            cs = [self.contribs[t][q][i] for q in range(self.world)]
+            cs = [self.contribs[t][q][i] for q in range(self.n_contribs)]
             oracle.reduce(cs, out=o["g"])
             oracle.adamw(h, o["g"], o["master"], o["m"], o["v"], o["p"])
             o["full"][pc.own_lo:pc.own_hi] = o["p"]
@@ -384,6 +386,25 @@ def test_multi_tensor_runtime_world(zs):
     run = MultiRun(zs, _small_model(H=128, I=344, V=300, L=1), 5, 4, 1, 78, _hp(zs))
     run.step(1, True)
     run.check()
+
+
+@pytest.mark.parametrize("world,replicas,fused", [(4, 2, False), (4, 2, True), (8, 8, True), (2, 3, True)])
+def test_hybrid_sharding(zs, world, replicas, fused):
+    """Shards cut `world` ways, `replicas` groups: world*replicas contributions
+    averaged (8*8 = 64 takes the two-pass large-N fused path)."""
+    run = FlatRun(zs, [300_007, 4099], world, world - 1, 1, 2, 57, _hp(zs), bucket=40_000, fused=fused,
+                  replicas=replicas)
+    for t in (1, 2):
+        run.step(t)
+        run.check()
+
+
+def test_multi_tensor_hybrid(zs):
+    """Per-tensor pieces of a 4-way shard with 3 replica groups (12 contributions)."""
+    run = MultiRun(zs, _small_model(H=128, I=344, V=300, L=1), 4, 2, 2, 79, _hp(zs), replicas=3)
+    for t in (1, 2):
+        run.step(t, True)
+        run.check()
 
 
 def _norm_groups(numels, H):

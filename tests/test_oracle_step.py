@@ -58,6 +58,49 @@ def test_sharding_invariance_tiny(ora):
         assert not ddp[key][pad].view(np.uint8).any()
 
 
+def test_hybrid_sharding_invariance(ora):
+    """Hybrid sharding: shards cut 4 ways inside a group, 2 groups replicating
+    them, 8 data-parallel contributions. The 4 shard ranks' steps, gathered,
+    equal the DDP update over all 8 contributions and the full-shard update
+    over 8 ranks ("ZeRO vs FSDP..." section 3.1, HYBRID_SHARD; the averaged
+    gradient is the same whatever the sharding)."""
+    numels, Ns, R, steps = [70_001, 333], 4, 2, 3
+    N = Ns * R
+    ph = plan_flat(numels, Ns, 0, 1)
+    pf = plan_flat(numels, N, 0, 1)
+    T = max(ph.T, pf.T)
+    real = sum(numels)
+    master0 = synth.cpu_f32(T, 0, synth.spec(41, synth.STREAM_MASTER, 0, 0.02, real))
+    hp = HParams(lr=3e-4, weight_decay=0.05)
+
+    def fresh(n, lo=0):
+        return dict(g=np.zeros(n, np.uint16), master=master0[lo:lo + n].copy(), m=np.zeros(n, np.float32),
+                    v=np.zeros(n, np.float32), p=np.zeros(n, np.uint16))
+
+    ddp = fresh(T)
+    hyb = [fresh(ph.S, r * ph.S) for r in range(Ns)]
+    fs = [fresh(pf.S, r * pf.S) for r in range(N)]
+    full_h = np.full(ph.T, 0xDEAD, np.uint16)
+    full_f = np.full(pf.T, 0xDEAD, np.uint16)
+    for t in range(1, steps + 1):
+        cs = [synth.cpu_bf16(T, 0, synth.spec(41, synth.STREAM_CONTRIB + q, t, 1e-3, real)) for q in range(N)]
+        h = hp.at(t)
+        ora.reduce(cs, out=ddp["g"])
+        ora.adamw(h, ddp["g"], ddp["master"], ddp["m"], ddp["v"], ddp["p"])
+        for r, st in enumerate(hyb):
+            mine = [c[r * ph.S:(r + 1) * ph.S].copy() for c in cs]
+            ora.shard_step(h, mine, st["g"], st["master"], st["m"], st["v"], st["p"], full_h, r)
+        for r, st in enumerate(fs):
+            mine = [c[r * pf.S:(r + 1) * pf.S].copy() for c in cs]
+            ora.shard_step(h, mine, st["g"], st["master"], st["m"], st["v"], st["p"], full_f, r)
+        for key in ("g", "master", "m", "v", "p"):
+            a = np.concatenate([st[key] for st in hyb])
+            b = np.concatenate([st[key] for st in fs])
+            assert a.tobytes() == ddp[key][:ph.T].tobytes(), (t, key)
+            assert b.tobytes() == ddp[key][:pf.T].tobytes(), (t, key)
+        assert np.array_equal(full_h, ddp["p"][:ph.T]) and np.array_equal(full_f, ddp["p"][:pf.T])
+
+
 def test_gather_touches_only_own_slice(ora):
     S, N = 1000, 4
     p = np.arange(S, dtype=np.uint16)
