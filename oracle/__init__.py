@@ -55,6 +55,9 @@ def lib():
         L.ora_clip_scale.argtypes = [ctypes.POINTER(ctypes.c_double), _i32, ctypes.c_double]
         L.ora_adamw_f32grad.argtypes = [_f32p, _f32p, ctypes.c_float, ctypes.c_float, _i32, _f32p, _f32p,
                                         _f32p, _u16p, _i64, _i64]
+        _u8p = ctypes.POINTER(ctypes.c_uint8)
+        L.ora_quantize.argtypes = [_u16p, _i64, _i32, _i32, _u8p, _f32p]
+        L.ora_dequantize.argtypes = [_u8p, _f32p, _i64, _i32, _i32, _u16p]
         _lib = L
     return _lib
 
@@ -211,3 +214,50 @@ def adamw_f32grad(hp, acc, divisor, scale, skip, master, m, v, p, lo=0, hi=None)
     hi = acc.size if hi is None else hi
     lib().ora_adamw_f32grad(_p32(hp.coef()), _p32(acc), divisor, scale, 1 if skip else 0, _p32(master),
                             _p32(m), _p32(v), _p16(p), lo, hi)
+
+
+# ---------------------------------------------------------------- quantized parameter gather
+
+
+def quant_bytes(n, bits):
+    """Code bytes of n elements at ``bits`` (8 or 4) per element."""
+    return n if bits == 8 else (n + 1) // 2
+
+
+def quant_blocks(n, block):
+    return -(-n // block)
+
+
+def _p8(a):
+    assert a.dtype == np.uint8 and a.flags.c_contiguous
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+
+
+def quantize(p, bits, block):
+    """Block-wise symmetric quantization of a bf16 (uint16) array: (codes uint8, scales float32)."""
+    if bits not in (4, 8) or block < 1:
+        raise ValueError("bits must be 4 or 8 and block >= 1")
+    p = np.ascontiguousarray(p, dtype=np.uint16)
+    q = np.zeros(quant_bytes(p.size, bits), np.uint8)
+    sc = np.zeros(quant_blocks(p.size, block), np.float32)
+    lib().ora_quantize(_p16(p), p.size, bits, block, _p8(q), _p32(sc))
+    return q, sc
+
+
+def dequantize(q, scales, n, bits, block):
+    """bf16 (uint16) array of n elements from codes and block scales."""
+    out = np.zeros(n, np.uint16)
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    assert q.size >= quant_bytes(n, bits) and scales.size >= quant_blocks(n, block)
+    lib().ora_dequantize(_p8(q), _p32(scales), n, bits, block, _p16(out))
+    return out
+
+
+def dequant_gather(q_all, scales_all, S, world, bits, block):
+    """Gathered bf16 buffer of world*S elements from every rank's payload, laid
+    end to end in rank order (codes: world * quant_bytes(S) bytes; scales:
+    world * quant_blocks(S) floats)."""
+    qb, nb = quant_bytes(S, bits), quant_blocks(S, block)
+    return np.concatenate([dequantize(q_all[r * qb:(r + 1) * qb], scales_all[r * nb:(r + 1) * nb], S, bits, block)
+                           for r in range(world)]) if world else np.zeros(0, np.uint16)

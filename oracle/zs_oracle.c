@@ -291,3 +291,78 @@ void ora_adamw_f32grad(const float* c, const float* acc, float divisor, float sc
         p[j] = ora_f32_to_bf16(w);
     }
 }
+
+/* ---------------------------------------------------------------- quantized parameter gather
+ * ZeRO++ quantizes the parameters that the all-gather moves, down to 4 bits,
+ * for up to four times less traffic ("ZeRO vs FSDP...", section 5.2). The
+ * pages give no scheme; this is the plain symmetric block-wise reading:
+ *
+ *   the rank's updated bf16 shard is cut into blocks of B elements (the last
+ *   one may be shorter); per block, amax = max |x| over its elements and
+ *   scale = amax / qmax in fp32, qmax = 2^(bits-1) - 1 (127 for 8 bits, 7
+ *   for 4 bits); each element becomes the integer k = x / scale rounded to
+ *   nearest, ties to even, clamped to [-qmax, qmax]. A block whose amax is 0
+ *   has scale 0 and every k = 0. A block holding a NaN or an infinity has
+ *   scale NaN and every k = 0, so every element of it dequantizes to NaN.
+ *   Dequantization: x' = bf16(f32(k) * scale), round-to-nearest-even.
+ *
+ * Storage: 8 bits -- one two's-complement byte per element; 4 bits -- two
+ * elements per byte, element 2i in the low nibble and 2i+1 in the high
+ * nibble, each a 4-bit two's-complement value. One fp32 scale per block. */
+
+static int32_t ora_qmax(int32_t bits) { return (1 << (bits - 1)) - 1; }
+
+static void ora_put_code(uint8_t* q, int32_t bits, int64_t j, int32_t k) {
+    if (bits == 8) {
+        q[j] = (uint8_t)(k & 0xFF);
+    } else {
+        uint8_t nib = (uint8_t)(k & 0xF);
+        if (j & 1)
+            q[j >> 1] = (uint8_t)((q[j >> 1] & 0x0F) | (nib << 4));
+        else
+            q[j >> 1] = (uint8_t)((q[j >> 1] & 0xF0) | nib);
+    }
+}
+
+static int32_t ora_get_code(const uint8_t* q, int32_t bits, int64_t j) {
+    if (bits == 8) return (int32_t)(int8_t)q[j];
+    int32_t nib = (j & 1) ? (q[j >> 1] >> 4) : (q[j >> 1] & 0xF);
+    return nib >= 8 ? nib - 16 : nib;
+}
+
+/* Quantizes p[0, n) in blocks of B: codes into q (n bytes for 8 bits,
+ * ceil(n/2) for 4 bits), one scale per block into scales. */
+void ora_quantize(const uint16_t* p, int64_t n, int32_t bits, int32_t B, uint8_t* q, float* scales) {
+    const int32_t qmax = ora_qmax(bits);
+    for (int64_t lo = 0, b = 0; lo < n; lo += B, ++b) {
+        const int64_t hi = lo + B < n ? lo + B : n;
+        float amax = 0.0f;
+        int finite = 1;
+        for (int64_t j = lo; j < hi; ++j) {
+            float x = ora_bf16_to_f32(p[j]);
+            if (!isfinite(x)) finite = 0;
+            float a = fabsf(x);
+            if (a > amax) amax = a;
+        }
+        const float scale = finite ? amax / (float)qmax : NAN;
+        for (int64_t j = lo; j < hi; ++j) {
+            int32_t k = 0;
+            if (finite && amax > 0.0f) {
+                float r = nearbyintf(ora_bf16_to_f32(p[j]) / scale);
+                if (r > (float)qmax) r = (float)qmax;
+                if (r < -(float)qmax) r = -(float)qmax;
+                k = (int32_t)r;
+            }
+            ora_put_code(q, bits, j, k);
+        }
+        scales[b] = scale;
+    }
+}
+
+/* out[j] = bf16(f32(code j) * scale of its block), j in [0, n). */
+void ora_dequantize(const uint8_t* q, const float* scales, int64_t n, int32_t bits, int32_t B, uint16_t* out) {
+    for (int64_t j = 0; j < n; ++j) {
+        float x = (float)ora_get_code(q, bits, j) * scales[j / B];
+        out[j] = ora_f32_to_bf16(x);
+    }
+}
