@@ -98,6 +98,12 @@ def _load():
         "zs_fused_shard_step_multi": (st, [vp, ctypes.POINTER(AdamWHParams), vp, vp]),
         "zs_adamw_shard_step_multi_groups": (st, [vp, ctypes.POINTER(AdamWHParams), i32, vp, vp]),
         "zs_fused_shard_step_multi_groups": (st, [vp, ctypes.POINTER(AdamWHParams), i32, vp, vp]),
+        "zs_quant_code_bytes": (i64, [vp, i32]),
+        "zs_quant_num_scales": (i64, [vp, i32]),
+        "zs_quantize_shard": (st, [vp, i32, i32, vp, vp, vp, vp]),
+        "zs_fused_shard_step_quant": (st, [vp, ctypes.POINTER(AdamWHParams), ctypes.POINTER(vp), i32, vp, vp, vp,
+                                           vp, vp, i32, i32, vp, vp, vp]),
+        "zs_dequant_gather": (st, [vp, i32, i32, vp, vp, vp, vp]),
         "zs_accumulate_shard": (st, [vp, ctypes.POINTER(vp), i32, vp, i64, i64, i32, vp]),
         "zs_grad_stats_workspace_bytes": (i64, [vp]),
         "zs_grad_stats": (st, [vp, vp, ctypes.c_float, vp, vp, vp, i64, vp]),
@@ -122,7 +128,8 @@ EXPORTED = ("zs_shard_plan", "zs_shard_plan_ex", "zs_plan_tensor_group", "zs_pla
             "zs_gather_params", "zs_fused_shard_step", "zs_multi_workspace_bytes", "zs_multi_bind",
             "zs_reduce_shard_multi", "zs_adamw_shard_step_multi", "zs_gather_params_multi",
             "zs_fused_shard_step_multi", "zs_adamw_shard_step_multi_groups",
-            "zs_fused_shard_step_multi_groups", "zs_accumulate_shard", "zs_grad_stats_workspace_bytes",
+            "zs_fused_shard_step_multi_groups", "zs_quant_code_bytes", "zs_quant_num_scales", "zs_quantize_shard",
+            "zs_fused_shard_step_quant", "zs_dequant_gather", "zs_accumulate_shard", "zs_grad_stats_workspace_bytes",
             "zs_grad_stats", "zs_clip_scale", "zs_adamw_shard_step_accum", "zs_last_error", "zs_version")
 
 
@@ -161,7 +168,10 @@ def _ptr(t, kind, need, what):
         raise ValueError(f"{what} must be a CUDA tensor")
     if not t.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
-    if kind == "bf16":
+    if kind == "bytes":
+        if t.dtype not in (torch.uint8, torch.int8):
+            raise ValueError(f"{what} must be a uint8 or int8 byte buffer, got {t.dtype}")
+    elif kind == "bf16":
         if str(t.dtype).split(".")[-1] not in _BF16_NAMES:
             raise ValueError(f"{what} must hold bf16 (bfloat16 or 16-bit integer storage), got {t.dtype}")
     elif t.dtype != torch.float32:
@@ -308,6 +318,49 @@ def zs_fused_shard_step(plan, hp, contribs, master, m, v, grad=None, param=None,
                                     _ptr(v, "f32", S, "v"), _ptr(grad, "bf16", S, "grad"),
                                     _ptr(param, "bf16", S, "param"),
                                     _ptr(full, "bf16", (r + 1) * S, "full"), _stream(stream)))
+
+
+# ---------------------------------------------------------------- quantized parameter gather
+
+
+def zs_quant_code_bytes(plan, bits):
+    n = _lib.zs_quant_code_bytes(plan.handle, bits)
+    if n < 0:
+        raise ValueError(f"bits = {bits} must be 4 or 8")
+    return n
+
+
+def zs_quant_num_scales(plan, block):
+    n = _lib.zs_quant_num_scales(plan.handle, block)
+    if n < 0:
+        raise ValueError(f"block = {block} must be a power of two in [8, 256]")
+    return n
+
+
+def zs_quantize_shard(plan, bits, block, param, codes, scales, stream=None):
+    S = plan.shard_numel
+    _check(_lib.zs_quantize_shard(plan.handle, bits, block, _ptr(param, "bf16", S, "param"),
+                                  _ptr(codes, "bytes", S * bits // 8, "codes"),
+                                  _ptr(scales, "f32", -(-S // max(block, 1)), "scales"), _stream(stream)))
+
+
+def zs_fused_shard_step_quant(plan, hp, contribs, master, m, v, bits, block, codes, scales, grad=None, param=None,
+                              stream=None):
+    S = plan.shard_numel
+    ptrs = [_ptr(c, "bf16", S, f"contribs[{q}]") for q, c in enumerate(contribs)]
+    _check(_lib.zs_fused_shard_step_quant(plan.handle, ctypes.byref(hp), _ptr_array(ptrs), len(ptrs),
+                                          _ptr(master, "f32", S, "master"), _ptr(m, "f32", S, "m"),
+                                          _ptr(v, "f32", S, "v"), _ptr(grad, "bf16", S, "grad"),
+                                          _ptr(param, "bf16", S, "param"), bits, block,
+                                          _ptr(codes, "bytes", S * bits // 8, "codes"),
+                                          _ptr(scales, "f32", -(-S // max(block, 1)), "scales"), _stream(stream)))
+
+
+def zs_dequant_gather(plan, bits, block, codes_all, scales_all, full, stream=None):
+    S, N = plan.shard_numel, plan.world_size
+    _check(_lib.zs_dequant_gather(plan.handle, bits, block, _ptr(codes_all, "bytes", N * S * bits // 8, "codes_all"),
+                                  _ptr(scales_all, "f32", N * -(-S // max(block, 1)), "scales_all"),
+                                  _ptr(full, "bf16", N * S, "full"), _stream(stream)))
 
 
 # ---------------------------------------------------------------- multi-tensor

@@ -336,6 +336,82 @@ zs_status zs_fused_shard_step(const zs_plan* plan, const zs_adamw_hparams* hp, c
                       "fused launch");
 }
 
+// ------------------------------------------------------------------ quantized parameter gather
+
+namespace {
+
+bool quant_spec_ok(int32_t bits, int32_t block) {
+    return (bits == 4 || bits == 8) && block >= zs::kQuantMinBlock && block <= zs::kQuantMaxBlock &&
+           (block & (block - 1)) == 0;
+}
+
+zs_status check_quant(const zs_plan* plan, int32_t bits, int32_t block) {
+    if (zs_status st = check_plan(plan)) return st;
+    if (plan->layout != ZS_LAYOUT_FLAT) return fail(ZS_EINVAL, "the quantized gather needs a FLAT plan");
+    if (!quant_spec_ok(bits, block))
+        return fail(ZS_EINVAL, "bits = %d must be 4 or 8 and block = %d a power of two in [%d, %d]", bits, block,
+                    zs::kQuantMinBlock, zs::kQuantMaxBlock);
+    return ZS_OK;
+}
+
+}  // namespace
+
+int64_t zs_quant_code_bytes(const zs_plan* plan, int32_t bits) {
+    if (!plan || (bits != 4 && bits != 8)) return -1;
+    return plan->S * bits / 8;
+}
+
+int64_t zs_quant_num_scales(const zs_plan* plan, int32_t block) {
+    if (!plan || !quant_spec_ok(8, block)) return -1;
+    return (plan->S + block - 1) / block;
+}
+
+zs_status zs_quantize_shard(const zs_plan* plan, int32_t bits, int32_t block, const void* param_bf16, void* codes,
+                            float* scales, void* stream) {
+    if (zs_status st = check_quant(plan, bits, block)) return st;
+    if (zs_status st = check_ptr(param_bf16, "param_bf16")) return st;
+    if (zs_status st = check_ptr(codes, "codes")) return st;
+    if (zs_status st = check_ptr(scales, "scales")) return st;
+    if (plan->S == 0) return ZS_OK;
+    const zs::QuantOut q{codes, scales, bits, block};
+    return hip_status(zs::launch_quantize(q, param_bf16, plan->S, stream), "quantize launch");
+}
+
+zs_status zs_fused_shard_step_quant(const zs_plan* plan, const zs_adamw_hparams* hp, const void* const* contribs,
+                                    int32_t n_contribs, float* master, float* m, float* v, void* grad_bf16,
+                                    void* param_bf16, int32_t bits, int32_t block, void* codes, float* scales,
+                                    void* stream) {
+    if (zs_status st = check_quant(plan, bits, block)) return st;
+    if (zs_status st = check_hp(hp)) return st;
+    if (zs_status st = check_contribs(plan, contribs, n_contribs)) return st;
+    if (zs_status st = check_ptr(master, "master")) return st;
+    if (zs_status st = check_ptr(m, "m")) return st;
+    if (zs_status st = check_ptr(v, "v")) return st;
+    if (zs_status st = check_opt_ptr(grad_bf16, "grad_bf16")) return st;
+    if (zs_status st = check_opt_ptr(param_bf16, "param_bf16")) return st;
+    if (zs_status st = check_ptr(codes, "codes")) return st;
+    if (zs_status st = check_ptr(scales, "scales")) return st;
+    if (plan->S == 0) return ZS_OK;
+    const zs::QuantOut q{codes, scales, bits, block};
+    return hip_status(zs::launch_fused(zs::make_coef(*hp), contribs, n_contribs, master, m, v, grad_bf16, param_bf16,
+                                       nullptr, plan->S, stream, &q),
+                      "fused quantized launch");
+}
+
+zs_status zs_dequant_gather(const zs_plan* plan, int32_t bits, int32_t block, const void* codes_all,
+                            const float* scales_all, void* full_bf16, void* stream) {
+    if (zs_status st = check_quant(plan, bits, block)) return st;
+    if (zs_status st = check_ptr(codes_all, "codes_all")) return st;
+    if (zs_status st = check_ptr(scales_all, "scales_all")) return st;
+    if (zs_status st = check_ptr(full_bf16, "full_bf16")) return st;
+    if (plan->S == 0) return ZS_OK;
+    if ((plan->S / 8 + zs::kBlockThreads - 1) / zs::kBlockThreads > INT32_MAX)
+        return fail(ZS_EINVAL, "shard of %lld elements is too long for one dequantizing launch", (long long)plan->S);
+    return hip_status(zs::launch_dequant(bits, block, codes_all, scales_all, zs_quant_code_bytes(plan, bits),
+                                         zs_quant_num_scales(plan, block), plan->world, full_bf16, plan->S, stream),
+                      "dequantize launch");
+}
+
 // ------------------------------------------------------------------ accumulation and clipping
 
 zs_status zs_accumulate_shard(const zs_plan* plan, const void* const* contribs, int32_t n_contribs, float* acc_f32,

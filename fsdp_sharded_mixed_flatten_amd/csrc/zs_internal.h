@@ -101,13 +101,31 @@ enum MultiFlags : int32_t {
 
 constexpr uint64_t kMultiMagic = 0x7A734D554C544931ull;
 
+// Quantized output of the updated shard (block-wise symmetric codes).
+struct QuantOut {
+    void* codes;    // this rank's codes: bits/8 bytes per element
+    float* scales;  // one fp32 scale per block
+    int32_t bits;   // 4 or 8
+    int32_t block;  // elements per block: a power of two in [kQuantMinBlock, kQuantMaxBlock]
+};
+constexpr int32_t kQuantMinBlock = 8;
+constexpr int32_t kQuantMaxBlock = 256;
+
 // Launchers (zs_kernels.hip). They return a hipError_t value cast to int.
 int launch_reduce(const void* const* contribs, int n, void* grad, int64_t len, void* stream);
+// launch_adamw / launch_fused: q (optional) also writes the updated shard's
+// codes and scales.
 int launch_adamw(const AdamCoef& c, const void* grad, float* master, float* m, float* v,
-                 void* param, void* full_at_own, int64_t len, void* stream);
+                 void* param, void* full_at_own, int64_t len, void* stream, const QuantOut* q = nullptr);
 int launch_gather(const void* param, void* full_at_own, int64_t len, void* stream);
 int launch_fused(const AdamCoef& c, const void* const* contribs, int n, float* master, float* m,
-                 float* v, void* grad, void* param, void* full_at_own, int64_t len, void* stream);
+                 float* v, void* grad, void* param, void* full_at_own, int64_t len, void* stream,
+                 const QuantOut* q = nullptr);
+int launch_quantize(const QuantOut& q, const void* param, int64_t len, void* stream);
+// Dequantizes n_ranks payloads (codes end to end, code_bytes each; scales end
+// to end, n_scales each) into full[r*S, (r+1)*S) for every rank r.
+int launch_dequant(int bits, int block, const void* codes_all, const float* scales_all, int64_t code_bytes,
+                   int64_t n_scales, int n_ranks, void* full, int64_t S, void* stream);
 
 // Elements one block of the stats kernel reduces (kBlockThreads lanes x 4
 // elements x 16 trips).

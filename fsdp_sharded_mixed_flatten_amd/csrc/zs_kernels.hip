@@ -322,12 +322,86 @@ __device__ __forceinline__ void reduce4_tile(const void* const* cp, int n_rt, fl
         if (ok[k]) st_out(out + u[k], avg_bf16x4<N>(a[k], nf));
 }
 
+// ------------------------------------------------------------------ block quantization
+//
+// Symmetric block-wise codes of the updated bf16 shard (ZeRO++'s quantized
+// parameter gather): per block of B elements, scale = amax / qmax in fp32 and
+// code = rne(x / scale) clamped to [-qmax, qmax]; amax == 0 gives scale 0 and
+// codes 0, a non-finite element gives scale NaN and codes 0. A lane holds E
+// consecutive elements, so a block spans B / E consecutive lanes of the wave
+// and its amax is a butterfly max over them. Every lane of the wave must call
+// this (the shuffles), with ok == false where it holds no elements.
+
+template <int QB, int E>
+__device__ __forceinline__ void quant_store(const uint32_t* w, bool ok, int64_t unit, const QuantOut& qo) {
+    constexpr float qmax = (float)((1 << (QB - 1)) - 1);
+    const int lanes = qo.block / E;
+    float x[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = (e & 1) ? hi_bf16(w[e >> 1]) : lo_bf16(w[e >> 1]);
+    float amax = 0.0f;
+    int bad = 0;
+    if (ok) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float a = fabsf(x[e]);
+            bad |= !__builtin_isfinite(x[e]);
+            amax = a > amax ? a : amax;
+        }
+    }
+    for (int off = lanes >> 1; off > 0; off >>= 1) {
+        const float o = __shfl_xor(amax, off, 64);
+        amax = o > amax ? o : amax;
+        bad |= __shfl_xor(bad, off, 64);
+    }
+    if (!ok) return;
+    const float scale = bad ? __builtin_nanf("") : amax / qmax;
+    const bool zero = bad || !(amax > 0.0f);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        int k = 0;
+        if (!zero) {
+            float r = rintf(x[e] / scale);
+            r = r > qmax ? qmax : r;
+            r = r < -qmax ? -qmax : r;
+            k = (int)r;
+        }
+        const uint32_t c = (uint32_t)k & ((1u << QB) - 1u);
+        if (QB * e < 32)
+            lo |= c << (QB * e);
+        else
+            hi |= c << (QB * e - 32);
+    }
+    const int64_t first = unit * E;  // first element of the lane
+    char* cb = static_cast<char*>(qo.codes) + first * QB / 8;
+    if constexpr (QB * E == 64)
+        st_out(reinterpret_cast<u32x2*>(cb), u32x2{lo, hi});
+    else if constexpr (QB * E == 32)
+        st_out(reinterpret_cast<uint32_t*>(cb), lo);
+    else
+        st_out(reinterpret_cast<uint16_t*>(cb), (uint16_t)lo);
+    if ((threadIdx.x & (lanes - 1)) == 0) st_out(qo.scales + first / qo.block, scale);
+}
+
+template <int QB, int U>
+__device__ __forceinline__ void quant_units(const u32x2* pv, const bool* ok, const int64_t* u, const QuantOut& qo) {
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const uint32_t w[2] = {pv[k].x, pv[k].y};
+        quant_store<QB, 4>(w, ok[k], u[k], qo);
+    }
+}
+
 // AdamW from a bf16 grad; writes the bf16 parameter to `param` and/or `full`
-template <int U>
+template <int U, int QB = 0>
 __device__ __forceinline__ void adamw_tile(const AdamCoef& c, const u32x2* __restrict__ g, f32x4* __restrict__ master,
                                            f32x4* __restrict__ m, f32x4* __restrict__ v, u32x2* __restrict__ param,
-                                           u32x2* __restrict__ full, int64_t base, int64_t limit) {
-    u32x2 gv[U];
+                                           u32x2* __restrict__ full, int64_t base, int64_t limit,
+                                           const QuantOut& qo = QuantOut{}) {
+    u32x2 gv[U], pv[U];
+    int64_t uu[U];
+    bool ok[U];
     f32x4 wv[U], mv[U], vv[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
@@ -348,9 +422,19 @@ __device__ __forceinline__ void adamw_tile(const AdamCoef& c, const u32x2* __res
             st_state(m + u, mv[k]);
             st_state(v + u, vv[k]);
             const u32x2 p = to_bf16x4(wv[k]);
+            pv[k] = p;
             if (param) st_out(param + u, p);
             if (full) st_out(full + u, p);
         }
+    }
+    if constexpr (QB != 0) {
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            uu[k] = base + (int64_t)k * kBlock;
+            ok[k] = uu[k] < limit;
+            if (!ok[k]) pv[k] = u32x2{0u, 0u};
+        }
+        quant_units<QB, U>(pv, ok, uu, qo);
     }
 }
 
@@ -371,19 +455,21 @@ __device__ __forceinline__ void copy_tile(const V* __restrict__ src, V* __restri
 }
 
 // reduce + AdamW + gather write in registers
-template <int N, int U>
+template <int N, int U, int QB = 0>
 __device__ __forceinline__ void fused_tile(const AdamCoef& c, const void* const* cp, int n_rt, float nf,
                                            f32x4* __restrict__ master, f32x4* __restrict__ m,
                                            f32x4* __restrict__ v, u32x2* __restrict__ grad,
                                            u32x2* __restrict__ param, u32x2* __restrict__ full,
-                                           int64_t base, int64_t limit) {
+                                           int64_t base, int64_t limit, const QuantOut& qo = QuantOut{}) {
     int64_t u[U];
     bool ok[U];
     f32x4 wv[U], mv[U], vv[U];
+    u32x2 pv[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
         u[k] = base + (int64_t)k * kBlock;
         ok[k] = u[k] < limit;
+        pv[k] = u32x2{0u, 0u};
         if (ok[k]) {
             wv[k] = ld_state(master + u[k]);
             mv[k] = ld_state(m + u[k]);
@@ -401,10 +487,12 @@ __device__ __forceinline__ void fused_tile(const AdamCoef& c, const void* const*
         st_state(m + u[k], mv[k]);
         st_state(v + u[k], vv[k]);
         const u32x2 p = to_bf16x4(wv[k]);
+        pv[k] = p;
         if (grad) st_out(grad + u[k], g);
         if (param) st_out(param + u[k], p);
         if (full) st_out(full + u[k], p);
     }
+    if constexpr (QB != 0) quant_units<QB, U>(pv, ok, u, qo);
 }
 
 // ------------------------------------------------------------------ flat kernels
@@ -420,12 +508,12 @@ __global__ __launch_bounds__(kBlock) void k_reduce(Ptrs<CAP> cp, int n_rt, float
     reduce8_tile<N, U>(cp.p, n_rt, nf, out, tile_base(U), n8);
 }
 
-template <int U>
+template <int U, int QB>
 __global__ __launch_bounds__(kBlock) void k_adamw(AdamCoef c, const u32x2* __restrict__ g,
                                                   f32x4* __restrict__ master, f32x4* __restrict__ m,
                                                   f32x4* __restrict__ v, u32x2* __restrict__ param,
-                                                  u32x2* __restrict__ full, int64_t n4) {
-    adamw_tile<U>(c, g, master, m, v, param, full, tile_base(U), n4);
+                                                  u32x2* __restrict__ full, int64_t n4, QuantOut qo) {
+    adamw_tile<U, QB>(c, g, master, m, v, param, full, tile_base(U), n4, qo);
 }
 
 __global__ __launch_bounds__(kBlock) void k_gather(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
@@ -433,13 +521,71 @@ __global__ __launch_bounds__(kBlock) void k_gather(const u32x4* __restrict__ src
     copy_tile<u32x4, 1>(src, dst, tile_base(1), n8);
 }
 
-template <int N, int CAP, int U>
+template <int N, int CAP, int U, int QB>
 __global__ __launch_bounds__(kBlock) void k_fused(AdamCoef c, Ptrs<CAP> cp, int n_rt, float nf,
                                                   f32x4* __restrict__ master, f32x4* __restrict__ m,
                                                   f32x4* __restrict__ v, u32x2* __restrict__ grad,
                                                   u32x2* __restrict__ param, u32x2* __restrict__ full,
-                                                  int64_t n4) {
-    fused_tile<N, U>(c, cp.p, n_rt, nf, master, m, v, grad, param, full, tile_base(U), n4);
+                                                  int64_t n4, QuantOut qo) {
+    fused_tile<N, U, QB>(c, cp.p, n_rt, nf, master, m, v, grad, param, full, tile_base(U), n4, qo);
+}
+
+// Codes of a bf16 shard, 8 elements per lane.
+template <int QB>
+__global__ __launch_bounds__(kBlock) void k_quant(const u32x4* __restrict__ p, QuantOut qo, int64_t n8) {
+    const int64_t u = tile_base(1);
+    const bool ok = u < n8;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (ok) {
+        const u32x4 x = ld_in(p + u);
+        w[0] = x.x;
+        w[1] = x.y;
+        w[2] = x.z;
+        w[3] = x.w;
+    }
+    quant_store<QB, 8>(w, ok, u, qo);
+}
+
+// The receiving side of the quantized gather: blockIdx.y is the rank whose
+// payload a block decodes, 8 elements per lane, one 16-byte store each.
+template <int QB>
+__global__ __launch_bounds__(kBlock) void k_dequant(const char* __restrict__ codes_all,
+                                                    const float* __restrict__ scales_all, int64_t code_bytes,
+                                                    int64_t n_scales, int block_shift, u32x4* __restrict__ full,
+                                                    int64_t s8) {
+    const int64_t r = blockIdx.y;
+    const int64_t u = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (u >= s8) return;
+    const char* cb = codes_all + r * code_bytes + u * QB;  // 8 codes of QB bits = QB bytes
+    const float scale = ld_in(scales_all + r * n_scales + ((u * 8) >> block_shift));
+    uint32_t lo, hi;
+    if constexpr (QB == 8) {
+        const u32x2 c = ld_in(reinterpret_cast<const u32x2*>(cb));
+        lo = c.x;
+        hi = c.y;
+    } else {
+        lo = ld_in(reinterpret_cast<const uint32_t*>(cb));
+        hi = 0u;
+    }
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        int k;
+        if constexpr (QB == 8) {
+            const uint32_t w = e < 4 ? lo : hi;
+            k = (int)(int8_t)((w >> (8 * (e & 3))) & 0xFFu);
+        } else {
+            const int nib = (int)((lo >> (4 * e)) & 0xFu);
+            k = nib >= 8 ? nib - 16 : nib;
+        }
+        x[e] = (float)k * scale;
+    }
+    u32x4 o;
+    o.x = pack2(x[0], x[1]);
+    o.y = pack2(x[2], x[3]);
+    o.z = pack2(x[4], x[5]);
+    o.w = pack2(x[6], x[7]);
+    st_out(full + r * s8 + u, o);
 }
 
 // ------------------------------------------------------------------ multi-tensor kernel
@@ -684,17 +830,25 @@ int launch_reduce_t(const void* const* contribs, int n, void* grad, int64_t len,
     return (int)hipGetLastError();
 }
 
-template <int N, int CAP>
-int launch_fused_t(const AdamCoef& c, const void* const* contribs, int n, float* master, float* m,
-                   float* v, void* grad, void* param, void* full, int64_t len, hipStream_t s) {
+template <int N, int CAP, int QB>
+int launch_fused_q(const AdamCoef& c, const void* const* contribs, int n, float* master, float* m,
+                   float* v, void* grad, void* param, void* full, int64_t len, const QuantOut& qo, hipStream_t s) {
     Ptrs<CAP> cp{};
     for (int q = 0; q < n; ++q) cp.p[q] = contribs[q];
     const int64_t n4 = len / 4;
-    hipLaunchKernelGGL((k_fused<N, CAP, kFusedU>), dim3(grid_for(n4, kFusedU)), dim3(kBlock), kFusedLds, s, c,
+    hipLaunchKernelGGL((k_fused<N, CAP, kFusedU, QB>), dim3(grid_for(n4, kFusedU)), dim3(kBlock), kFusedLds, s, c,
                        cp, n, (float)n, reinterpret_cast<f32x4*>(master), reinterpret_cast<f32x4*>(m),
                        reinterpret_cast<f32x4*>(v), reinterpret_cast<u32x2*>(grad),
-                       reinterpret_cast<u32x2*>(param), reinterpret_cast<u32x2*>(full), n4);
+                       reinterpret_cast<u32x2*>(param), reinterpret_cast<u32x2*>(full), n4, qo);
     return (int)hipGetLastError();
+}
+
+template <int N, int CAP>
+int launch_fused_t(const AdamCoef& c, const void* const* contribs, int n, float* master, float* m,
+                   float* v, void* grad, void* param, void* full, int64_t len, const QuantOut* q, hipStream_t s) {
+    if (!q) return launch_fused_q<N, CAP, 0>(c, contribs, n, master, m, v, grad, param, full, len, QuantOut{}, s);
+    if (q->bits == 8) return launch_fused_q<N, CAP, 8>(c, contribs, n, master, m, v, grad, param, full, len, *q, s);
+    return launch_fused_q<N, CAP, 4>(c, contribs, n, master, m, v, grad, param, full, len, *q, s);
 }
 
 template <int OP, int N>
@@ -732,6 +886,17 @@ int launch_accum_t(const void* const* contribs, int n, float* acc, int first, in
     return (int)hipGetLastError();
 }
 
+template <int QB>
+int launch_adamw_q(const AdamCoef& c, const void* grad, float* master, float* m, float* v, void* param,
+                   void* full_at_own, int64_t len, const QuantOut& qo, hipStream_t s) {
+    const int64_t n4 = len / 4;
+    hipLaunchKernelGGL((k_adamw<kAdamwU, QB>), dim3(grid_for(n4, kAdamwU)), dim3(kBlock), kAdamwLds, s, c,
+                       reinterpret_cast<const u32x2*>(grad), reinterpret_cast<f32x4*>(master),
+                       reinterpret_cast<f32x4*>(m), reinterpret_cast<f32x4*>(v), reinterpret_cast<u32x2*>(param),
+                       reinterpret_cast<u32x2*>(full_at_own), n4, qo);
+    return (int)hipGetLastError();
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ public launchers
@@ -752,14 +917,42 @@ int launch_reduce(const void* const* contribs, int n, void* grad, int64_t len, v
 }
 
 int launch_adamw(const AdamCoef& c, const void* grad, float* master, float* m, float* v, void* param,
-                 void* full_at_own, int64_t len, void* stream) {
+                 void* full_at_own, int64_t len, void* stream, const QuantOut* q) {
     if (len <= 0) return 0;
-    const int64_t n4 = len / 4;
-    hipLaunchKernelGGL((k_adamw<kAdamwU>), dim3(grid_for(n4, kAdamwU)), dim3(kBlock), kAdamwLds,
-                       (hipStream_t)stream, c, reinterpret_cast<const u32x2*>(grad),
-                       reinterpret_cast<f32x4*>(master), reinterpret_cast<f32x4*>(m),
-                       reinterpret_cast<f32x4*>(v), reinterpret_cast<u32x2*>(param),
-                       reinterpret_cast<u32x2*>(full_at_own), n4);
+    hipStream_t s = (hipStream_t)stream;
+    if (!q) return launch_adamw_q<0>(c, grad, master, m, v, param, full_at_own, len, QuantOut{}, s);
+    if (q->bits == 8) return launch_adamw_q<8>(c, grad, master, m, v, param, full_at_own, len, *q, s);
+    return launch_adamw_q<4>(c, grad, master, m, v, param, full_at_own, len, *q, s);
+}
+
+int launch_quantize(const QuantOut& q, const void* param, int64_t len, void* stream) {
+    if (len <= 0) return 0;
+    const int64_t n8 = len / 8;
+    hipStream_t s = (hipStream_t)stream;
+    if (q.bits == 8)
+        hipLaunchKernelGGL(k_quant<8>, dim3(grid_for(n8, 1)), dim3(kBlock), kGatherLds, s,
+                           reinterpret_cast<const u32x4*>(param), q, n8);
+    else
+        hipLaunchKernelGGL(k_quant<4>, dim3(grid_for(n8, 1)), dim3(kBlock), kGatherLds, s,
+                           reinterpret_cast<const u32x4*>(param), q, n8);
+    return (int)hipGetLastError();
+}
+
+int launch_dequant(int bits, int block, const void* codes_all, const float* scales_all, int64_t code_bytes,
+                   int64_t n_scales, int n_ranks, void* full, int64_t S, void* stream) {
+    if (S <= 0 || n_ranks <= 0) return 0;
+    const int64_t s8 = S / 8;
+    int shift = 0;
+    while ((1 << shift) < block) ++shift;
+    const dim3 grid(grid_for(s8, 1), (unsigned)n_ranks);
+    hipStream_t s = (hipStream_t)stream;
+    const char* cb = static_cast<const char*>(codes_all);
+    if (bits == 8)
+        hipLaunchKernelGGL(k_dequant<8>, grid, dim3(kBlock), kGatherLds, s, cb, scales_all, code_bytes, n_scales,
+                           shift, reinterpret_cast<u32x4*>(full), s8);
+    else
+        hipLaunchKernelGGL(k_dequant<4>, grid, dim3(kBlock), kGatherLds, s, cb, scales_all, code_bytes, n_scales,
+                           shift, reinterpret_cast<u32x4*>(full), s8);
     return (int)hipGetLastError();
 }
 
@@ -772,25 +965,25 @@ int launch_gather(const void* param, void* full_at_own, int64_t len, void* strea
 }
 
 int launch_fused(const AdamCoef& c, const void* const* contribs, int n, float* master, float* m, float* v,
-                 void* grad, void* param, void* full_at_own, int64_t len, void* stream) {
+                 void* grad, void* param, void* full_at_own, int64_t len, void* stream, const QuantOut* q) {
     if (len <= 0) return 0;
     if (kSplitMinN > 0 && n >= kSplitMinN && grad) {
         // Large N: a nearly read-only reduce, then AdamW writing the outputs.
         // Same bytes in every buffer as the one-pass kernel.
         if (int e = launch_reduce(contribs, n, grad, len, stream)) return e;
-        return launch_adamw(c, grad, master, m, v, param, full_at_own, len, stream);
+        return launch_adamw(c, grad, master, m, v, param, full_at_own, len, stream, q);
     }
     hipStream_t s = (hipStream_t)stream;
+    void* f = full_at_own;
     switch (n) {
-        case 1: return launch_fused_t<1, 1>(c, contribs, n, master, m, v, grad, param, full_at_own, len, s);
-        case 2: return launch_fused_t<2, 2>(c, contribs, n, master, m, v, grad, param, full_at_own, len, s);
-        case 4: return launch_fused_t<4, 4>(c, contribs, n, master, m, v, grad, param, full_at_own, len, s);
-        case 8: return launch_fused_t<8, 8>(c, contribs, n, master, m, v, grad, param, full_at_own, len, s);
-        case 16: return launch_fused_t<16, 16>(c, contribs, n, master, m, v, grad, param, full_at_own, len, s);
-        case 32: return launch_fused_t<32, 32>(c, contribs, n, master, m, v, grad, param, full_at_own, len, s);
-        case 64: return launch_fused_t<64, 64>(c, contribs, n, master, m, v, grad, param, full_at_own, len, s);
-        default:
-            return launch_fused_t<0, ZS_MAX_CONTRIBS>(c, contribs, n, master, m, v, grad, param, full_at_own, len, s);
+        case 1: return launch_fused_t<1, 1>(c, contribs, n, master, m, v, grad, param, f, len, q, s);
+        case 2: return launch_fused_t<2, 2>(c, contribs, n, master, m, v, grad, param, f, len, q, s);
+        case 4: return launch_fused_t<4, 4>(c, contribs, n, master, m, v, grad, param, f, len, q, s);
+        case 8: return launch_fused_t<8, 8>(c, contribs, n, master, m, v, grad, param, f, len, q, s);
+        case 16: return launch_fused_t<16, 16>(c, contribs, n, master, m, v, grad, param, f, len, q, s);
+        case 32: return launch_fused_t<32, 32>(c, contribs, n, master, m, v, grad, param, f, len, q, s);
+        case 64: return launch_fused_t<64, 64>(c, contribs, n, master, m, v, grad, param, f, len, q, s);
+        default: return launch_fused_t<0, ZS_MAX_CONTRIBS>(c, contribs, n, master, m, v, grad, param, f, len, q, s);
     }
 }
 

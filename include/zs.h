@@ -262,6 +262,50 @@ zs_status zs_adamw_shard_step_multi_groups(const zs_plan* plan, const zs_adamw_h
 zs_status zs_fused_shard_step_multi_groups(const zs_plan* plan, const zs_adamw_hparams* hps, int32_t n_groups,
                                            const void* workspace, void* stream);
 
+/* ------------------------------------------------------------------ quantized parameter gather
+ * ZeRO++ moves the gathered parameters as low-bit codes, 4 bits giving up to
+ * four times less all-gather traffic ("ZeRO vs FSDP...", section 5.2). Here
+ * each rank quantizes its updated bf16 shard block-wise and symmetrically;
+ * the all-gather then carries every rank's codes and scales, and every rank
+ * (the owner included) decodes all of them into the gathered buffer, so all
+ * ranks hold the same dequantized parameters. The fp32 master weights stay
+ * exact. FLAT plans only.
+ *
+ * Per block of `block` consecutive shard elements (the last block of a shard
+ * may be shorter): amax = max |x|; scale = fp32(amax / qmax), qmax = 127 for
+ * bits = 8 and 7 for bits = 4; code = x / scale (one fp32 division) rounded
+ * to nearest, ties to even, clamped to [-qmax, qmax]. amax == 0 gives scale
+ * 0 and codes 0; a NaN or infinity in the block gives scale NaN and codes 0.
+ * Decoding: x' = bf16_rne(f32(code) * scale).
+ * Codes: bits = 8 -- one two's-complement byte per element; bits = 4 -- two
+ * elements per byte, the even element in the low nibble. block is a power
+ * of two in [8, 256].
+ *
+ * One rank's payload: zs_quant_code_bytes(plan, bits) code bytes (S*bits/8)
+ * and zs_quant_num_scales(plan, block) fp32 scales (ceil(S/block)); -1 on a
+ * bad argument. */
+int64_t zs_quant_code_bytes(const zs_plan* plan, int32_t bits);
+int64_t zs_quant_num_scales(const zs_plan* plan, int32_t block);
+
+/* Codes and scales of a bf16 shard (S elements of param_bf16). */
+zs_status zs_quantize_shard(const zs_plan* plan, int32_t bits, int32_t block, const void* param_bf16, void* codes,
+                            float* scales, void* stream);
+
+/* zs_fused_shard_step whose gather output is the quantized payload: the
+ * reduce and AdamW as there (grad_bf16 and param_bf16 optional), then the
+ * updated bf16 shard's codes and scales, bit-identical to
+ * zs_quantize_shard of the param_bf16 zs_fused_shard_step writes. */
+zs_status zs_fused_shard_step_quant(const zs_plan* plan, const zs_adamw_hparams* hp, const void* const* contribs,
+                                    int32_t n_contribs, float* master, float* m, float* v, void* grad_bf16,
+                                    void* param_bf16, int32_t bits, int32_t block, void* codes, float* scales,
+                                    void* stream);
+
+/* The receiving side: codes_all holds the N ranks' codes end to end (rank q
+ * at q * zs_quant_code_bytes), scales_all their scales end to end (rank q at
+ * q * zs_quant_num_scales); writes every element of full_bf16[0, T). */
+zs_status zs_dequant_gather(const zs_plan* plan, int32_t bits, int32_t block, const void* codes_all,
+                            const float* scales_all, void* full_bf16, void* stream);
+
 /* ------------------------------------------------------------------ accumulation and clipping
  * Gradient accumulation over G micro-batches with an fp32 gradient shard,
  * global-norm clipping and a non-finite skip ("从 Data Parallel 到

@@ -226,3 +226,35 @@ def test_multi_validation_without_device(zs):
     assert L.zs_multi_bind(pt.handle, recs, None, 0, FAKE, need, None) == zs.ZS_EINVAL
     # flat plans have no multi-tensor form
     assert L.zs_gather_params_multi(flat.handle, FAKE, None) == zs.ZS_EINVAL
+
+
+def test_quant_validation_without_device(zs):
+    L = zs.lib()
+    plan = zs.zs_shard_plan([1000, 24], 4, 1)  # S = 256
+    h = plan.handle
+    assert L.zs_quant_code_bytes(h, 8) == 256 and L.zs_quant_code_bytes(h, 4) == 128
+    assert L.zs_quant_code_bytes(h, 2) == -1 and L.zs_quant_code_bytes(None, 8) == -1
+    assert L.zs_quant_num_scales(h, 64) == 4 and L.zs_quant_num_scales(h, 256) == 1
+    assert L.zs_quant_num_scales(h, 48) == -1 and L.zs_quant_num_scales(h, 512) == -1
+    assert zs.zs_quant_num_scales(zs.zs_shard_plan([1000], 4, 0), 128) == 2  # S = 256 -> 2 blocks
+    assert zs.zs_quant_num_scales(zs.zs_shard_plan([1200], 4, 0), 256) == 2  # S = 304 -> ragged 2nd block
+    for bits, block in ((2, 64), (16, 64), (8, 4), (8, 512), (4, 96), (8, 0)):
+        assert L.zs_quantize_shard(h, bits, block, FAKE, FAKE, FAKE, None) == zs.ZS_EINVAL
+        assert L.zs_dequant_gather(h, bits, block, FAKE, FAKE, FAKE, None) == zs.ZS_EINVAL
+    assert L.zs_quantize_shard(h, 8, 64, None, FAKE, FAKE, None) == zs.ZS_EINVAL
+    assert L.zs_quantize_shard(h, 8, 64, FAKE, FAKE + 4, FAKE, None) == zs.ZS_EALIGN
+    assert L.zs_dequant_gather(h, 4, 64, FAKE, FAKE, None, None) == zs.ZS_EINVAL
+    pt = zs.zs_shard_plan([1000], 4, 1, 1, zs.ZS_LAYOUT_PER_TENSOR)
+    assert L.zs_quantize_shard(pt.handle, 8, 64, FAKE, FAKE, FAKE, None) == zs.ZS_EINVAL
+    assert "FLAT" in zs.zs_last_error()
+    vp = ctypes.c_void_p
+    good = (vp * 4)(FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288)
+    hp = zs.AdamWHParams()
+    fq = L.zs_fused_shard_step_quant
+    assert fq(h, ctypes.byref(hp), good, 4, FAKE, FAKE, FAKE, None, None, 8, 64, None, FAKE, None) == zs.ZS_EINVAL
+    assert fq(h, ctypes.byref(hp), good, 3, FAKE, FAKE, FAKE, None, None, 8, 64, FAKE, FAKE, None) == zs.ZS_EINVAL
+    assert fq(h, ctypes.byref(hp), good, 4, FAKE, FAKE, FAKE, None, None, 4, 7, FAKE, FAKE, None) == zs.ZS_EINVAL
+    bad = zs.AdamWHParams(step=0)
+    assert fq(h, ctypes.byref(bad), good, 4, FAKE, FAKE, FAKE, None, None, 8, 64, FAKE, FAKE, None) == zs.ZS_EINVAL
+    empty = zs.zs_shard_plan([], 4, 0)
+    assert L.zs_quantize_shard(empty.handle, 8, 64, FAKE, FAKE, FAKE, None) == zs.ZS_OK  # nothing to launch
