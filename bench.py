@@ -64,6 +64,9 @@ def parse():
                     help="also time an optimizer step with this many accumulated micro-batches, global-norm "
                          "clipping and the non-finite skip (FLAT workloads)")
     ap.add_argument("--clip", type=float, default=1.0, help="max norm of the --accum path")
+    ap.add_argument("--quant", default="4:256",
+                    help="BITS:BLOCK of the quantized-gather legs (fused step writing codes, and the "
+                         "dequantizing gather of all ranks' payloads), FLAT workloads; 'none' skips them")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
     return ap.parse_args()
@@ -304,6 +307,51 @@ def main():
                                        "bytes_per_param": unfused_bytes_per_param(N),
                                        "launches_per_step": (S + B - 1) // B + 2,
                                        "reduce_buckets": (S + B - 1) // B}
+        if args.quant != "none":
+            bits, qblock = (int(x) for x in args.quant.split(":"))
+            nq, ns = zs.zs_quant_code_bytes(plan, bits), zs.zs_quant_num_scales(plan, qblock)
+            codes = torch.empty(nq, dtype=torch.uint8, device="cuda")
+            scales = torch.empty(ns, dtype=torch.float32, device="cuda")
+
+            def fused_q(t, timer):
+                e = timer.start() if timer else None
+                zs.zs_fused_shard_step_quant(plan, hp0.at(t), st["contribs"], st["master"], st["m"], st["v"],
+                                             bits, qblock, codes, scales, grad=grad_out)
+                if timer:
+                    timer.stop(e)
+
+            q_wall, q_dev, q_ev = time_loop(fused_q, 1, max(3, args.steps // 2))
+            q_bpp = fused_bytes_per_param(N, write_grad=write_grad) - 2 + bits / 8 + 4 / qblock
+            result_paths["fused_quant"] = {"bits": bits, "block": qblock, "ms_per_step": q_wall,
+                                           "device_ms_per_step": q_dev, "events_ms_median": statistics.median(q_ev),
+                                           "bytes_per_param": q_bpp, "gbps": S * q_bpp / (q_dev / 1e3) / 1e9,
+                                           "payload_bytes": nq + 4 * ns,
+                                           "bf16_slice_bytes": 2 * S}
+            T = plan.padded_numel
+            free, _ = torch.cuda.mem_get_info()
+            if st["full_is_T"] and free > N * (nq + 4 * ns) + (2 << 30):
+                # every rank's payload (copies of this rank's stand in for the others)
+                codes_all = codes.repeat(N)
+                scales_all = scales.repeat(N)
+
+                def dequant(t, timer):
+                    e = timer.start() if timer else None
+                    zs.zs_dequant_gather(plan, bits, qblock, codes_all, scales_all, st["full"])
+                    if timer:
+                        timer.stop(e)
+
+                d_wall, d_dev, d_ev = time_loop(dequant, 1, max(3, args.steps // 2))
+                d_bpe = bits / 8 + 4 / qblock + 2
+                result_paths["dequant_gather"] = {"bits": bits, "block": qblock, "gathered_elems": T,
+                                                  "ms_per_step": d_wall, "device_ms_per_step": d_dev,
+                                                  "events_ms_median": statistics.median(d_ev),
+                                                  "bytes_per_gathered_elem": d_bpe,
+                                                  "gbps": T * d_bpe / (d_dev / 1e3) / 1e9}
+                del codes_all, scales_all
+            else:
+                result_paths["dequant_gather"] = {"skipped": "the gathered buffer and all payloads do not fit "
+                                                             "beside the resident contributions"}
+            del codes, scales
         if args.accum > 0:
             G, B = args.accum, wl.bucket_elems or S
             acc = torch.empty(S, dtype=torch.float32, device="cuda")

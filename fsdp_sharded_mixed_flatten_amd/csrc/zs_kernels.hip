@@ -68,6 +68,13 @@
 #ifndef ZS_MULTI_LDS_KB
 #define ZS_MULTI_LDS_KB 16
 #endif
+// Dequantizing gather: 8-element units per lane, and its occupancy throttle.
+#ifndef ZS_DEQUANT_U
+#define ZS_DEQUANT_U 4
+#endif
+#ifndef ZS_DEQUANT_LDS_KB
+#define ZS_DEQUANT_LDS_KB 0
+#endif
 // World size from which the fused entry point runs reduce, then AdamW +
 // gather, when the caller provides the grad buffer (0: never).
 #ifndef ZS_SPLIT_MIN_N
@@ -106,6 +113,8 @@ constexpr unsigned kAdamwLds = ZS_ADAMW_LDS_KB * 1024u;
 constexpr unsigned kGatherLds = ZS_GATHER_LDS_KB * 1024u;
 constexpr unsigned kMultiLds = ZS_MULTI_LDS_KB * 1024u;
 constexpr int kSplitMinN = ZS_SPLIT_MIN_N;
+constexpr int kDequantU = ZS_DEQUANT_U;
+constexpr unsigned kDequantLds = ZS_DEQUANT_LDS_KB * 1024u;
 
 // ------------------------------------------------------------------ bf16
 
@@ -332,10 +341,16 @@ __device__ __forceinline__ void reduce4_tile(const void* const* cp, int n_rt, fl
 // and its amax is a butterfly max over them. Every lane of the wave must call
 // this (the shuffles), with ok == false where it holds no elements.
 
+// The codes of one lane (QB*E bits, low element first) and its block's scale.
+struct QuantWord {
+    uint32_t lo, hi;
+    float scale;
+};
+
 template <int QB, int E>
-__device__ __forceinline__ void quant_store(const uint32_t* w, bool ok, int64_t unit, const QuantOut& qo) {
+__device__ __forceinline__ QuantWord quant_compute(const uint32_t* w, bool ok, int block) {
     constexpr float qmax = (float)((1 << (QB - 1)) - 1);
-    const int lanes = qo.block / E;
+    const int lanes = block / E;
     float x[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) x[e] = (e & 1) ? hi_bf16(w[e >> 1]) : lo_bf16(w[e >> 1]);
@@ -354,43 +369,41 @@ __device__ __forceinline__ void quant_store(const uint32_t* w, bool ok, int64_t 
         amax = o > amax ? o : amax;
         bad |= __shfl_xor(bad, off, 64);
     }
-    if (!ok) return;
-    const float scale = bad ? __builtin_nanf("") : amax / qmax;
+    QuantWord q;
+    q.scale = bad ? __builtin_nanf("") : amax / qmax;
     const bool zero = bad || !(amax > 0.0f);
-    uint32_t lo = 0, hi = 0;
+    q.lo = 0u;
+    q.hi = 0u;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        int k = 0;
-        if (!zero) {
-            float r = rintf(x[e] / scale);
-            r = r > qmax ? qmax : r;
-            r = r < -qmax ? -qmax : r;
-            k = (int)r;
-        }
+        // Branch-free: a zero or NaN scale gives an inf/NaN quotient that the
+        // select below discards.
+        float r = rintf(x[e] / q.scale);
+        r = r > qmax ? qmax : r;
+        r = r < -qmax ? -qmax : r;
+        const int k = zero ? 0 : (int)r;
         const uint32_t c = (uint32_t)k & ((1u << QB) - 1u);
         if (QB * e < 32)
-            lo |= c << (QB * e);
+            q.lo |= c << (QB * e);
         else
-            hi |= c << (QB * e - 32);
+            q.hi |= c << (QB * e - 32);
     }
+    return q;
+}
+
+// Stores a lane's codes, and its block's scale from the block's first lane.
+template <int QB, int E>
+__device__ __forceinline__ void quant_emit(const QuantWord& q, int64_t unit, const QuantOut& qo) {
+    const int lanes = qo.block / E;
     const int64_t first = unit * E;  // first element of the lane
     char* cb = static_cast<char*>(qo.codes) + first * QB / 8;
     if constexpr (QB * E == 64)
-        st_out(reinterpret_cast<u32x2*>(cb), u32x2{lo, hi});
+        st_out(reinterpret_cast<u32x2*>(cb), u32x2{q.lo, q.hi});
     else if constexpr (QB * E == 32)
-        st_out(reinterpret_cast<uint32_t*>(cb), lo);
+        st_out(reinterpret_cast<uint32_t*>(cb), q.lo);
     else
-        st_out(reinterpret_cast<uint16_t*>(cb), (uint16_t)lo);
-    if ((threadIdx.x & (lanes - 1)) == 0) st_out(qo.scales + first / qo.block, scale);
-}
-
-template <int QB, int U>
-__device__ __forceinline__ void quant_units(const u32x2* pv, const bool* ok, const int64_t* u, const QuantOut& qo) {
-#pragma unroll
-    for (int k = 0; k < U; ++k) {
-        const uint32_t w[2] = {pv[k].x, pv[k].y};
-        quant_store<QB, 4>(w, ok[k], u[k], qo);
-    }
+        st_out(reinterpret_cast<uint16_t*>(cb), (uint16_t)q.lo);
+    if ((threadIdx.x & (lanes - 1)) == 0) st_out(qo.scales + first / qo.block, q.scale);
 }
 
 // AdamW from a bf16 grad; writes the bf16 parameter to `param` and/or `full`
@@ -399,42 +412,46 @@ __device__ __forceinline__ void adamw_tile(const AdamCoef& c, const u32x2* __res
                                            f32x4* __restrict__ m, f32x4* __restrict__ v, u32x2* __restrict__ param,
                                            u32x2* __restrict__ full, int64_t base, int64_t limit,
                                            const QuantOut& qo = QuantOut{}) {
-    u32x2 gv[U], pv[U];
-    int64_t uu[U];
+    int64_t u[U];
     bool ok[U];
+    u32x2 gv[U], pv[U];
     f32x4 wv[U], mv[U], vv[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-        const int64_t u = base + (int64_t)k * kBlock;
-        if (u < limit) {
-            gv[k] = ld_in(g + u);
-            wv[k] = ld_state(master + u);
-            mv[k] = ld_state(m + u);
-            vv[k] = ld_state(v + u);
+        u[k] = base + (int64_t)k * kBlock;
+        ok[k] = u[k] < limit;
+        pv[k] = u32x2{0u, 0u};
+        if (ok[k]) {
+            gv[k] = ld_in(g + u[k]);
+            wv[k] = ld_state(master + u[k]);
+            mv[k] = ld_state(m + u[k]);
+            vv[k] = ld_state(v + u[k]);
         }
     }
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-        const int64_t u = base + (int64_t)k * kBlock;
-        if (u < limit) {
-            adamw_unit(c, gv[k], wv[k], mv[k], vv[k]);
-            st_state(master + u, wv[k]);
-            st_state(m + u, mv[k]);
-            st_state(v + u, vv[k]);
-            const u32x2 p = to_bf16x4(wv[k]);
-            pv[k] = p;
-            if (param) st_out(param + u, p);
-            if (full) st_out(full + u, p);
-        }
+        if (!ok[k]) continue;
+        adamw_unit(c, gv[k], wv[k], mv[k], vv[k]);
+        pv[k] = to_bf16x4(wv[k]);
     }
+    // Codes are computed by every lane before any store is issued.
+    QuantWord qw[QB != 0 ? U : 1];
     if constexpr (QB != 0) {
 #pragma unroll
         for (int k = 0; k < U; ++k) {
-            uu[k] = base + (int64_t)k * kBlock;
-            ok[k] = uu[k] < limit;
-            if (!ok[k]) pv[k] = u32x2{0u, 0u};
+            const uint32_t w[2] = {pv[k].x, pv[k].y};
+            qw[k] = quant_compute<QB, 4>(w, ok[k], qo.block);
         }
-        quant_units<QB, U>(pv, ok, uu, qo);
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        if (!ok[k]) continue;
+        st_state(master + u[k], wv[k]);
+        st_state(m + u[k], mv[k]);
+        st_state(v + u[k], vv[k]);
+        if (param) st_out(param + u[k], pv[k]);
+        if (full) st_out(full + u[k], pv[k]);
+        if constexpr (QB != 0) quant_emit<QB, 4>(qw[k], u[k], qo);
     }
 }
 
@@ -464,7 +481,7 @@ __device__ __forceinline__ void fused_tile(const AdamCoef& c, const void* const*
     int64_t u[U];
     bool ok[U];
     f32x4 wv[U], mv[U], vv[U];
-    u32x2 pv[U];
+    u32x2 gv[U], pv[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
         u[k] = base + (int64_t)k * kBlock;
@@ -478,21 +495,47 @@ __device__ __forceinline__ void fused_tile(const AdamCoef& c, const void* const*
     }
     float a[U][4];
     rank_sum<u32x2, U, N>(cp, n_rt, u, ok, a);
+    if constexpr (QB == 0) {
 #pragma unroll
-    for (int k = 0; k < U; ++k) {
-        if (!ok[k]) continue;
-        const u32x2 g = avg_bf16x4<N>(a[k], nf);
-        adamw_unit(c, g, wv[k], mv[k], vv[k]);
-        st_state(master + u[k], wv[k]);
-        st_state(m + u[k], mv[k]);
-        st_state(v + u[k], vv[k]);
-        const u32x2 p = to_bf16x4(wv[k]);
-        pv[k] = p;
-        if (grad) st_out(grad + u[k], g);
-        if (param) st_out(param + u[k], p);
-        if (full) st_out(full + u[k], p);
+        for (int k = 0; k < U; ++k) {
+            if (!ok[k]) continue;
+            const u32x2 g = avg_bf16x4<N>(a[k], nf);
+            adamw_unit(c, g, wv[k], mv[k], vv[k]);
+            st_state(master + u[k], wv[k]);
+            st_state(m + u[k], mv[k]);
+            st_state(v + u[k], vv[k]);
+            const u32x2 p = to_bf16x4(wv[k]);
+            if (grad) st_out(grad + u[k], g);
+            if (param) st_out(param + u[k], p);
+            if (full) st_out(full + u[k], p);
+        }
+    } else {
+        // Codes are computed by every lane before any store is issued.
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            if (!ok[k]) continue;
+            gv[k] = avg_bf16x4<N>(a[k], nf);
+            adamw_unit(c, gv[k], wv[k], mv[k], vv[k]);
+            pv[k] = to_bf16x4(wv[k]);
+        }
+        QuantWord qw[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const uint32_t w[2] = {pv[k].x, pv[k].y};
+            qw[k] = quant_compute<QB, 4>(w, ok[k], qo.block);
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            if (!ok[k]) continue;
+            st_state(master + u[k], wv[k]);
+            st_state(m + u[k], mv[k]);
+            st_state(v + u[k], vv[k]);
+            if (grad) st_out(grad + u[k], gv[k]);
+            if (param) st_out(param + u[k], pv[k]);
+            if (full) st_out(full + u[k], pv[k]);
+            quant_emit<QB, 4>(qw[k], u[k], qo);
+        }
     }
-    if constexpr (QB != 0) quant_units<QB, U>(pv, ok, u, qo);
 }
 
 // ------------------------------------------------------------------ flat kernels
@@ -543,49 +586,62 @@ __global__ __launch_bounds__(kBlock) void k_quant(const u32x4* __restrict__ p, Q
         w[2] = x.z;
         w[3] = x.w;
     }
-    quant_store<QB, 8>(w, ok, u, qo);
+    const QuantWord q = quant_compute<QB, 8>(w, ok, qo.block);
+    if (ok) quant_emit<QB, 8>(q, u, qo);
 }
 
 // The receiving side of the quantized gather: blockIdx.y is the rank whose
-// payload a block decodes, 8 elements per lane, one 16-byte store each.
-template <int QB>
+// payload a block decodes; a lane decodes U units of 8 elements (units
+// kBlock apart), each one 16-byte store.
+template <int QB, int U>
 __global__ __launch_bounds__(kBlock) void k_dequant(const char* __restrict__ codes_all,
                                                     const float* __restrict__ scales_all, int64_t code_bytes,
                                                     int64_t n_scales, int block_shift, u32x4* __restrict__ full,
                                                     int64_t s8) {
     const int64_t r = blockIdx.y;
-    const int64_t u = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (u >= s8) return;
-    const char* cb = codes_all + r * code_bytes + u * QB;  // 8 codes of QB bits = QB bytes
-    const float scale = ld_in(scales_all + r * n_scales + ((u * 8) >> block_shift));
-    uint32_t lo, hi;
-    if constexpr (QB == 8) {
-        const u32x2 c = ld_in(reinterpret_cast<const u32x2*>(cb));
-        lo = c.x;
-        hi = c.y;
-    } else {
-        lo = ld_in(reinterpret_cast<const uint32_t*>(cb));
-        hi = 0u;
-    }
-    float x[8];
+    const int64_t base = (int64_t)blockIdx.x * kBlock * U + threadIdx.x;
+    const char* cb = codes_all + r * code_bytes;
+    const float* sb = scales_all + r * n_scales;
+    uint32_t lo[U], hi[U];
+    float sc[U];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        int k;
+    for (int k = 0; k < U; ++k) {
+        const int64_t u = base + (int64_t)k * kBlock;
+        if (u >= s8) continue;
+        sc[k] = ld_in(sb + ((u * 8) >> block_shift));
         if constexpr (QB == 8) {
-            const uint32_t w = e < 4 ? lo : hi;
-            k = (int)(int8_t)((w >> (8 * (e & 3))) & 0xFFu);
+            const u32x2 c = ld_in(reinterpret_cast<const u32x2*>(cb + u * 8));
+            lo[k] = c.x;
+            hi[k] = c.y;
         } else {
-            const int nib = (int)((lo >> (4 * e)) & 0xFu);
-            k = nib >= 8 ? nib - 16 : nib;
+            lo[k] = ld_in(reinterpret_cast<const uint32_t*>(cb + u * 4));
+            hi[k] = 0u;
         }
-        x[e] = (float)k * scale;
     }
-    u32x4 o;
-    o.x = pack2(x[0], x[1]);
-    o.y = pack2(x[2], x[3]);
-    o.z = pack2(x[4], x[5]);
-    o.w = pack2(x[6], x[7]);
-    st_out(full + r * s8 + u, o);
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const int64_t u = base + (int64_t)k * kBlock;
+        if (u >= s8) continue;
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            int q;
+            if constexpr (QB == 8) {
+                const uint32_t w = e < 4 ? lo[k] : hi[k];
+                q = (int)(int8_t)((w >> (8 * (e & 3))) & 0xFFu);
+            } else {
+                const int nib = (int)((lo[k] >> (4 * e)) & 0xFu);
+                q = nib >= 8 ? nib - 16 : nib;
+            }
+            x[e] = (float)q * sc[k];
+        }
+        u32x4 o;
+        o.x = pack2(x[0], x[1]);
+        o.y = pack2(x[2], x[3]);
+        o.z = pack2(x[4], x[5]);
+        o.w = pack2(x[6], x[7]);
+        st_out(full + r * s8 + u, o);
+    }
 }
 
 // ------------------------------------------------------------------ multi-tensor kernel
@@ -944,15 +1000,15 @@ int launch_dequant(int bits, int block, const void* codes_all, const float* scal
     const int64_t s8 = S / 8;
     int shift = 0;
     while ((1 << shift) < block) ++shift;
-    const dim3 grid(grid_for(s8, 1), (unsigned)n_ranks);
+    const dim3 grid(grid_for(s8, kDequantU), (unsigned)n_ranks);
     hipStream_t s = (hipStream_t)stream;
     const char* cb = static_cast<const char*>(codes_all);
     if (bits == 8)
-        hipLaunchKernelGGL(k_dequant<8>, grid, dim3(kBlock), kGatherLds, s, cb, scales_all, code_bytes, n_scales,
-                           shift, reinterpret_cast<u32x4*>(full), s8);
+        hipLaunchKernelGGL((k_dequant<8, kDequantU>), grid, dim3(kBlock), kDequantLds, s, cb, scales_all, code_bytes,
+                           n_scales, shift, reinterpret_cast<u32x4*>(full), s8);
     else
-        hipLaunchKernelGGL(k_dequant<4>, grid, dim3(kBlock), kGatherLds, s, cb, scales_all, code_bytes, n_scales,
-                           shift, reinterpret_cast<u32x4*>(full), s8);
+        hipLaunchKernelGGL((k_dequant<4, kDequantU>), grid, dim3(kBlock), kDequantLds, s, cb, scales_all, code_bytes,
+                           n_scales, shift, reinterpret_cast<u32x4*>(full), s8);
     return (int)hipGetLastError();
 }
 
