@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--quant", default="4:256",
                     help="BITS:BLOCK of the quantized-gather legs (fused step writing codes, and the "
                          "dequantizing gather of all ranks' payloads), FLAT workloads; 'none' skips them")
+    ap.add_argument("--no-offload", action="store_true",
+                    help="skip the CPU-offloaded optimizer step leg (FLAT workloads up to the 7B shape)")
+    ap.add_argument("--offload-chunk", type=int, default=1 << 24, help="elements per offload pipeline chunk")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
     return ap.parse_args()
@@ -218,6 +221,41 @@ def cpu_baseline(oracle, synth, wl, S, window, fused_bpp):
             "single_thread_params_per_s": n / secs1[0]}
 
 
+def offload_leg(zs, torch, plan, st, hp0, S, args, fused):
+    """ZeRO-Offload step: device grad shard -> pinned host, host AdamW on
+    pinned fp32 state, bf16 parameters -> the gathered buffer; pipelined in
+    chunks. Times whole steps (host arithmetic included)."""
+    threads = max(1, min(16, os.cpu_count() or 1))
+    try:
+        t0 = time.perf_counter()
+        hm = torch.empty(S, dtype=torch.float32, pin_memory=True)
+        hm.copy_(st["master"].cpu())
+        hmm = torch.zeros(S, dtype=torch.float32, pin_memory=True)
+        hv = torch.zeros(S, dtype=torch.float32, pin_memory=True)
+        gh = torch.empty(S, dtype=torch.int16, pin_memory=True)
+        ph = torch.empty(S, dtype=torch.int16, pin_memory=True)
+        alloc_s = time.perf_counter() - t0
+    except RuntimeError as e:
+        return {"skipped": f"pinned host buffers: {e}"}
+    zs.zs_reduce_shard(plan, st["contribs"], st["grad"])
+
+    def step(t, timer):
+        e = timer.start() if timer else None
+        zs.zs_offload_adamw_step(plan, hp0.at(t), st["grad"], hm, hmm, hv, gh, ph, full_dev=st["full"],
+                                 chunk_elems=args.offload_chunk, n_threads=threads)
+        if timer:
+            timer.stop(e)
+
+    wall, dev, ev = time_loop(step, 1, 3)
+    host_bpp, pcie_bpp = 28, 4
+    out = {"ms_per_step": wall, "events_ms_median": statistics.median(ev), "host_threads": threads,
+           "chunk_elems": args.offload_chunk, "host_bytes_per_param": host_bpp, "pcie_bytes_per_param": pcie_bpp,
+           "host_gbps": S * host_bpp / (wall / 1e3) / 1e9, "pcie_gbps": S * pcie_bpp / (wall / 1e3) / 1e9,
+           "slowdown_vs_fused_gpu_step": wall / fused["ms_per_step"], "pinned_alloc_s": alloc_s}
+    del hm, hmm, hv, gh, ph
+    return out
+
+
 def read_traffic(kernel_name, workload):
     if not os.path.exists(TRAFFIC_FILE):
         return None
@@ -352,6 +390,8 @@ def main():
                 result_paths["dequant_gather"] = {"skipped": "the gathered buffer and all payloads do not fit "
                                                              "beside the resident contributions"}
             del codes, scales
+        if not args.no_offload and S <= 1_000_000_000:
+            result_paths["offload"] = offload_leg(zs, torch, plan, st, hp0, S, args, result_paths["fused"])
         if args.accum > 0:
             G, B = args.accum, wl.bucket_elems or S
             acc = torch.empty(S, dtype=torch.float32, device="cuda")

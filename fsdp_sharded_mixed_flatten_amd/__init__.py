@@ -104,6 +104,9 @@ def _load():
         "zs_fused_shard_step_quant": (st, [vp, ctypes.POINTER(AdamWHParams), ctypes.POINTER(vp), i32, vp, vp, vp,
                                            vp, vp, i32, i32, vp, vp, vp]),
         "zs_dequant_gather": (st, [vp, i32, i32, vp, vp, vp, vp]),
+        "zs_host_adamw_step": (st, [ctypes.POINTER(AdamWHParams), vp, vp, vp, vp, vp, i64, i32]),
+        "zs_offload_adamw_step": (st, [vp, ctypes.POINTER(AdamWHParams), vp, vp, vp, vp, vp, vp, vp, vp, i64, i32,
+                                       vp]),
         "zs_accumulate_shard": (st, [vp, ctypes.POINTER(vp), i32, vp, i64, i64, i32, vp]),
         "zs_grad_stats_workspace_bytes": (i64, [vp]),
         "zs_grad_stats": (st, [vp, vp, ctypes.c_float, vp, vp, vp, i64, vp]),
@@ -129,7 +132,8 @@ EXPORTED = ("zs_shard_plan", "zs_shard_plan_ex", "zs_plan_tensor_group", "zs_pla
             "zs_reduce_shard_multi", "zs_adamw_shard_step_multi", "zs_gather_params_multi",
             "zs_fused_shard_step_multi", "zs_adamw_shard_step_multi_groups",
             "zs_fused_shard_step_multi_groups", "zs_quant_code_bytes", "zs_quant_num_scales", "zs_quantize_shard",
-            "zs_fused_shard_step_quant", "zs_dequant_gather", "zs_accumulate_shard", "zs_grad_stats_workspace_bytes",
+            "zs_fused_shard_step_quant", "zs_dequant_gather", "zs_host_adamw_step", "zs_offload_adamw_step",
+            "zs_accumulate_shard", "zs_grad_stats_workspace_bytes",
             "zs_grad_stats", "zs_clip_scale", "zs_adamw_shard_step_accum", "zs_last_error", "zs_version")
 
 
@@ -361,6 +365,55 @@ def zs_dequant_gather(plan, bits, block, codes_all, scales_all, full, stream=Non
     _check(_lib.zs_dequant_gather(plan.handle, bits, block, _ptr(codes_all, "bytes", N * S * bits // 8, "codes_all"),
                                   _ptr(scales_all, "f32", N * -(-S // max(block, 1)), "scales_all"),
                                   _ptr(full, "bf16", N * S, "full"), _stream(stream)))
+
+
+# ---------------------------------------------------------------- CPU-offloaded optimizer step
+
+_HOST_KINDS = {"bf16": ("uint16", "int16", "bfloat16"), "f32": ("float32",)}
+
+
+def _host_ptr(a, kind, need, what):
+    """Host address of a numpy array or CPU tensor after checking dtype, contiguity and length."""
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a
+    if hasattr(a, "is_cuda"):  # torch tensor
+        if a.is_cuda:
+            raise ValueError(f"{what} must be host memory")
+        if not a.is_contiguous():
+            raise ValueError(f"{what} must be contiguous")
+        dt, n, addr = str(a.dtype).split(".")[-1], a.numel(), a.data_ptr()
+    else:
+        if not a.flags.c_contiguous:
+            raise ValueError(f"{what} must be contiguous")
+        dt, n, addr = str(a.dtype), a.size, a.ctypes.data
+    if dt not in _HOST_KINDS[kind]:
+        raise ValueError(f"{what} must be {kind}, got {dt}")
+    if n < need:
+        raise ValueError(f"{what} holds {n} elements, the call touches {need}")
+    return addr
+
+
+def zs_host_adamw_step(hp, grad, master, m, v, param=None, n=None, n_threads=1):
+    if n is None:
+        n = master.numel() if hasattr(master, "numel") else master.size
+    _check(_lib.zs_host_adamw_step(ctypes.byref(hp), _host_ptr(grad, "bf16", n, "grad"),
+                                   _host_ptr(master, "f32", n, "master"), _host_ptr(m, "f32", n, "m"),
+                                   _host_ptr(v, "f32", n, "v"), _host_ptr(param, "bf16", n, "param"), n, n_threads))
+
+
+def zs_offload_adamw_step(plan, hp, grad_dev, master_host, m_host, v_host, grad_host, param_host, param_dev=None,
+                          full_dev=None, chunk_elems=1 << 24, n_threads=8, stream=None):
+    S, r = plan.shard_numel, plan.rank
+    _check(_lib.zs_offload_adamw_step(plan.handle, ctypes.byref(hp), _ptr(grad_dev, "bf16", S, "grad_dev"),
+                                      _host_ptr(master_host, "f32", S, "master_host"),
+                                      _host_ptr(m_host, "f32", S, "m_host"), _host_ptr(v_host, "f32", S, "v_host"),
+                                      _host_ptr(grad_host, "bf16", S, "grad_host"),
+                                      _host_ptr(param_host, "bf16", S, "param_host"),
+                                      _ptr(param_dev, "bf16", S, "param_dev"),
+                                      _ptr(full_dev, "bf16", (r + 1) * S, "full_dev"), chunk_elems, n_threads,
+                                      _stream(stream)))
 
 
 # ---------------------------------------------------------------- multi-tensor

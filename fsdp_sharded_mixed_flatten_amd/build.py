@@ -1,8 +1,9 @@
 """Builds the shard-step library libzs.so for gfx950, in-tree.
 
-Host code (plan, validation) is C++17; kernels are HIP compiled for gfx950
-with contraction off (the element arithmetic must round operation by
-operation) and packed-fp32 instruction generation disabled.
+Host code (plan, validation, the host AdamW of the offloaded step) is C++17;
+kernels and the offload pipeline are HIP compiled for gfx950. Everything is
+built with contraction off (the element arithmetic must round operation by
+operation); HIP code also with packed-fp32 instruction generation disabled.
 """
 
 import os
@@ -42,13 +43,20 @@ def build(verbose=False, out=None, defines=()):
     _run(["g++", *COMMON, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, "zs_api.cpp"), "-o", api_o],
          verbose)
     objs.append(api_o)
-    ker_o = os.path.join(BUILD, "zs_kernels.o")
-    _run([HIPCC, *COMMON, *HIP_ONLY, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, "zs_kernels.hip"),
-          "-o", ker_o], verbose)
-    objs.append(ker_o)
+    host_o = os.path.join(BUILD, "zs_host_adamw.o")
+    # host AdamW: same one-rounding-per-operation rule; -fno-math-errno lets
+    # sqrtf become the (correctly rounded) vector instruction
+    _run(["g++", *COMMON, "-fno-math-errno", "-pthread", "-c", os.path.join(CSRC, "zs_host_adamw.cpp"), "-o",
+          host_o], verbose)
+    objs.append(host_o)
+    for name in ("zs_kernels", "zs_offload"):
+        o = os.path.join(BUILD, f"{name}.o")
+        _run([HIPCC, *COMMON, *HIP_ONLY, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, f"{name}.hip"),
+              "-o", o], verbose)
+        objs.append(o)
     target = out or LIB
     tmp = target + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", "-o", tmp, *objs], verbose)
     os.replace(tmp, target)
     return target
 

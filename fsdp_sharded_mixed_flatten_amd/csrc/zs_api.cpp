@@ -412,6 +412,65 @@ zs_status zs_dequant_gather(const zs_plan* plan, int32_t bits, int32_t block, co
                       "dequantize launch");
 }
 
+// ------------------------------------------------------------------ CPU-offloaded optimizer step
+
+namespace {
+
+constexpr int32_t kMaxHostThreads = 256;
+
+zs_status check_host_threads(int32_t n_threads) {
+    if (n_threads < 1 || n_threads > kMaxHostThreads)
+        return fail(ZS_EINVAL, "n_threads = %d outside [1, %d]", n_threads, kMaxHostThreads);
+    return ZS_OK;
+}
+
+}  // namespace
+
+zs_status zs_host_adamw_step(const zs_adamw_hparams* hp, const void* grad_bf16, float* master, float* m, float* v,
+                             void* param_bf16, int64_t n, int32_t n_threads) {
+    if (zs_status st = check_hp(hp)) return st;
+    if (n < 0) return fail(ZS_EINVAL, "n = %lld is negative", (long long)n);
+    if (zs_status st = check_host_threads(n_threads)) return st;
+    if (zs_status st = check_ptr(grad_bf16, "grad_bf16")) return st;
+    if (zs_status st = check_ptr(master, "master")) return st;
+    if (zs_status st = check_ptr(m, "m")) return st;
+    if (zs_status st = check_ptr(v, "v")) return st;
+    if (zs_status st = check_opt_ptr(param_bf16, "param_bf16")) return st;
+    zs::host_adamw(zs::make_coef(*hp), static_cast<const uint16_t*>(grad_bf16), master, m, v,
+                   static_cast<uint16_t*>(param_bf16), n, n_threads);
+    return ZS_OK;
+}
+
+zs_status zs_offload_adamw_step(const zs_plan* plan, const zs_adamw_hparams* hp, const void* grad_bf16_dev,
+                                float* master_host, float* m_host, float* v_host, void* grad_bf16_host,
+                                void* param_bf16_host, void* param_bf16_dev, void* full_bf16_dev, int64_t chunk_elems,
+                                int32_t n_threads, void* stream) {
+    if (zs_status st = check_plan(plan)) return st;
+    if (zs_status st = check_hp(hp)) return st;
+    if (zs_status st = check_host_threads(n_threads)) return st;
+    if (chunk_elems < 1024 || chunk_elems % 8)
+        return fail(ZS_EINVAL, "chunk_elems = %lld must be a multiple of 8, at least 1024", (long long)chunk_elems);
+    if (zs_status st = check_ptr(grad_bf16_dev, "grad_bf16_dev")) return st;
+    if (zs_status st = check_ptr(master_host, "master_host")) return st;
+    if (zs_status st = check_ptr(m_host, "m_host")) return st;
+    if (zs_status st = check_ptr(v_host, "v_host")) return st;
+    if (zs_status st = check_ptr(grad_bf16_host, "grad_bf16_host")) return st;
+    if (zs_status st = check_ptr(param_bf16_host, "param_bf16_host")) return st;
+    if (zs_status st = check_opt_ptr(param_bf16_dev, "param_bf16_dev")) return st;
+    if (zs_status st = check_opt_ptr(full_bf16_dev, "full_bf16_dev")) return st;
+    if (full_bf16_dev && plan->layout != ZS_LAYOUT_FLAT)
+        return fail(ZS_EINVAL, "a gather into full_bf16_dev needs a FLAT plan");
+    if (plan->S == 0) return ZS_OK;
+    if (!zs::is_pinned_host(grad_bf16_host) || !zs::is_pinned_host(param_bf16_host))
+        return fail(ZS_EINVAL, "grad_bf16_host and param_bf16_host must be page-locked host memory "
+                               "(hipHostMalloc, or a pinned tensor)");
+    char* own = full_bf16_dev ? static_cast<char*>(full_bf16_dev) + 2 * (int64_t)plan->rank * plan->S : nullptr;
+    return hip_status(zs::offload_adamw(zs::make_coef(*hp), grad_bf16_dev, master_host, m_host, v_host,
+                                        grad_bf16_host, param_bf16_host, param_bf16_dev, own, plan->S, chunk_elems,
+                                        n_threads, stream),
+                      "offloaded step");
+}
+
 // ------------------------------------------------------------------ accumulation and clipping
 
 zs_status zs_accumulate_shard(const zs_plan* plan, const void* const* contribs, int32_t n_contribs, float* acc_f32,

@@ -143,6 +143,18 @@ enum MultiOp : int32_t { kOpReduce = 0, kOpAdamw = 1, kOpGather = 2, kOpFused = 
 int launch_multi(int op, const CoefTable* c, const void* workspace, int n_chunks, int n_contribs,
                  void* stream);
 int copy_h2d_sync(void* dst, const void* src, int64_t bytes, void* stream);
+
+// Host AdamW over n elements with n_threads host threads (zs_host_adamw.cpp);
+// p may be nullptr.
+void host_adamw(const AdamCoef& c, const uint16_t* g, float* master, float* m, float* v, uint16_t* p, int64_t n,
+                int n_threads);
+// zs_offload.hip: 1 if p is page-locked host memory known to the HIP runtime.
+int is_pinned_host(const void* p);
+// CPU-offloaded step of `len` elements in chunks of `chunk`; returns a
+// hipError_t value.
+int offload_adamw(const AdamCoef& c, const void* grad_dev, float* master, float* m, float* v, void* grad_host,
+                  void* param_host, void* param_dev, void* full_own_dev, int64_t len, int64_t chunk, int n_threads,
+                  void* stream);
 const char* hip_error_text(int err);
 
 }  // namespace zs

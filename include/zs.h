@@ -306,6 +306,38 @@ zs_status zs_fused_shard_step_quant(const zs_plan* plan, const zs_adamw_hparams*
 zs_status zs_dequant_gather(const zs_plan* plan, int32_t bits, int32_t block, const void* codes_all,
                             const float* scales_all, void* full_bf16, void* stream);
 
+/* ------------------------------------------------------------------ CPU-offloaded optimizer step
+ * ZeRO-Offload keeps the fp32 optimizer state in host memory and runs the
+ * step on the CPU ("ZeRO vs FSDP...", section 2.4); the step then pays PCIe
+ * transfers and host memory bandwidth, hidden only as far as they overlap
+ * ("从 Data Parallel 到 ZeRO/FSDP", section "CPU/NVMe Offload 不是免费显存").
+ * Both calls compute exactly the AdamW of zs_adamw_shard_step (same fp32
+ * operations in the same order), so host and device steps give identical
+ * bytes. */
+
+/* AdamW on host arrays of n elements with n_threads host threads: reads
+ * grad_bf16, updates master/m/v, writes param_bf16 (optional). Synchronous.
+ * Host pointers, 16-byte aligned; 1 <= n_threads <= 256. */
+zs_status zs_host_adamw_step(const zs_adamw_hparams* hp, const void* grad_bf16, float* master, float* m, float* v,
+                             void* param_bf16, int64_t n, int32_t n_threads);
+
+/* Offloaded step of the rank's shard (S elements): the device grad shard
+ * (grad_bf16_dev, complete in `stream` order) is copied chunk by chunk into
+ * grad_bf16_host; each chunk is stepped on the host (master/m/v_host) as
+ * soon as it arrives, and its bf16 parameters (param_bf16_host) are copied
+ * back to param_bf16_dev and/or the gathered buffer full_bf16_dev (FLAT, at
+ * r*S) on a second stream while the next chunks arrive and update. Later
+ * work on `stream` sees the new parameters. grad_bf16_host and
+ * param_bf16_host must be page-locked (hipHostMalloc or pinned tensors);
+ * chunk_elems is a multiple of 8, at least 1024. The call returns once the
+ * host arithmetic is done (it waits on the copies it needs). Calls are
+ * serialized process-wide. Unlike the other calls, a ZS_EHIP return in the
+ * middle of the pipeline may leave a prefix of the chunks updated. */
+zs_status zs_offload_adamw_step(const zs_plan* plan, const zs_adamw_hparams* hp, const void* grad_bf16_dev,
+                                float* master_host, float* m_host, float* v_host, void* grad_bf16_host,
+                                void* param_bf16_host, void* param_bf16_dev, void* full_bf16_dev, int64_t chunk_elems,
+                                int32_t n_threads, void* stream);
+
 /* ------------------------------------------------------------------ accumulation and clipping
  * Gradient accumulation over G micro-batches with an fp32 gradient shard,
  * global-norm clipping and a non-finite skip ("从 Data Parallel 到
