@@ -59,6 +59,14 @@
 #ifndef ZS_REDUCE_LDS_KB
 #define ZS_REDUCE_LDS_KB 8
 #endif
+// ... and from ZS_WIDE_N ranks on: 64 concurrent read streams per lane group
+// run fastest with only a few resident waves per CU.
+#ifndef ZS_REDUCE_WIDE_LDS_KB
+#define ZS_REDUCE_WIDE_LDS_KB 32
+#endif
+#ifndef ZS_WIDE_N
+#define ZS_WIDE_N 32
+#endif
 #ifndef ZS_ADAMW_LDS_KB
 #define ZS_ADAMW_LDS_KB 8
 #endif
@@ -109,6 +117,8 @@ constexpr int kAdamwU = ZS_ADAMW_U;
 constexpr int kFusedU = ZS_FUSED_U;
 constexpr unsigned kFusedLds = ZS_FUSED_LDS_KB * 1024u;
 constexpr unsigned kReduceLds = ZS_REDUCE_LDS_KB * 1024u;
+constexpr unsigned kReduceWideLds = ZS_REDUCE_WIDE_LDS_KB * 1024u;
+constexpr int kWideN = ZS_WIDE_N;
 constexpr unsigned kAdamwLds = ZS_ADAMW_LDS_KB * 1024u;
 constexpr unsigned kGatherLds = ZS_GATHER_LDS_KB * 1024u;
 constexpr unsigned kMultiLds = ZS_MULTI_LDS_KB * 1024u;
@@ -881,8 +891,9 @@ int launch_reduce_t(const void* const* contribs, int n, void* grad, int64_t len,
     Ptrs<CAP> cp{};
     for (int q = 0; q < n; ++q) cp.p[q] = contribs[q];
     const int64_t n8 = len / 8;
-    hipLaunchKernelGGL((k_reduce<N, CAP, kReduceU>), dim3(grid_for(n8, kReduceU)), dim3(kBlock), kReduceLds, s,
-                       cp, n, (float)n, reinterpret_cast<u32x4*>(grad), n8);
+    hipLaunchKernelGGL((k_reduce<N, CAP, kReduceU>), dim3(grid_for(n8, kReduceU)), dim3(kBlock),
+                       n >= kWideN ? kReduceWideLds : kReduceLds, s, cp, n, (float)n, reinterpret_cast<u32x4*>(grad),
+                       n8);
     return (int)hipGetLastError();
 }
 
