@@ -70,6 +70,8 @@ def parse():
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the CPU-offloaded optimizer step leg (FLAT workloads up to the 7B shape)")
     ap.add_argument("--offload-chunk", type=int, default=1 << 24, help="elements per offload pipeline chunk")
+    ap.add_argument("--no-separate", action="store_true",
+                    help="per-tensor workloads: skip the leg with one allocation per piece and array")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
     return ap.parse_args()
@@ -143,33 +145,51 @@ def flat_setup(zs, synth, wl, pad_kb=-1):
     return plan, st
 
 
-def per_tensor_setup(zs, synth, oracle, wl):
+def per_tensor_setup(zs, synth, oracle, wl, packed=True):
+    """PER_TENSOR pieces. packed: every piece's buffers are carved from one
+    allocation per array at the plan's shard offset (the gathered tensors from
+    one packed buffer at their flat offsets), contiguous as DeepSpeed's
+    contiguous_gradients keeps them; otherwise one allocation per piece and
+    array, as per-parameter tensors would be."""
     import torch
     plan = zs.zs_shard_plan(wl.numels, wl.world, wl.rank, 1, zs.ZS_LAYOUT_PER_TENSOR)
     op = oracle.plan_per_tensor(wl.numels, wl.world, wl.rank)
+    S = plan.shard_numel
+    if packed:
+        arena = {k: torch.empty(S, dtype=dt, device="cuda") for k, dt in
+                 (("grad", torch.int16), ("master", torch.float32), ("m", torch.float32), ("v", torch.float32),
+                  ("param", torch.int16))}
+        arena["m"].zero_()
+        arena["v"].zero_()
+        carena = [torch.empty(S, dtype=torch.int16, device="cuda") for _ in range(wl.world)]
+        full_arena = torch.empty(op.T, dtype=torch.int16, device="cuda")
     pieces, contribs = [], [[] for _ in range(wl.world)]
     for i, pc in enumerate(op.pieces):
         Si = pc.own_hi - pc.own_lo
         valid = op.offsets[i] + wl.numels[i]
-        d = dict(grad=torch.empty(Si, dtype=torch.int16, device="cuda"),
-                 master=torch.empty(Si, dtype=torch.float32, device="cuda"),
-                 m=torch.zeros(Si, dtype=torch.float32, device="cuda"),
-                 v=torch.zeros(Si, dtype=torch.float32, device="cuda"),
-                 param=torch.empty(Si, dtype=torch.int16, device="cuda"),
-                 full=torch.empty(op.padded[i], dtype=torch.int16, device="cuda"))
+        if packed:
+            lo = pc.shard_off
+            d = {k: arena[k][lo:lo + Si] for k in arena}
+            d["full"] = full_arena[op.offsets[i]:op.offsets[i] + op.padded[i]]
+        else:
+            d = dict(grad=torch.empty(Si, dtype=torch.int16, device="cuda"),
+                     master=torch.empty(Si, dtype=torch.float32, device="cuda"),
+                     m=torch.zeros(Si, dtype=torch.float32, device="cuda"),
+                     v=torch.zeros(Si, dtype=torch.float32, device="cuda"),
+                     param=torch.empty(Si, dtype=torch.int16, device="cuda"),
+                     full=torch.empty(op.padded[i], dtype=torch.int16, device="cuda"))
         synth.gpu_f32(d["master"], pc.full_off, wl.master_spec(valid))
         pieces.append(d)
         for q in range(wl.world):
-            c = torch.empty(Si, dtype=torch.int16, device="cuda")
+            c = carena[q][pc.shard_off:pc.shard_off + Si] if packed else torch.empty(Si, dtype=torch.int16,
+                                                                                      device="cuda")
             synth.gpu_bf16(c, pc.full_off, wl.contrib_spec(q, 1, valid))
             contribs[q].append(c)
     ws = torch.zeros(zs.zs_multi_workspace_bytes(plan, wl.world), dtype=torch.uint8, device="cuda")
     zs.zs_multi_bind(plan, pieces, contribs, ws)
-    nofull = [dict(pc, full=None, param=None, grad=None) for pc in pieces]
     ws_fused = torch.zeros_like(ws)
     zs.zs_multi_bind(plan, [dict(pc, param=None, grad=None) for pc in pieces], contribs, ws_fused)
     torch.cuda.synchronize()
-    del nofull
     return plan, dict(pieces=pieces, contribs=contribs, ws=ws, ws_fused=ws_fused)
 
 
@@ -456,6 +476,22 @@ def main():
                                              "events_ms_median": statistics.median(u_ev),
                                              "bytes_per_param": unfused_bytes_per_param(N),
                                              "launches_per_step": 3}
+        if not args.no_separate:
+            del st
+            torch.cuda.empty_cache()
+            plan2, st2 = per_tensor_setup(zs, synth, oracle, wl, packed=False)
+
+            def fused_sep(t, timer):
+                e = timer.start() if timer else None
+                zs.zs_fused_shard_step_multi(plan2, hp0.at(t), st2["ws_fused"])
+                if timer:
+                    timer.stop(e)
+
+            s_wall, s_dev, s_ev = time_loop(fused_sep, 1, max(3, args.steps // 2))
+            result_paths["fused_multi_separate_allocations"] = {
+                "ms_per_step": s_wall, "device_ms_per_step": s_dev, "events_ms_median": statistics.median(s_ev),
+                "bytes_per_param": bpp, "gbps": S * bpp / (s_dev / 1e3) / 1e9}
+            del st2
 
     params_per_s = S / (wall_ms / 1e3)
     achieved = S * bpp / (kern_ms / 1e3) / 1e9
@@ -482,7 +518,9 @@ def main():
         "data": "synthetic (seeded counter-based generator; model shapes only, no weights)",
         "config": {"workload": f"{wl.name}_n{N}_{main_path}", "world_size": N, "rank": wl.rank,
                    "layout": wl.layout, "shard_elems": S, "bytes_per_param": bpp,
-                   "gathered_buffer": "full" if wl.layout != "flat" or st.get("full_is_T") else "owned slice"},
+                   "gathered_buffer": "full" if wl.layout != "flat" or st.get("full_is_T") else "owned slice",
+                   **({"piece_buffers": "carved from one allocation per array at the plan's offsets"}
+                      if wl.layout != "flat" else {})},
         "hbm_gbps": step_gbps,
         "pct_of_peak": 100.0 * step_gbps / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -176,26 +176,34 @@ __device__ __forceinline__ u32x2 to_bf16x4(const f32x4& w) {
 
 // ------------------------------------------------------------------ memory helpers
 
+// Every access goes through a global-address-space pointer. Pointers read
+// from a device table (the multi-tensor pieces) are generic to the compiler,
+// which would emit flat memory instructions for them; flat loads count
+// against both wait counters and serialize the grouped loads. Every buffer
+// here is global memory.
 template <typename T>
-__device__ __forceinline__ T ld_nt(const T* p) { return __builtin_nontemporal_load(p); }
+using gptr = __attribute__((address_space(1))) T*;
+
 template <typename T>
-__device__ __forceinline__ void st_nt(T* p, T x) { __builtin_nontemporal_store(x, p); }
+__device__ __forceinline__ T ld_nt(const T* p) { return __builtin_nontemporal_load((gptr<const T>)p); }
+template <typename T>
+__device__ __forceinline__ void st_nt(T* p, T x) { __builtin_nontemporal_store(x, (gptr<T>)p); }
 
 template <typename T>
 __device__ __forceinline__ T ld_in(const T* p) {
-    if constexpr (ZS_NT_IN) return ld_nt(p); else return *p;
+    if constexpr (ZS_NT_IN) return ld_nt(p); else return *(gptr<const T>)p;
 }
 template <typename T>
 __device__ __forceinline__ T ld_state(const T* p) {
-    if constexpr (ZS_NT_STATE_LD) return ld_nt(p); else return *p;
+    if constexpr (ZS_NT_STATE_LD) return ld_nt(p); else return *(gptr<const T>)p;
 }
 template <typename T>
 __device__ __forceinline__ void st_state(T* p, T x) {
-    if constexpr (ZS_NT_STATE_ST) st_nt(p, x); else *p = x;
+    if constexpr (ZS_NT_STATE_ST) st_nt(p, x); else *(gptr<T>)p = x;
 }
 template <typename T>
 __device__ __forceinline__ void st_out(T* p, T x) {
-    if constexpr (ZS_NT_OUT) st_nt(p, x); else *p = x;
+    if constexpr (ZS_NT_OUT) st_nt(p, x); else *(gptr<T>)p = x;
 }
 
 template <int CAP>
