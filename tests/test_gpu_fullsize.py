@@ -274,3 +274,107 @@ def test_llama70b_shape_fused(zs):
     assert np.abs(oracle.bf16_to_f32(run.o_g)).max() > 3e-3
     del run, full
     _release()
+
+
+def _block_samples(S, B, n_blocks, seed):
+    """Element indices of whole quantization blocks: the first, the last (ragged
+    if S % B) and n_blocks random ones."""
+    rng = np.random.default_rng(seed)
+    nb = -(-S // B)
+    blocks = np.unique(np.concatenate([[0, nb - 1], rng.integers(0, nb, n_blocks)]))
+    return blocks, np.concatenate([np.arange(b * B, min((b + 1) * B, S)) for b in blocks]).astype(np.int64)
+
+
+@pytest.mark.parametrize("bits,block", [(4, 256), (8, 64)])
+def test_llama7b_shape_quantized_step_and_gather(zs, bits, block):
+    """Fused step writing codes at the 7B shard (N=8), then the dequantizing
+    gather of all ranks' payloads over the 6.7 G-element gathered buffer; whole
+    blocks sampled (codes and scales bit-exact, decoded values bit-exact)."""
+    import torch
+    wl = synth.workloads()["llama7b"]
+    if _free_gib() < 60:
+        pytest.skip("needs ~50 GiB of free device memory")
+    run = FlatBig(zs, wl, n_random=0)
+    S, T = run.S, run.T
+    blocks, idx = _block_samples(S, block, 400, 23)
+    run.idx, run.didx = idx, torch.from_numpy(idx).cuda()
+    gi = run.base + idx
+    run.o_master = synth.cpu_at_f32(gi, wl.master_spec(run.valid_hi))
+    K = idx.size
+    run.o_m, run.o_v = np.zeros(K, np.float32), np.zeros(K, np.float32)
+    run.o_g, run.o_p = np.zeros(K, np.uint16), np.zeros(K, np.uint16)
+    hp = _hp(zs, wl)
+    codes = torch.empty(zs.zs_quant_code_bytes(run.plan, bits), dtype=torch.uint8, device="cuda")
+    scales = torch.empty(zs.zs_quant_num_scales(run.plan, block), dtype=torch.float32, device="cuda")
+    for t in (1, 2):
+        run.gen_contribs(t)
+        zs.zs_fused_shard_step_quant(run.plan, hp.at(t), run.contribs, run.master, run.m, run.v, bits, block,
+                                     codes, scales)
+        run.oracle_step(t, hp)
+    torch.cuda.synchronize()
+    assert run.check_state("llama7b quant") == 0
+    # oracle codes of each sampled block, from the oracle's parameters of the block
+    o_codes, o_scales = [], []
+    pos = 0
+    for b in blocks:
+        n = min(block, S - b * block)
+        q, sc = oracle.quantize(run.o_p[pos:pos + n], bits, block)
+        o_codes.append(q)
+        o_scales.append(sc)
+        pos += n
+    g_scales = scales.index_select(0, torch.from_numpy(blocks).cuda()).cpu().numpy()
+    assert np.array_equal(g_scales.view(np.uint32), np.concatenate(o_scales).view(np.uint32))
+    byte_idx = np.concatenate([np.arange(b * block * bits // 8, (b * block + min(block, S - b * block)) * bits // 8)
+                               for b in blocks])
+    g_codes = codes.index_select(0, torch.from_numpy(byte_idx).cuda()).cpu().numpy()
+    assert np.array_equal(g_codes, np.concatenate(o_codes)), "code bytes differ"
+    # the gather: every rank's payload (copies of this rank's stand in for the others)
+    for c in run.contribs:
+        c.set_(torch.empty(0, dtype=torch.int16, device="cuda"))
+    _release()
+    full = torch.empty(T, dtype=torch.int16, device="cuda")
+    zs.zs_dequant_gather(run.plan, bits, block, codes.repeat(wl.world), scales.repeat(wl.world), full)
+    torch.cuda.synchronize()
+    o_dec = np.concatenate([oracle.dequantize(q, sc, min(block, S - b * block), bits, block)
+                            for q, sc, b in zip(o_codes, o_scales, blocks)])
+    for r in (0, 3, wl.world - 1):
+        got = full.index_select(0, torch.from_numpy(r * S + idx).cuda()).cpu().numpy().view(np.uint16)
+        assert check_bf16(got, o_dec, f"gathered rank {r} slice") == 0
+    del run, full, codes, scales
+    _release()
+
+
+def test_llama7b_shape_offloaded_step(zs):
+    """The CPU-offloaded step at the 7B shard: pinned host state, chunked
+    pipeline as the bench runs it; sampled host state and device parameters."""
+    import torch
+    wl = synth.workloads()["llama7b"]
+    if _free_gib() < 40:
+        pytest.skip("needs ~30 GiB of free device memory")
+    run = FlatBig(zs, wl, n_random=100_000)
+    S = run.S
+    hp = _hp(zs, wl)
+    hm = torch.empty(S, dtype=torch.float32, pin_memory=True)
+    hm.copy_(run.master.cpu())
+    hmm = torch.zeros(S, dtype=torch.float32, pin_memory=True)
+    hv = torch.zeros(S, dtype=torch.float32, pin_memory=True)
+    gh = torch.empty(S, dtype=torch.int16, pin_memory=True)
+    ph = torch.empty(S, dtype=torch.int16, pin_memory=True)
+    grad = torch.empty(S, dtype=torch.int16, device="cuda")
+    full = torch.full((run.T,), SENT, dtype=torch.int16, device="cuda")
+    for t in (1, 2):
+        run.gen_contribs(t)
+        zs.zs_reduce_shard(run.plan, run.contribs, grad)
+        zs.zs_offload_adamw_step(run.plan, hp.at(t), grad, hm, hmm, hv, gh, ph, full_dev=full,
+                                 chunk_elems=1 << 24, n_threads=16)
+        run.oracle_step(t, hp)
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(run.idx)
+    nd = check_f32(hm.index_select(0, idx).numpy(), run.o_master, "host master")
+    nd += check_f32(hmm.index_select(0, idx).numpy(), run.o_m, "host m")
+    nd += check_f32(hv.index_select(0, idx).numpy(), run.o_v, "host v")
+    nd += check_bf16(run.pick16(full), run.o_p, "gathered slice")
+    assert nd == 0
+    assert bool((full[S:S + 4096] == SENT).all())
+    del run, full, grad, hm, hmm, hv, gh, ph
+    _release()
