@@ -357,7 +357,41 @@ __device__ __forceinline__ void reduce4_tile(const void* const* cp, int n_rt, fl
 // codes 0, a non-finite element gives scale NaN and codes 0. A lane holds E
 // consecutive elements, so a block spans B / E consecutive lanes of the wave
 // and its amax is a butterfly max over them. Every lane of the wave must call
-// this (the shuffles), with ok == false where it holds no elements.
+// this (the cross-lane exchange), with ok == false where it holds no elements.
+
+// Butterfly over groups of `lanes` consecutive lanes (a power of two <= 64):
+// afterwards every lane of a group holds the group's largest amax and the OR
+// of its flags. Within a row of 16 lanes the exchange is DPP (quad
+// permutations, then the half-row and row mirrors); across rows it is
+// gfx950's permlane swaps; no LDS round trip. All 64 lanes must execute it.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ void group_max_or(float& amax, int& bad, int lanes) {
+    auto merge = [&](int o_amax, int o_bad) {
+        const float o = __int_as_float(o_amax);
+        amax = o > amax ? o : amax;
+        bad |= o_bad;
+    };
+    if (lanes > 1) merge(dpp_i<0xB1>(__float_as_int(amax)), dpp_i<0xB1>(bad));    // quad_perm [1,0,3,2]
+    if (lanes > 2) merge(dpp_i<0x4E>(__float_as_int(amax)), dpp_i<0x4E>(bad));    // quad_perm [2,3,0,1]
+    if (lanes > 4) merge(dpp_i<0x141>(__float_as_int(amax)), dpp_i<0x141>(bad));  // row_half_mirror
+    if (lanes > 8) merge(dpp_i<0x140>(__float_as_int(amax)), dpp_i<0x140>(bad));  // row_mirror
+    if (lanes > 16) {  // rows 0<->1, 2<->3: each lane sees its partner in one of the two results
+        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_int(amax), __float_as_int(amax), false, false);
+        const auto b = __builtin_amdgcn_permlane16_swap(bad, bad, false, false);
+        merge(a[0], b[0]);
+        merge(a[1], b[1]);
+    }
+    if (lanes > 32) {  // halves of the wave
+        const auto a = __builtin_amdgcn_permlane32_swap(__float_as_int(amax), __float_as_int(amax), false, false);
+        const auto b = __builtin_amdgcn_permlane32_swap(bad, bad, false, false);
+        merge(a[0], b[0]);
+        merge(a[1], b[1]);
+    }
+}
 
 // The codes of one lane (QB*E bits, low element first) and its block's scale.
 struct QuantWord {
@@ -382,11 +416,7 @@ __device__ __forceinline__ QuantWord quant_compute(const uint32_t* w, bool ok, i
             amax = a > amax ? a : amax;
         }
     }
-    for (int off = lanes >> 1; off > 0; off >>= 1) {
-        const float o = __shfl_xor(amax, off, 64);
-        amax = o > amax ? o : amax;
-        bad |= __shfl_xor(bad, off, 64);
-    }
+    group_max_or(amax, bad, lanes);
     QuantWord q;
     q.scale = bad ? __builtin_nanf("") : amax / qmax;
     const bool zero = bad || !(amax > 0.0f);
