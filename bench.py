@@ -292,9 +292,9 @@ def read_traffic(kernel_name, workload):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU's shard step; --gpus {args.gpus} is not supported "
-              f"(this build runs on a single GPU; see DESIGN.md for how the path shards).",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU's share of the step; --gpus {args.gpus} is not supported: "
+              f"every rank runs the same kernels on its own shard, so one GPU at its real shard shape is "
+              f"the measurement (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -91,6 +91,7 @@ def _load():
         "zs_fused_shard_step": (st, [vp, ctypes.POINTER(AdamWHParams), ctypes.POINTER(vp), i32, vp, vp,
                                      vp, vp, vp, vp, vp]),
         "zs_multi_workspace_bytes": (i64, [vp, i32]),
+        "zs_plan_workspace_bytes": (i64, [vp]),
         "zs_multi_bind": (st, [vp, ctypes.POINTER(PiecePtrs), ctypes.POINTER(vp), i32, vp, i64, vp]),
         "zs_reduce_shard_multi": (st, [vp, vp, vp]),
         "zs_adamw_shard_step_multi": (st, [vp, ctypes.POINTER(AdamWHParams), vp, vp]),
@@ -128,7 +129,8 @@ EXPORTED = ("zs_shard_plan", "zs_shard_plan_ex", "zs_plan_tensor_group", "zs_pla
             "zs_plan_destroy", "zs_plan_padded_numel", "zs_plan_shard_numel",
             "zs_plan_persistent_bytes", "zs_plan_num_tensors", "zs_plan_world_size", "zs_plan_rank",
             "zs_plan_layout", "zs_plan_tensor", "zs_reduce_shard", "zs_adamw_shard_step",
-            "zs_gather_params", "zs_fused_shard_step", "zs_multi_workspace_bytes", "zs_multi_bind",
+            "zs_gather_params", "zs_fused_shard_step", "zs_multi_workspace_bytes", "zs_plan_workspace_bytes",
+            "zs_multi_bind",
             "zs_reduce_shard_multi", "zs_adamw_shard_step_multi", "zs_gather_params_multi",
             "zs_fused_shard_step_multi", "zs_adamw_shard_step_multi_groups",
             "zs_fused_shard_step_multi_groups", "zs_quant_code_bytes", "zs_quant_num_scales", "zs_quantize_shard",
@@ -245,6 +247,10 @@ class Plan:
     @property
     def layout(self):
         return _lib.zs_plan_layout(self.handle)
+
+    @property
+    def workspace_bytes(self):
+        return _lib.zs_plan_workspace_bytes(self.handle)
 
     def tensor(self, i):
         info = TensorInfo()

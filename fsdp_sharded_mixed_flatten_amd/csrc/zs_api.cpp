@@ -589,6 +589,12 @@ zs_status lookup_binding(const zs_plan* plan, const void* ws, int32_t need, Bind
 
 }  // namespace
 
+int64_t zs_plan_workspace_bytes(const zs_plan* plan) {
+    if (!plan) return -1;
+    if (plan->layout != ZS_LAYOUT_PER_TENSOR) return 0;
+    return multi_layout(plan, plan->world).total;
+}
+
 int64_t zs_multi_workspace_bytes(const zs_plan* plan, int32_t n_contribs) {
     if (!plan || plan->layout != ZS_LAYOUT_PER_TENSOR || n_contribs < 0 || n_contribs > ZS_MAX_CONTRIBS) return -1;
     return multi_layout(plan, n_contribs).total;

@@ -236,6 +236,10 @@ typedef struct zs_piece_ptrs {
 } zs_piece_ptrs;
 
 int64_t zs_multi_workspace_bytes(const zs_plan* plan, int32_t n_contribs);
+/* The workspace a binding with the plan's world size of contributions needs:
+ * zs_multi_workspace_bytes(plan, world size) for PER_TENSOR plans, 0 for FLAT
+ * plans (their calls need none); -1 for a NULL plan. */
+int64_t zs_plan_workspace_bytes(const zs_plan* plan);
 
 /* pieces: host array of zs_plan_num_tensors(plan) records. contribs: host
  * array of n_contribs * num_tensors device pointers, contribs[q*n_tensors+i]

@@ -258,3 +258,10 @@ def test_quant_validation_without_device(zs):
     assert fq(h, ctypes.byref(bad), good, 4, FAKE, FAKE, FAKE, None, None, 8, 64, FAKE, FAKE, None) == zs.ZS_EINVAL
     empty = zs.zs_shard_plan([], 4, 0)
     assert L.zs_quantize_shard(empty.handle, 8, 64, FAKE, FAKE, FAKE, None) == zs.ZS_OK  # nothing to launch
+
+
+def test_plan_workspace_bytes(zs):
+    pt = zs.zs_shard_plan([4096, 512, 77], 8, 2, 1, zs.ZS_LAYOUT_PER_TENSOR)
+    assert pt.workspace_bytes == zs.zs_multi_workspace_bytes(pt, 8) > 0
+    assert zs.zs_shard_plan([4096], 8, 0).workspace_bytes == 0
+    assert zs.lib().zs_plan_workspace_bytes(None) == -1
