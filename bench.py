@@ -234,7 +234,14 @@ def cpu_baseline(oracle, synth, wl, S, window, fused_bpp):
     secs = oracle.time_shard_step(hp, contribs, g, master, m, v, p, full, threads, 4)
     med = statistics.median(secs[1:])
     secs1 = oracle.time_shard_step(hp, contribs, g, master, m, v, p, full, 1, 1)
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), cpu_model)
+    except OSError:
+        pass
     return {"value": n / med, "unit": "params/s", "cores": threads, "kind": "oracle",
+            "host_cpu": cpu_model, "host_logical_cpus": os.cpu_count(),
             "sample": f"{n:,}-element window of the {wl.name} shard (N={wl.world}), "
                       f"median of 3 timed passes after 1 warm-up, {threads} threads",
             "gbps_algorithmic": n * fused_bpp / med / 1e9,
