@@ -829,21 +829,40 @@ __global__ __launch_bounds__(kBlock) void k_stats(const f32x4* __restrict__ acc,
     }
 }
 
-// Stage 2 (one block): the partials in a fixed order.
-__global__ __launch_bounds__(kBlock) void k_stats_final(const double* __restrict__ part,
-                                                        const int32_t* __restrict__ flags, int64_t nb,
-                                                        double* __restrict__ sumsq_out,
-                                                        int32_t* __restrict__ nonfinite_out) {
+// Stage 2 (one block of kFinalThreads): thread i sums partials i, i + 1024,
+// ... in order, then a fixed tree within each wave and the wave sums in
+// order: a fixed partition, so reruns give identical bits.
+constexpr int kFinalThreads = 1024;
+
+__global__ __launch_bounds__(kFinalThreads) void k_stats_final(const double* __restrict__ part,
+                                                               const int32_t* __restrict__ flags, int64_t nb,
+                                                               double* __restrict__ sumsq_out,
+                                                               int32_t* __restrict__ nonfinite_out) {
     double s = 0.0;
     int bad = 0;
-    for (int64_t i = threadIdx.x; i < nb; i += kBlock) {
+    for (int64_t i = threadIdx.x; i < nb; i += kFinalThreads) {
         s = s + part[i];
         bad |= flags[i];
     }
-    block_reduce(s, bad);
+    s = wave_sum(s);
+    bad = wave_or(bad);
+    __shared__ double ws[kFinalThreads / 64];
+    __shared__ int wb[kFinalThreads / 64];
+    const int w = threadIdx.x / 64;
+    if ((threadIdx.x & 63) == 0) {
+        ws[w] = s;
+        wb[w] = bad;
+    }
+    __syncthreads();
     if (threadIdx.x == 0) {
-        *sumsq_out = s;
-        *nonfinite_out = bad ? 1 : 0;
+        double t = 0.0;
+        int b = 0;
+        for (int i = 0; i < kFinalThreads / 64; ++i) {
+            t += ws[i];
+            b |= wb[i];
+        }
+        *sumsq_out = t;
+        *nonfinite_out = b ? 1 : 0;
     }
 }
 
@@ -1129,7 +1148,7 @@ int launch_grad_stats(const float* acc, float divisor, double* sumsq_out, int32_
     if (nb > 0)
         hipLaunchKernelGGL(k_stats, dim3((unsigned)nb), dim3(kBlock), 0, s, reinterpret_cast<const f32x4*>(acc),
                            divisor, len / 4, part, flags);
-    hipLaunchKernelGGL(k_stats_final, dim3(1), dim3(kBlock), 0, s, part, flags, nb, sumsq_out, nonfinite_out);
+    hipLaunchKernelGGL(k_stats_final, dim3(1), dim3(kFinalThreads), 0, s, part, flags, nb, sumsq_out, nonfinite_out);
     return (int)hipGetLastError();
 }
 
