@@ -189,6 +189,10 @@ __device__ __forceinline__ T ld_nt(const T* p) { return __builtin_nontemporal_lo
 template <typename T>
 __device__ __forceinline__ void st_nt(T* p, T x) { __builtin_nontemporal_store(x, (gptr<T>)p); }
 
+// Plain (cached) global load, for table records.
+template <typename T>
+__device__ __forceinline__ T ld_g(const T* p) { return *(gptr<const T>)p; }
+
 template <typename T>
 __device__ __forceinline__ T ld_in(const T* p) {
     if constexpr (ZS_NT_IN) return ld_nt(p); else return *(gptr<const T>)p;
@@ -329,24 +333,6 @@ __device__ __forceinline__ void reduce8_tile(const void* const* cp, int n_rt, fl
         o.w = pack2(div_n<N>(a[k][6], nf), div_n<N>(a[k][7], nf));
         st_out(out + u[k], o);
     }
-}
-
-// reduce in units of 4 elements
-template <int N, int U>
-__device__ __forceinline__ void reduce4_tile(const void* const* cp, int n_rt, float nf, u32x2* __restrict__ out,
-                                             int64_t base, int64_t limit) {
-    int64_t u[U];
-    bool ok[U];
-#pragma unroll
-    for (int k = 0; k < U; ++k) {
-        u[k] = base + (int64_t)k * kBlock;
-        ok[k] = u[k] < limit;
-    }
-    float a[U][4];
-    rank_sum<u32x2, U, N>(cp, n_rt, u, ok, a);
-#pragma unroll
-    for (int k = 0; k < U; ++k)
-        if (ok[k]) st_out(out + u[k], avg_bf16x4<N>(a[k], nf));
 }
 
 // ------------------------------------------------------------------ block quantization
@@ -694,12 +680,14 @@ __global__ __launch_bounds__(kBlock) void k_dequant(const char* __restrict__ cod
 
 // ------------------------------------------------------------------ multi-tensor kernel
 
-// One block per chunk; a chunk is one tile (kBlock lanes x kMultiU units of
-// 4 elements) of one piece. The piece supplies every pointer; the
+// AdamW and the fused step over the pieces: one block per chunk; a chunk is
+// one tile (kBlock lanes x kMultiU units of 4 elements) of one piece. The
+// piece supplies every pointer and its hyperparameter group; the
 // contributions of piece i are cps[i * N .. i * N + N).
 template <int OP, int N>
 __global__ __launch_bounds__(kBlock) void k_multi(CoefTable ct, const MultiHeader* __restrict__ hdr,
                                                   int n_rt, float nf) {
+    static_assert(OP == kOpAdamw || OP == kOpFused, "reduce and gather have kernels of their own");
     const char* ws = reinterpret_cast<const char*>(hdr);
     const Chunk ch = reinterpret_cast<const Chunk*>(ws + hdr->chunks_off)[blockIdx.x];
     const PieceDev pc = reinterpret_cast<const PieceDev*>(ws + hdr->pieces_off)[ch.piece];
@@ -708,24 +696,120 @@ __global__ __launch_bounds__(kBlock) void k_multi(CoefTable ct, const MultiHeade
     const int64_t u0 = ch.start >> 2;  // chunk start and length are multiples of 8
     const int64_t base = u0 + threadIdx.x;
     const int64_t limit = u0 + (ch.len >> 2);
-    if constexpr (OP == kOpGather) {
-        copy_tile<u32x2, kMultiU>(reinterpret_cast<const u32x2*>(pc.param), reinterpret_cast<u32x2*>(pc.full_own),
-                                  base, limit);
-    } else if constexpr (OP == kOpAdamw) {
+    if constexpr (OP == kOpAdamw) {
         adamw_tile<kMultiU>(c, reinterpret_cast<const u32x2*>(pc.grad), reinterpret_cast<f32x4*>(pc.master),
                             reinterpret_cast<f32x4*>(pc.m), reinterpret_cast<f32x4*>(pc.v),
                             (flags & kHasParam) ? reinterpret_cast<u32x2*>(pc.param) : nullptr, nullptr, base, limit);
     } else {
         const void* const* cps =
             reinterpret_cast<const void* const*>(ws + hdr->contribs_off) + (int64_t)ch.piece * (N > 0 ? N : n_rt);
-        if constexpr (OP == kOpReduce) {
-            reduce4_tile<N, kMultiU>(cps, n_rt, nf, reinterpret_cast<u32x2*>(pc.grad), base, limit);
-        } else {
-            fused_tile<N, kMultiU>(c, cps, n_rt, nf, reinterpret_cast<f32x4*>(pc.master), reinterpret_cast<f32x4*>(pc.m),
-                                   reinterpret_cast<f32x4*>(pc.v),
-                                   (flags & kHasGrad) ? reinterpret_cast<u32x2*>(pc.grad) : nullptr,
-                                   (flags & kHasParam) ? reinterpret_cast<u32x2*>(pc.param) : nullptr,
-                                   (flags & kHasFull) ? reinterpret_cast<u32x2*>(pc.full_own) : nullptr, base, limit);
+        fused_tile<N, kMultiU>(c, cps, n_rt, nf, reinterpret_cast<f32x4*>(pc.master), reinterpret_cast<f32x4*>(pc.m),
+                               reinterpret_cast<f32x4*>(pc.v),
+                               (flags & kHasGrad) ? reinterpret_cast<u32x2*>(pc.grad) : nullptr,
+                               (flags & kHasParam) ? reinterpret_cast<u32x2*>(pc.param) : nullptr,
+                               (flags & kHasFull) ? reinterpret_cast<u32x2*>(pc.full_own) : nullptr, base, limit);
+    }
+}
+
+// Multi-tensor gather (bf16 copy, no arithmetic): one chunk per block would
+// move only 1 KiB after its table lookups, so a block covers kGatherRows rows
+// of chunks with 8 elements (one 16-byte access) per lane; each lane looks up
+// its own chunk and piece, all rows' lookups and loads are issued before any
+// store.
+constexpr int kGatherLanesPerChunk = kChunkElems / 8;
+constexpr int kGatherChunksPerRow = kBlock / kGatherLanesPerChunk;
+constexpr int kGatherRows = 4;
+constexpr int kGatherChunksPerBlock = kGatherChunksPerRow * kGatherRows;
+static_assert(kChunkElems % 8 == 0 && kBlock % kGatherLanesPerChunk == 0, "gather lanes must tile the wave");
+
+__global__ __launch_bounds__(kBlock) void k_multi_gather(const MultiHeader* __restrict__ hdr, int n_chunks) {
+    const char* ws = reinterpret_cast<const char*>(hdr);
+    const Chunk* chunks = reinterpret_cast<const Chunk*>(ws + hdr->chunks_off);
+    const PieceDev* pieces = reinterpret_cast<const PieceDev*>(ws + hdr->pieces_off);
+    const int lane = threadIdx.x;
+    const int64_t first = (int64_t)blockIdx.x * kGatherChunksPerBlock + lane / kGatherLanesPerChunk;
+    const int off = (lane % kGatherLanesPerChunk) * 8;
+    // phase 1: every row's chunk record (rows past the end read chunk 0 and are dropped)
+    int32_t piece[kGatherRows], len[kGatherRows];
+    int64_t start[kGatherRows];
+#pragma unroll
+    for (int r = 0; r < kGatherRows; ++r) {
+        const int64_t c = first + (int64_t)r * kGatherChunksPerRow;
+        const Chunk* ch = chunks + (c < n_chunks ? c : 0);
+        piece[r] = ld_g(&ch->piece);
+        len[r] = c < n_chunks ? ld_g(&ch->len) : 0;
+        start[r] = ld_g(&ch->start);
+    }
+    // phase 2: the pieces' pointers. A lane past its chunk's end reads the
+    // chunk's first vector instead (always inside the piece) and stores nothing,
+    // so the loads below need no branch.
+    const char* src[kGatherRows];
+    char* dst[kGatherRows];
+#pragma unroll
+    for (int r = 0; r < kGatherRows; ++r) {
+        const PieceDev* pc = pieces + piece[r];
+        const int o = off < len[r] ? off : 0;
+        src[r] = static_cast<const char*>(ld_g(&pc->param)) + 2 * (start[r] + o);
+        dst[r] = static_cast<char*>(ld_g(&pc->full_own)) + 2 * (start[r] + off);
+    }
+    // phase 3: loads, then stores
+    u32x4 x[kGatherRows];
+#pragma unroll
+    for (int r = 0; r < kGatherRows; ++r) x[r] = ld_in(reinterpret_cast<const u32x4*>(src[r]));
+#pragma unroll
+    for (int r = 0; r < kGatherRows; ++r)
+        if (off < len[r]) st_out(reinterpret_cast<u32x4*>(dst[r]), x[r]);
+}
+
+// Multi-tensor reduce in the same shape: 8 elements (16-byte loads) per lane,
+// two chunks per row of the wave, kReduceRows rows per block; the rows' table
+// lookups are batched, then each row sums its N contributions in rank order.
+#ifndef ZS_MULTI_REDUCE_ROWS
+#define ZS_MULTI_REDUCE_ROWS 2
+#endif
+constexpr int kReduceRows = ZS_MULTI_REDUCE_ROWS;
+constexpr int kReduceChunksPerBlock = kGatherChunksPerRow * kReduceRows;
+
+template <int N>
+__global__ __launch_bounds__(kBlock) void k_multi_reduce(const MultiHeader* __restrict__ hdr, int n_chunks,
+                                                         int n_rt, float nf) {
+    const char* ws = reinterpret_cast<const char*>(hdr);
+    const Chunk* chunks = reinterpret_cast<const Chunk*>(ws + hdr->chunks_off);
+    const PieceDev* pieces = reinterpret_cast<const PieceDev*>(ws + hdr->pieces_off);
+    const void* const* cps = reinterpret_cast<const void* const*>(ws + hdr->contribs_off);
+    const int nq = N > 0 ? N : n_rt;
+    const int lane = threadIdx.x;
+    const int64_t first = (int64_t)blockIdx.x * kReduceChunksPerBlock + lane / kGatherLanesPerChunk;
+    const int off = (lane % kGatherLanesPerChunk) * 8;
+    int32_t piece[kReduceRows], len[kReduceRows];
+    int64_t start[kReduceRows];
+#pragma unroll
+    for (int r = 0; r < kReduceRows; ++r) {
+        const int64_t c = first + (int64_t)r * kGatherChunksPerRow;
+        const Chunk* ch = chunks + (c < n_chunks ? c : 0);
+        piece[r] = ld_g(&ch->piece);
+        len[r] = c < n_chunks ? ld_g(&ch->len) : 0;
+        start[r] = ld_g(&ch->start);
+    }
+    char* grad[kReduceRows];
+#pragma unroll
+    for (int r = 0; r < kReduceRows; ++r) grad[r] = static_cast<char*>(ld_g(&pieces[piece[r]].grad));
+#pragma unroll
+    for (int r = 0; r < kReduceRows; ++r) {
+        // a lane past its chunk's end sums the chunk's first vector (inside the
+        // piece) and stores nothing
+        const bool ok = off < len[r];
+        const int64_t u = (start[r] + (ok ? off : 0)) / 8;
+        const bool t = true;
+        float a[1][8];
+        rank_sum<u32x4, 1, N>(cps + (int64_t)piece[r] * nq, n_rt, &u, &t, a);
+        if (ok) {
+            u32x4 o;
+            o.x = pack2(div_n<N>(a[0][0], nf), div_n<N>(a[0][1], nf));
+            o.y = pack2(div_n<N>(a[0][2], nf), div_n<N>(a[0][3], nf));
+            o.z = pack2(div_n<N>(a[0][4], nf), div_n<N>(a[0][5], nf));
+            o.w = pack2(div_n<N>(a[0][6], nf), div_n<N>(a[0][7], nf));
+            st_out(reinterpret_cast<u32x4*>(grad[r]) + u, o);
         }
     }
 }
@@ -982,6 +1066,27 @@ int launch_multi_t(const CoefTable& c, const void* ws, int n_chunks, int n, hipS
     return (int)hipGetLastError();
 }
 
+template <int N>
+int launch_multi_reduce_t(const void* ws, int n_chunks, int n, hipStream_t s) {
+    hipLaunchKernelGGL((k_multi_reduce<N>),
+                       dim3((unsigned)((n_chunks + kReduceChunksPerBlock - 1) / kReduceChunksPerBlock)), dim3(kBlock),
+                       kMultiLds, s, reinterpret_cast<const MultiHeader*>(ws), n_chunks, n, (float)n);
+    return (int)hipGetLastError();
+}
+
+int launch_multi_reduce(const void* ws, int n_chunks, int n, hipStream_t s) {
+    switch (n) {
+        case 1: return launch_multi_reduce_t<1>(ws, n_chunks, n, s);
+        case 2: return launch_multi_reduce_t<2>(ws, n_chunks, n, s);
+        case 4: return launch_multi_reduce_t<4>(ws, n_chunks, n, s);
+        case 8: return launch_multi_reduce_t<8>(ws, n_chunks, n, s);
+        case 16: return launch_multi_reduce_t<16>(ws, n_chunks, n, s);
+        case 32: return launch_multi_reduce_t<32>(ws, n_chunks, n, s);
+        case 64: return launch_multi_reduce_t<64>(ws, n_chunks, n, s);
+        default: return launch_multi_reduce_t<0>(ws, n_chunks, n, s);
+    }
+}
+
 template <int OP>
 int launch_multi_op(const CoefTable& c, const void* ws, int n_chunks, int n, hipStream_t s) {
     switch (n) {
@@ -1116,9 +1221,13 @@ int launch_multi(int op, const CoefTable* c, const void* workspace, int n_chunks
     const CoefTable cc = c ? *c : CoefTable{};
     hipStream_t s = (hipStream_t)stream;
     switch (op) {
-        case kOpReduce: return launch_multi_op<kOpReduce>(cc, workspace, n_chunks, n_contribs, s);
+        case kOpReduce: return launch_multi_reduce(workspace, n_chunks, n_contribs, s);
         case kOpAdamw: return launch_multi_t<kOpAdamw, 1>(cc, workspace, n_chunks, 1, s);
-        case kOpGather: return launch_multi_t<kOpGather, 1>(cc, workspace, n_chunks, 1, s);
+        case kOpGather:
+            hipLaunchKernelGGL(k_multi_gather, dim3((unsigned)((n_chunks + kGatherChunksPerBlock - 1) /
+                                                               kGatherChunksPerBlock)),
+                               dim3(kBlock), kMultiLds, s, reinterpret_cast<const MultiHeader*>(workspace), n_chunks);
+            return (int)hipGetLastError();
         default: return launch_multi_op<kOpFused>(cc, workspace, n_chunks, n_contribs, s);
     }
 }
