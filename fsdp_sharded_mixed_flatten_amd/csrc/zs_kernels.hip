@@ -56,6 +56,11 @@
 #ifndef ZS_FUSED_LDS_KB
 #define ZS_FUSED_LDS_KB 16
 #endif
+// ... for the fused kernel at 4 or fewer ranks, whose lighter reads leave
+// room for more resident waves.
+#ifndef ZS_FUSED_NARROW_LDS_KB
+#define ZS_FUSED_NARROW_LDS_KB 12
+#endif
 #ifndef ZS_REDUCE_LDS_KB
 #define ZS_REDUCE_LDS_KB 8
 #endif
@@ -116,6 +121,7 @@ constexpr int kReduceU = ZS_REDUCE_U;
 constexpr int kAdamwU = ZS_ADAMW_U;
 constexpr int kFusedU = ZS_FUSED_U;
 constexpr unsigned kFusedLds = ZS_FUSED_LDS_KB * 1024u;
+constexpr unsigned kFusedNarrowLds = ZS_FUSED_NARROW_LDS_KB * 1024u;
 constexpr unsigned kReduceLds = ZS_REDUCE_LDS_KB * 1024u;
 constexpr unsigned kReduceWideLds = ZS_REDUCE_WIDE_LDS_KB * 1024u;
 constexpr int kWideN = ZS_WIDE_N;
@@ -1044,7 +1050,8 @@ int launch_fused_q(const AdamCoef& c, const void* const* contribs, int n, float*
     Ptrs<CAP> cp{};
     for (int q = 0; q < n; ++q) cp.p[q] = contribs[q];
     const int64_t n4 = len / 4;
-    hipLaunchKernelGGL((k_fused<N, CAP, kFusedU, QB>), dim3(grid_for(n4, kFusedU)), dim3(kBlock), kFusedLds, s, c,
+    hipLaunchKernelGGL((k_fused<N, CAP, kFusedU, QB>), dim3(grid_for(n4, kFusedU)), dim3(kBlock),
+                       n <= 4 ? kFusedNarrowLds : kFusedLds, s, c,
                        cp, n, (float)n, reinterpret_cast<f32x4*>(master), reinterpret_cast<f32x4*>(m),
                        reinterpret_cast<f32x4*>(v), reinterpret_cast<u32x2*>(grad),
                        reinterpret_cast<u32x2*>(param), reinterpret_cast<u32x2*>(full), n4, qo);
