@@ -93,6 +93,7 @@ def _load():
         "zs_multi_workspace_bytes": (i64, [vp, i32]),
         "zs_plan_workspace_bytes": (i64, [vp]),
         "zs_multi_bind": (st, [vp, ctypes.POINTER(PiecePtrs), ctypes.POINTER(vp), i32, vp, i64, vp]),
+        "zs_multi_unbind": (st, [vp, vp]),
         "zs_reduce_shard_multi": (st, [vp, vp, vp]),
         "zs_adamw_shard_step_multi": (st, [vp, ctypes.POINTER(AdamWHParams), vp, vp]),
         "zs_gather_params_multi": (st, [vp, vp, vp]),
@@ -130,7 +131,7 @@ EXPORTED = ("zs_shard_plan", "zs_shard_plan_ex", "zs_plan_tensor_group", "zs_pla
             "zs_plan_persistent_bytes", "zs_plan_num_tensors", "zs_plan_world_size", "zs_plan_rank",
             "zs_plan_layout", "zs_plan_tensor", "zs_reduce_shard", "zs_adamw_shard_step",
             "zs_gather_params", "zs_fused_shard_step", "zs_multi_workspace_bytes", "zs_plan_workspace_bytes",
-            "zs_multi_bind",
+            "zs_multi_bind", "zs_multi_unbind",
             "zs_reduce_shard_multi", "zs_adamw_shard_step_multi", "zs_gather_params_multi",
             "zs_fused_shard_step_multi", "zs_adamw_shard_step_multi_groups",
             "zs_fused_shard_step_multi_groups", "zs_quant_code_bytes", "zs_quant_num_scales", "zs_quantize_shard",
@@ -463,6 +464,10 @@ def zs_multi_bind(plan, pieces, contribs, workspace, stream=None):
     _check(_lib.zs_multi_bind(plan.handle, recs, _ptr_array(flat) if nq else None, nq,
                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                               _stream(stream)))
+
+
+def zs_multi_unbind(workspace, stream=None):
+    _check(_lib.zs_multi_unbind(workspace.data_ptr(), _stream(stream)))
 
 
 def zs_reduce_shard_multi(plan, workspace, stream=None):

@@ -687,6 +687,16 @@ zs_status zs_multi_bind(const zs_plan* plan, const zs_piece_ptrs* pieces, const 
     return ZS_OK;
 }
 
+zs_status zs_multi_unbind(void* workspace, void* stream) {
+    if (!workspace) return fail(ZS_EINVAL, "workspace is NULL");
+    {
+        std::lock_guard<std::mutex> lk(g_bind_mu);
+        if (g_bind.erase(workspace) == 0) return fail(ZS_EINVAL, "workspace %p is not bound", workspace);
+    }
+    const uint64_t zero = 0;  // clear the table's magic: later launches on it do nothing
+    return hip_status(zs::copy_h2d_sync(workspace, &zero, sizeof zero, stream), "workspace clear");
+}
+
 zs_status zs_reduce_shard_multi(const zs_plan* plan, const void* workspace, void* stream) {
     if (zs_status st = check_multi_plan(plan)) return st;
     Binding b;

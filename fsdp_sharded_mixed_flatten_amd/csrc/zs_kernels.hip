@@ -694,6 +694,7 @@ template <int OP, int N>
 __global__ __launch_bounds__(kBlock) void k_multi(CoefTable ct, const MultiHeader* __restrict__ hdr,
                                                   int n_rt, float nf) {
     static_assert(OP == kOpAdamw || OP == kOpFused, "reduce and gather have kernels of their own");
+    if (hdr->magic != kMultiMagic) return;  // not a bound table (e.g. reused memory): touch nothing
     const char* ws = reinterpret_cast<const char*>(hdr);
     const Chunk ch = reinterpret_cast<const Chunk*>(ws + hdr->chunks_off)[blockIdx.x];
     const PieceDev pc = reinterpret_cast<const PieceDev*>(ws + hdr->pieces_off)[ch.piece];
@@ -729,6 +730,7 @@ constexpr int kGatherChunksPerBlock = kGatherChunksPerRow * kGatherRows;
 static_assert(kChunkElems % 8 == 0 && kBlock % kGatherLanesPerChunk == 0, "gather lanes must tile the wave");
 
 __global__ __launch_bounds__(kBlock) void k_multi_gather(const MultiHeader* __restrict__ hdr, int n_chunks) {
+    if (hdr->magic != kMultiMagic) return;
     const char* ws = reinterpret_cast<const char*>(hdr);
     const Chunk* chunks = reinterpret_cast<const Chunk*>(ws + hdr->chunks_off);
     const PieceDev* pieces = reinterpret_cast<const PieceDev*>(ws + hdr->pieces_off);
@@ -779,6 +781,7 @@ constexpr int kReduceChunksPerBlock = kGatherChunksPerRow * kReduceRows;
 template <int N>
 __global__ __launch_bounds__(kBlock) void k_multi_reduce(const MultiHeader* __restrict__ hdr, int n_chunks,
                                                          int n_rt, float nf) {
+    if (hdr->magic != kMultiMagic) return;
     const char* ws = reinterpret_cast<const char*>(hdr);
     const Chunk* chunks = reinterpret_cast<const Chunk*>(ws + hdr->chunks_off);
     const PieceDev* pieces = reinterpret_cast<const PieceDev*>(ws + hdr->pieces_off);

@@ -249,6 +249,12 @@ int64_t zs_plan_workspace_bytes(const zs_plan* plan);
 zs_status zs_multi_bind(const zs_plan* plan, const zs_piece_ptrs* pieces, const void* const* contribs,
                         int32_t n_contribs, void* workspace, int64_t workspace_bytes, void* stream);
 
+/* Forgets a binding and clears the table's tag in the workspace (one 8-byte
+ * copy on `stream`, then a synchronization), so the memory can be reused.
+ * The kernels check that tag and do nothing on a workspace that holds no
+ * bound table. */
+zs_status zs_multi_unbind(void* workspace, void* stream);
+
 zs_status zs_reduce_shard_multi(const zs_plan* plan, const void* workspace, void* stream);
 zs_status zs_adamw_shard_step_multi(const zs_plan* plan, const zs_adamw_hparams* hp,
                                     const void* workspace, void* stream);

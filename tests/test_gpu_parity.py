@@ -382,6 +382,28 @@ def test_multi_tensor_apply(zs, fused):
         run.check()
 
 
+def test_multi_tensor_unbound_workspace_is_inert(zs):
+    """A workspace whose table was unbound, or whose memory was overwritten
+    after binding, launches nothing that touches the pieces."""
+    import torch
+    run = MultiRun(zs, _small_model(H=128, I=344, V=300, L=1), 4, 1, 1, 81, _hp(zs))
+    before = [{k: v.clone() for k, v in d.items()} for d in run.pieces]
+    ws = run.ws[1]
+    ws.zero_()  # the host still records the binding; the table's tag is gone
+    zs.zs_fused_shard_step_multi(run.plan, _hp(zs), ws)
+    zs.zs_reduce_shard_multi(run.plan, ws)
+    zs.zs_gather_params_multi(run.plan, ws)
+    torch.cuda.synchronize()
+    for d, b in zip(run.pieces, before):
+        for k in d:
+            assert torch.equal(d[k], b[k]), k
+    zs.zs_multi_unbind(ws)
+    with pytest.raises(zs.ZsError):
+        zs.zs_fused_shard_step_multi(run.plan, _hp(zs), ws)
+    with pytest.raises(zs.ZsError):
+        zs.zs_multi_unbind(ws)
+
+
 def test_multi_tensor_runtime_world(zs):
     run = MultiRun(zs, _small_model(H=128, I=344, V=300, L=1), 5, 4, 1, 78, _hp(zs))
     run.step(1, True)
