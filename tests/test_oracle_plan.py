@@ -146,3 +146,48 @@ def test_brute_force_coverage(seed):
                     cover[key] = r
         assert len(Ss) == 1
         assert len(cover) == sum(numels)
+
+
+def _units(sizes, per_block, n_layers=32, per_layer=9):
+    """FSDP units of the Llama-7B tensor list under a wrap policy ("FSDP2's
+    parameter lifecycle...", section "Wrap granularity is the lever"): per
+    block, every block is one unit and the root unit keeps the embedding,
+    final norm and head; per linear, every linear sublayer is a unit of its
+    own and each block's two norms stay in the block's unit."""
+    emb, layers, tail = sizes[:1], sizes[1:1 + n_layers * per_layer], sizes[1 + n_layers * per_layer:]
+    units = []
+    for b in range(n_layers):
+        blk = layers[b * per_layer:(b + 1) * per_layer]
+        if per_block:
+            units.append(blk)
+        else:
+            units += [[n] for n in blk[:7]] + [blk[7:]]
+    units.append(emb + tail)
+    return units
+
+
+def test_wrap_units_and_ledger():
+    """Per-block wrapping: 33 units (32 blocks + root), one all-gather each per
+    block; per-linear wrapping: 7 units per block (the page's example counts 6
+    linear sublayers and so a ratio of 6; Llama's gated MLP has 7). Each unit
+    is one FLAT plan, and the units' ledgers add up to 16 bytes per element
+    of all units' padded buffers."""
+    sizes = shapes.llama_7b()
+    blocks = _units(sizes, per_block=True)
+    linears = _units(sizes, per_block=False)
+    assert len(blocks) == 33
+    per_block_linear_units = (len(linears) - 1) // 32
+    assert per_block_linear_units == 8  # 7 linear units + the block's norm unit
+    assert per_block_linear_units - 1 == 7
+    for units in (blocks, linears):
+        assert sorted(n for u in units for n in u) == sorted(sizes)
+        total_T, total_bytes = 0, 0
+        for u in units:
+            ranks = [plan_flat(u, 8, r, 1) for r in range(8)]
+            total_T += ranks[0].T
+            total_bytes += sum(p.persistent_bytes for p in ranks)
+            assert ranks[0].T - sum(u) < 8 * 8  # padding below one granule per unit
+        assert total_bytes == 16 * total_T
+    # every block's unit holds the same 202,383,360 parameters; per block the
+    # per-linear policy issues 7 gathers where the per-block policy issues 1
+    assert {sum(u) for u in blocks[:32]} == {4 * 4096 * 4096 + 3 * 11008 * 4096 + 2 * 4096}
