@@ -55,7 +55,7 @@ def parse():
                     choices=["tiny", "qwen3b", "llama7b", "llama7b_wrap", "llama70b"])
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused path's timing")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-window", type=int, default=25_000_000,
+    ap.add_argument("--cpu-window", type=int, default=100_000_000,
                     help="owned elements of the CPU oracle's timed window")
     ap.add_argument("--arena-pad-kb", type=int, default=-1,
                     help="allocate the N contributions (and master/m/v) as rows of one buffer whose "
@@ -231,9 +231,10 @@ def cpu_baseline(oracle, synth, wl, S, window, fused_bpp):
     full = np.zeros(n, np.uint16)  # the window's slice of the gathered buffer (rank 0: offset 0)
     threads = max(1, min(16, os.cpu_count() or 1))
     hp = oracle.HParams(wl.lr, wl.beta1, wl.beta2, wl.eps, wl.weight_decay, 1)
-    secs = oracle.time_shard_step(hp, contribs, g, master, m, v, p, full, threads, 4)
+    secs = oracle.time_shard_step(hp, contribs, g, master, m, v, p, full, threads, 6)
     med = statistics.median(secs[1:])
     secs1 = oracle.time_shard_step(hp, contribs, g, master, m, v, p, full, 1, 1)
+    cpu_seconds = threads * sum(secs) + secs1[0]
     cpu_model = "unknown"
     try:
         with open("/proc/cpuinfo") as fh:
@@ -243,7 +244,9 @@ def cpu_baseline(oracle, synth, wl, S, window, fused_bpp):
     return {"value": n / med, "unit": "params/s", "cores": threads, "kind": "oracle",
             "host_cpu": cpu_model, "host_logical_cpus": os.cpu_count(),
             "sample": f"{n:,}-element window of the {wl.name} shard (N={wl.world}), "
-                      f"median of 3 timed passes after 1 warm-up, {threads} threads",
+                      f"median of 5 timed passes after 1 warm-up, {threads} threads, plus one "
+                      f"single-thread pass; {cpu_seconds:.1f} core-seconds of oracle work",
+            "core_seconds": cpu_seconds,
             "gbps_algorithmic": n * fused_bpp / med / 1e9,
             "single_thread_params_per_s": n / secs1[0]}
 
