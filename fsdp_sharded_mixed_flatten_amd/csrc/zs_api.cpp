@@ -28,6 +28,9 @@ zs_status fail(zs_status st, const char* fmt, ...) {
 }
 
 constexpr int64_t kMaxElems = int64_t(1) << 60;
+// Largest owned shard: 2^38 elements (512 GiB of bf16, beyond any one GPU's
+// memory) keeps every launch grid within 32-bit block counts.
+constexpr int64_t kMaxShardElems = int64_t(1) << 38;
 
 int64_t roundup(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
@@ -213,6 +216,11 @@ zs_status zs_shard_plan_ex(const int64_t* numels, int32_t n_tensors, int32_t wor
     } catch (const std::bad_alloc&) {
         delete p;
         return fail(ZS_ENOMEM, "out of host memory");
+    }
+    if (p->S > kMaxShardElems) {
+        const long long S = (long long)p->S;
+        delete p;
+        return fail(ZS_EINVAL, "owned shard of %lld elements exceeds 2^38", S);
     }
     *out = p;
     return ZS_OK;

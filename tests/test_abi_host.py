@@ -156,6 +156,13 @@ def test_plan_rejects_bad_arguments(zs):
         assert e.value.status == zs.ZS_EINVAL and e.value.message
 
 
+def test_plan_rejects_shards_beyond_any_device(zs):
+    with pytest.raises(zs.ZsError) as e:
+        zs.zs_shard_plan([1 << 40], 2, 0)
+    assert e.value.status == zs.ZS_EINVAL and "2^38" in e.value.message
+    assert zs.zs_shard_plan([1 << 38], 1, 0).shard_numel == 1 << 38
+
+
 def test_empty_plan(zs):
     p = zs.zs_shard_plan([], 4, 0)
     assert p.padded_numel == 0 and p.shard_numel == 0 and p.persistent_bytes == 0
