@@ -79,7 +79,7 @@
 #define ZS_GATHER_LDS_KB 8
 #endif
 #ifndef ZS_MULTI_LDS_KB
-#define ZS_MULTI_LDS_KB 16
+#define ZS_MULTI_LDS_KB 12
 #endif
 // Dequantizing gather: 8-element units per lane, and its occupancy throttle.
 #ifndef ZS_DEQUANT_U
