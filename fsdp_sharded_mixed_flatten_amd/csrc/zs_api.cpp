@@ -575,6 +575,11 @@ MultiLayout multi_layout(const zs_plan* p, int32_t n_contribs) {
     return L;
 }
 
+zs::MultiOffsets multi_offsets(const zs_plan* p, int32_t n_contribs) {
+    const MultiLayout L = multi_layout(p, n_contribs);
+    return zs::MultiOffsets{L.pieces_off, L.contribs_off, L.chunks_off};
+}
+
 zs_status check_multi_plan(const zs_plan* plan) {
     if (zs_status st = check_plan(plan)) return st;
     if (plan->layout != ZS_LAYOUT_PER_TENSOR)
@@ -709,7 +714,7 @@ zs_status zs_reduce_shard_multi(const zs_plan* plan, const void* workspace, void
     if (zs_status st = check_multi_plan(plan)) return st;
     Binding b;
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasContribs | zs::kHasGrad, &b)) return st;
-    return hip_status(zs::launch_multi(zs::kOpReduce, nullptr, workspace, (int)plan->chunks.size(), b.n_contribs, stream),
+    return hip_status(zs::launch_multi(zs::kOpReduce, nullptr, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunks.size(), b.n_contribs, stream),
                       "multi reduce launch");
 }
 
@@ -721,7 +726,7 @@ zs_status zs_adamw_shard_step_multi(const zs_plan* plan, const zs_adamw_hparams*
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasGrad | zs::kHasState, &b)) return st;
     zs::CoefTable ct;
     for (auto& e : ct.c) e = zs::make_coef(*hp);
-    return hip_status(zs::launch_multi(zs::kOpAdamw, &ct, workspace, (int)plan->chunks.size(), b.n_contribs, stream),
+    return hip_status(zs::launch_multi(zs::kOpAdamw, &ct, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunks.size(), b.n_contribs, stream),
                       "multi adamw launch");
 }
 
@@ -729,7 +734,7 @@ zs_status zs_gather_params_multi(const zs_plan* plan, const void* workspace, voi
     if (zs_status st = check_multi_plan(plan)) return st;
     Binding b;
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasParam | zs::kHasFull, &b)) return st;
-    return hip_status(zs::launch_multi(zs::kOpGather, nullptr, workspace, (int)plan->chunks.size(), b.n_contribs, stream),
+    return hip_status(zs::launch_multi(zs::kOpGather, nullptr, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunks.size(), b.n_contribs, stream),
                       "multi gather launch");
 }
 
@@ -741,7 +746,7 @@ zs_status zs_fused_shard_step_multi(const zs_plan* plan, const zs_adamw_hparams*
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasContribs | zs::kHasState, &b)) return st;
     zs::CoefTable ct;
     for (auto& e : ct.c) e = zs::make_coef(*hp);
-    return hip_status(zs::launch_multi(zs::kOpFused, &ct, workspace, (int)plan->chunks.size(), b.n_contribs, stream),
+    return hip_status(zs::launch_multi(zs::kOpFused, &ct, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunks.size(), b.n_contribs, stream),
                       "multi fused launch");
 }
 
@@ -770,7 +775,7 @@ zs_status zs_adamw_shard_step_multi_groups(const zs_plan* plan, const zs_adamw_h
     if (zs_status st = group_table(plan, hps, n_groups, &ct)) return st;
     Binding b;
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasGrad | zs::kHasState, &b)) return st;
-    return hip_status(zs::launch_multi(zs::kOpAdamw, &ct, workspace, (int)plan->chunks.size(), b.n_contribs, stream),
+    return hip_status(zs::launch_multi(zs::kOpAdamw, &ct, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunks.size(), b.n_contribs, stream),
                       "multi adamw launch");
 }
 
@@ -781,7 +786,7 @@ zs_status zs_fused_shard_step_multi_groups(const zs_plan* plan, const zs_adamw_h
     if (zs_status st = group_table(plan, hps, n_groups, &ct)) return st;
     Binding b;
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasContribs | zs::kHasState, &b)) return st;
-    return hip_status(zs::launch_multi(zs::kOpFused, &ct, workspace, (int)plan->chunks.size(), b.n_contribs, stream),
+    return hip_status(zs::launch_multi(zs::kOpFused, &ct, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunks.size(), b.n_contribs, stream),
                       "multi fused launch");
 }
 

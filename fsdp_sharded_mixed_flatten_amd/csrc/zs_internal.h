@@ -140,8 +140,15 @@ int launch_adamw_accum(const AdamCoef& c, const float* acc, float divisor, const
                        float* master, float* m, float* v, void* param, void* full_at_own, int64_t len, void* stream);
 
 enum MultiOp : int32_t { kOpReduce = 0, kOpAdamw = 1, kOpGather = 2, kOpFused = 3 };
-int launch_multi(int op, const CoefTable* c, const void* workspace, int n_chunks, int n_contribs,
-                 void* stream);
+// Byte offsets of the tables in a bound workspace (the header holds the same
+// values; the kernels take them as arguments to save a dependent load).
+struct MultiOffsets {
+    int64_t pieces;
+    int64_t contribs;
+    int64_t chunks;
+};
+int launch_multi(int op, const CoefTable* c, const void* workspace, const MultiOffsets& off, int n_chunks,
+                 int n_contribs, void* stream);
 int copy_h2d_sync(void* dst, const void* src, int64_t bytes, void* stream);
 
 // Host AdamW over n elements with n_threads host threads (zs_host_adamw.cpp);

@@ -691,13 +691,13 @@ __global__ __launch_bounds__(kBlock) void k_dequant(const char* __restrict__ cod
 // piece supplies every pointer and its hyperparameter group; the
 // contributions of piece i are cps[i * N .. i * N + N).
 template <int OP, int N>
-__global__ __launch_bounds__(kBlock) void k_multi(CoefTable ct, const MultiHeader* __restrict__ hdr,
+__global__ __launch_bounds__(kBlock) void k_multi(CoefTable ct, const MultiHeader* __restrict__ hdr, MultiOffsets off,
                                                   int n_rt, float nf) {
     static_assert(OP == kOpAdamw || OP == kOpFused, "reduce and gather have kernels of their own");
     if (hdr->magic != kMultiMagic) return;  // not a bound table (e.g. reused memory): touch nothing
     const char* ws = reinterpret_cast<const char*>(hdr);
-    const Chunk ch = reinterpret_cast<const Chunk*>(ws + hdr->chunks_off)[blockIdx.x];
-    const PieceDev pc = reinterpret_cast<const PieceDev*>(ws + hdr->pieces_off)[ch.piece];
+    const Chunk ch = reinterpret_cast<const Chunk*>(ws + off.chunks)[blockIdx.x];
+    const PieceDev pc = reinterpret_cast<const PieceDev*>(ws + off.pieces)[ch.piece];
     const AdamCoef c = ct.c[pc.group];
     const int flags = hdr->flags;
     const int64_t u0 = ch.start >> 2;  // chunk start and length are multiples of 8
@@ -709,7 +709,7 @@ __global__ __launch_bounds__(kBlock) void k_multi(CoefTable ct, const MultiHeade
                             (flags & kHasParam) ? reinterpret_cast<u32x2*>(pc.param) : nullptr, nullptr, base, limit);
     } else {
         const void* const* cps =
-            reinterpret_cast<const void* const*>(ws + hdr->contribs_off) + (int64_t)ch.piece * (N > 0 ? N : n_rt);
+            reinterpret_cast<const void* const*>(ws + off.contribs) + (int64_t)ch.piece * (N > 0 ? N : n_rt);
         fused_tile<N, kMultiU>(c, cps, n_rt, nf, reinterpret_cast<f32x4*>(pc.master), reinterpret_cast<f32x4*>(pc.m),
                                reinterpret_cast<f32x4*>(pc.v),
                                (flags & kHasGrad) ? reinterpret_cast<u32x2*>(pc.grad) : nullptr,
@@ -729,11 +729,12 @@ constexpr int kGatherRows = 4;
 constexpr int kGatherChunksPerBlock = kGatherChunksPerRow * kGatherRows;
 static_assert(kChunkElems % 8 == 0 && kBlock % kGatherLanesPerChunk == 0, "gather lanes must tile the wave");
 
-__global__ __launch_bounds__(kBlock) void k_multi_gather(const MultiHeader* __restrict__ hdr, int n_chunks) {
+__global__ __launch_bounds__(kBlock) void k_multi_gather(const MultiHeader* __restrict__ hdr, MultiOffsets moff,
+                                                         int n_chunks) {
     if (hdr->magic != kMultiMagic) return;
     const char* ws = reinterpret_cast<const char*>(hdr);
-    const Chunk* chunks = reinterpret_cast<const Chunk*>(ws + hdr->chunks_off);
-    const PieceDev* pieces = reinterpret_cast<const PieceDev*>(ws + hdr->pieces_off);
+    const Chunk* chunks = reinterpret_cast<const Chunk*>(ws + moff.chunks);
+    const PieceDev* pieces = reinterpret_cast<const PieceDev*>(ws + moff.pieces);
     const int lane = threadIdx.x;
     const int64_t first = (int64_t)blockIdx.x * kGatherChunksPerBlock + lane / kGatherLanesPerChunk;
     const int off = (lane % kGatherLanesPerChunk) * 8;
@@ -779,13 +780,13 @@ constexpr int kReduceRows = ZS_MULTI_REDUCE_ROWS;
 constexpr int kReduceChunksPerBlock = kGatherChunksPerRow * kReduceRows;
 
 template <int N>
-__global__ __launch_bounds__(kBlock) void k_multi_reduce(const MultiHeader* __restrict__ hdr, int n_chunks,
-                                                         int n_rt, float nf) {
+__global__ __launch_bounds__(kBlock) void k_multi_reduce(const MultiHeader* __restrict__ hdr, MultiOffsets moff,
+                                                         int n_chunks, int n_rt, float nf) {
     if (hdr->magic != kMultiMagic) return;
     const char* ws = reinterpret_cast<const char*>(hdr);
-    const Chunk* chunks = reinterpret_cast<const Chunk*>(ws + hdr->chunks_off);
-    const PieceDev* pieces = reinterpret_cast<const PieceDev*>(ws + hdr->pieces_off);
-    const void* const* cps = reinterpret_cast<const void* const*>(ws + hdr->contribs_off);
+    const Chunk* chunks = reinterpret_cast<const Chunk*>(ws + moff.chunks);
+    const PieceDev* pieces = reinterpret_cast<const PieceDev*>(ws + moff.pieces);
+    const void* const* cps = reinterpret_cast<const void* const*>(ws + moff.contribs);
     const int nq = N > 0 ? N : n_rt;
     const int lane = threadIdx.x;
     const int64_t first = (int64_t)blockIdx.x * kReduceChunksPerBlock + lane / kGatherLanesPerChunk;
@@ -1070,44 +1071,44 @@ int launch_fused_t(const AdamCoef& c, const void* const* contribs, int n, float*
 }
 
 template <int OP, int N>
-int launch_multi_t(const CoefTable& c, const void* ws, int n_chunks, int n, hipStream_t s) {
+int launch_multi_t(const CoefTable& c, const void* ws, const MultiOffsets& off, int n_chunks, int n, hipStream_t s) {
     hipLaunchKernelGGL((k_multi<OP, N>), dim3((unsigned)n_chunks), dim3(kBlock), kMultiLds, s, c,
-                       reinterpret_cast<const MultiHeader*>(ws), n, (float)n);
+                       reinterpret_cast<const MultiHeader*>(ws), off, n, (float)n);
     return (int)hipGetLastError();
 }
 
 template <int N>
-int launch_multi_reduce_t(const void* ws, int n_chunks, int n, hipStream_t s) {
+int launch_multi_reduce_t(const void* ws, const MultiOffsets& off, int n_chunks, int n, hipStream_t s) {
     hipLaunchKernelGGL((k_multi_reduce<N>),
                        dim3((unsigned)((n_chunks + kReduceChunksPerBlock - 1) / kReduceChunksPerBlock)), dim3(kBlock),
-                       kMultiLds, s, reinterpret_cast<const MultiHeader*>(ws), n_chunks, n, (float)n);
+                       kMultiLds, s, reinterpret_cast<const MultiHeader*>(ws), off, n_chunks, n, (float)n);
     return (int)hipGetLastError();
 }
 
-int launch_multi_reduce(const void* ws, int n_chunks, int n, hipStream_t s) {
+int launch_multi_reduce(const void* ws, const MultiOffsets& off, int n_chunks, int n, hipStream_t s) {
     switch (n) {
-        case 1: return launch_multi_reduce_t<1>(ws, n_chunks, n, s);
-        case 2: return launch_multi_reduce_t<2>(ws, n_chunks, n, s);
-        case 4: return launch_multi_reduce_t<4>(ws, n_chunks, n, s);
-        case 8: return launch_multi_reduce_t<8>(ws, n_chunks, n, s);
-        case 16: return launch_multi_reduce_t<16>(ws, n_chunks, n, s);
-        case 32: return launch_multi_reduce_t<32>(ws, n_chunks, n, s);
-        case 64: return launch_multi_reduce_t<64>(ws, n_chunks, n, s);
-        default: return launch_multi_reduce_t<0>(ws, n_chunks, n, s);
+        case 1: return launch_multi_reduce_t<1>(ws, off, n_chunks, n, s);
+        case 2: return launch_multi_reduce_t<2>(ws, off, n_chunks, n, s);
+        case 4: return launch_multi_reduce_t<4>(ws, off, n_chunks, n, s);
+        case 8: return launch_multi_reduce_t<8>(ws, off, n_chunks, n, s);
+        case 16: return launch_multi_reduce_t<16>(ws, off, n_chunks, n, s);
+        case 32: return launch_multi_reduce_t<32>(ws, off, n_chunks, n, s);
+        case 64: return launch_multi_reduce_t<64>(ws, off, n_chunks, n, s);
+        default: return launch_multi_reduce_t<0>(ws, off, n_chunks, n, s);
     }
 }
 
 template <int OP>
-int launch_multi_op(const CoefTable& c, const void* ws, int n_chunks, int n, hipStream_t s) {
+int launch_multi_op(const CoefTable& c, const void* ws, const MultiOffsets& off, int n_chunks, int n, hipStream_t s) {
     switch (n) {
-        case 1: return launch_multi_t<OP, 1>(c, ws, n_chunks, n, s);
-        case 2: return launch_multi_t<OP, 2>(c, ws, n_chunks, n, s);
-        case 4: return launch_multi_t<OP, 4>(c, ws, n_chunks, n, s);
-        case 8: return launch_multi_t<OP, 8>(c, ws, n_chunks, n, s);
-        case 16: return launch_multi_t<OP, 16>(c, ws, n_chunks, n, s);
-        case 32: return launch_multi_t<OP, 32>(c, ws, n_chunks, n, s);
-        case 64: return launch_multi_t<OP, 64>(c, ws, n_chunks, n, s);
-        default: return launch_multi_t<OP, 0>(c, ws, n_chunks, n, s);
+        case 1: return launch_multi_t<OP, 1>(c, ws, off, n_chunks, n, s);
+        case 2: return launch_multi_t<OP, 2>(c, ws, off, n_chunks, n, s);
+        case 4: return launch_multi_t<OP, 4>(c, ws, off, n_chunks, n, s);
+        case 8: return launch_multi_t<OP, 8>(c, ws, off, n_chunks, n, s);
+        case 16: return launch_multi_t<OP, 16>(c, ws, off, n_chunks, n, s);
+        case 32: return launch_multi_t<OP, 32>(c, ws, off, n_chunks, n, s);
+        case 64: return launch_multi_t<OP, 64>(c, ws, off, n_chunks, n, s);
+        default: return launch_multi_t<OP, 0>(c, ws, off, n_chunks, n, s);
     }
 }
 
@@ -1226,19 +1227,21 @@ int launch_fused(const AdamCoef& c, const void* const* contribs, int n, float* m
     }
 }
 
-int launch_multi(int op, const CoefTable* c, const void* workspace, int n_chunks, int n_contribs, void* stream) {
+int launch_multi(int op, const CoefTable* c, const void* workspace, const MultiOffsets& off, int n_chunks,
+                 int n_contribs, void* stream) {
     if (n_chunks <= 0) return 0;
     const CoefTable cc = c ? *c : CoefTable{};
     hipStream_t s = (hipStream_t)stream;
     switch (op) {
-        case kOpReduce: return launch_multi_reduce(workspace, n_chunks, n_contribs, s);
-        case kOpAdamw: return launch_multi_t<kOpAdamw, 1>(cc, workspace, n_chunks, 1, s);
+        case kOpReduce: return launch_multi_reduce(workspace, off, n_chunks, n_contribs, s);
+        case kOpAdamw: return launch_multi_t<kOpAdamw, 1>(cc, workspace, off, n_chunks, 1, s);
         case kOpGather:
             hipLaunchKernelGGL(k_multi_gather, dim3((unsigned)((n_chunks + kGatherChunksPerBlock - 1) /
                                                                kGatherChunksPerBlock)),
-                               dim3(kBlock), kMultiLds, s, reinterpret_cast<const MultiHeader*>(workspace), n_chunks);
+                               dim3(kBlock), kMultiLds, s, reinterpret_cast<const MultiHeader*>(workspace), off,
+                               n_chunks);
             return (int)hipGetLastError();
-        default: return launch_multi_op<kOpFused>(cc, workspace, n_chunks, n_contribs, s);
+        default: return launch_multi_op<kOpFused>(cc, workspace, off, n_chunks, n_contribs, s);
     }
 }
 
