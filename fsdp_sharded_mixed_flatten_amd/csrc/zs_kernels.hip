@@ -146,6 +146,12 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) { return bf16_rne(a) | (bf16_rne(b) << 16); }
 
+// The same rounding for values known not to be NaN (infinities included).
+__device__ __forceinline__ uint32_t pack2_finite(float a, float b) {
+    const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+    return ((ua + 0x7FFFu + ((ua >> 16) & 1u)) >> 16) | (((ub + 0x7FFFu + ((ub >> 16) & 1u)) >> 16) << 16);
+}
+
 // ------------------------------------------------------------------ AdamW element
 
 __device__ __forceinline__ void adamw_elem(const AdamCoef& c, float gf, float& w, float& m, float& v) {
@@ -668,18 +674,20 @@ __global__ __launch_bounds__(kBlock) void k_dequant(const char* __restrict__ cod
             int q;
             if constexpr (QB == 8) {
                 const uint32_t w = e < 4 ? lo[k] : hi[k];
-                q = (int)(int8_t)((w >> (8 * (e & 3))) & 0xFFu);
+                q = (int32_t)(w << (24 - 8 * (e & 3))) >> 24;  // signed byte: one v_bfe_i32
             } else {
-                const int nib = (int)((lo[k] >> (4 * e)) & 0xFu);
-                q = nib >= 8 ? nib - 16 : nib;
+                q = (int32_t)(lo[k] << (28 - 4 * e)) >> 28;  // signed 4-bit field: one v_bfe_i32
             }
             x[e] = (float)q * sc[k];
         }
+        // A code is finite, so a product is NaN only when the block's scale is:
+        // round without the per-element NaN path, then replace the whole unit.
         u32x4 o;
-        o.x = pack2(x[0], x[1]);
-        o.y = pack2(x[2], x[3]);
-        o.z = pack2(x[4], x[5]);
-        o.w = pack2(x[6], x[7]);
+        o.x = pack2_finite(x[0], x[1]);
+        o.y = pack2_finite(x[2], x[3]);
+        o.z = pack2_finite(x[4], x[5]);
+        o.w = pack2_finite(x[6], x[7]);
+        if (sc[k] != sc[k]) o = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
         st_out(full + r * s8 + u, o);
     }
 }
