@@ -7,10 +7,12 @@ bf16 parameter write into the gathered buffer. Inputs are synthetic (seeded
 generator, generated in HBM before the timed region); the other N-1 ranks'
 contributions are local buffers on the one GPU.
 
-Default workload: the Llama-7B shape (6,738,415,616 parameters, 291 tensors)
-at N=8, rank 0 -- an 842,301,952-element shard -- through the fused kernel.
-Prints one JSON line. ``--gpus`` above 1 exits: this benchmark is one GPU's
-share by construction.
+Default workload: the Qwen2.5-3B shape (3,085,938,688 parameters, 434
+tensors, 128-element tensor alignment) at N=4, rank 0 -- a 771,484,672-element
+shard -- through the fused kernel, after one warm step. The fused steps of the
+Llama-7B shape (N=8) and the Llama-70B shape (N=64) are timed as well and
+reported under ``other_workloads``. Prints one JSON line. ``--gpus`` above 1
+exits: this benchmark is one GPU's share by construction.
 """
 
 import argparse
@@ -51,8 +53,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama7b",
+    ap.add_argument("--workload", default="qwen3b",
                     choices=["tiny", "qwen3b", "llama7b", "llama7b_wrap", "llama70b"])
+    ap.add_argument("--also", default="llama7b,llama70b",
+                    help="comma-separated FLAT workloads whose fused step is also timed and reported under "
+                         "'other_workloads' ('none' skips them)")
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused path's timing")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-window", type=int, default=100_000_000,
@@ -249,6 +254,43 @@ def cpu_baseline(oracle, synth, wl, S, window, fused_bpp):
             "core_seconds": cpu_seconds,
             "gbps_algorithmic": n * fused_bpp / med / 1e9,
             "single_thread_params_per_s": n / secs1[0]}
+
+
+def extra_fused_leg(zs, synth, torch, name, args):
+    """The fused step of another FLAT workload, timed like the main one."""
+    wl = synth.workloads()[name]
+    N = wl.world
+    hp0 = zs.AdamWHParams(wl.lr, wl.beta1, wl.beta2, wl.eps, wl.weight_decay, 1)
+    log(f"[bench] also: workload={wl.name} N={N} rank={wl.rank}")
+    try:
+        plan, st = flat_setup(zs, synth, wl)
+    except torch.cuda.OutOfMemoryError as e:
+        torch.cuda.empty_cache()
+        return {"skipped": f"device memory: {str(e).splitlines()[0]}"}
+    S = plan.shard_numel
+    write_grad = N >= 64
+    grad_out = st["grad"] if write_grad else None
+
+    def fused(t, timer):
+        e = timer.start() if timer else None
+        zs.zs_fused_shard_step(plan, hp0.at(t), st["contribs"], st["master"], st["m"], st["v"], grad=grad_out,
+                               full=st["full"])
+        if timer:
+            timer.stop(e)
+
+    wall, kern, ev = time_loop(fused, args.warmup, args.steps)
+    bpp = fused_bytes_per_param(N, write_grad=write_grad)
+    kname = "k_reduce+k_adamw" if write_grad else "k_fused"
+    achieved = S * bpp / (kern / 1e3) / 1e9
+    out = {"workload": f"{wl.name}_n{N}_fused", "world_size": N, "shard_elems": S, "ms_per_step": wall,
+           "kernel_ms_mean": kern, "kernel_ms_median": statistics.median(ev), "kernel_ms_p99": p99(ev),
+           "params_per_s": S / (wall / 1e3), "bytes_per_param": bpp,
+           "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": achieved / HBM_PEAK_GBPS, "traffic": read_traffic(kname, wl.name), "kernel": kname,
+                        "algorithmic_bytes_per_launch": S * bpp}}
+    del st, plan
+    torch.cuda.empty_cache()
+    return out
 
 
 def offload_leg(zs, torch, plan, st, hp0, S, args, fused):
@@ -508,6 +550,14 @@ def main():
     step_gbps = S * bpp / (wall_ms / 1e3) / 1e9
     kname = result_paths[main_path]["kernel"]
     traffic = read_traffic(kname, wl.name)
+    gathered = "full" if wl.layout != "flat" or st.get("full_is_T") else "owned slice"
+    st = None
+    torch.cuda.empty_cache()
+    others = {}
+    for name in ([] if args.also == "none" else [x for x in args.also.split(",") if x and x != wl.name]):
+        if synth.workloads()[name].layout != "flat":
+            continue
+        others[name] = extra_fused_leg(zs, synth, torch, name, args)
     cpu = None
     if not args.no_cpu:
         import oracle
@@ -528,7 +578,7 @@ def main():
         "data": "synthetic (seeded counter-based generator; model shapes only, no weights)",
         "config": {"workload": f"{wl.name}_n{N}_{main_path}", "world_size": N, "rank": wl.rank,
                    "layout": wl.layout, "shard_elems": S, "bytes_per_param": bpp,
-                   "gathered_buffer": "full" if wl.layout != "flat" or st.get("full_is_T") else "owned slice",
+                   "gathered_buffer": gathered,
                    **({"piece_buffers": "carved from one allocation per array at the plan's offsets"}
                       if wl.layout != "flat" else {})},
         "hbm_gbps": step_gbps,
@@ -538,6 +588,7 @@ def main():
                      "kernel": kname, "algorithmic_bytes_per_launch": S * bpp},
         "cpu_baseline": cpu,
         "paths": result_paths,
+        "other_workloads": others,
     }
     print(json.dumps(out), flush=True)
 
