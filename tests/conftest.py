@@ -8,6 +8,19 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
+def import_zs():
+    """The library's binding; on a checkout where the library is not built
+    yet, build it first (hipcc cross-compiles gfx950 code without a GPU)."""
+    import importlib
+    import subprocess
+    try:
+        return importlib.import_module("fsdp_sharded_mixed_flatten_amd")
+    except ImportError:
+        subprocess.run([sys.executable, os.path.join(ROOT, "fsdp_sharded_mixed_flatten_amd", "build.py")],
+                       check=True)
+        return importlib.import_module("fsdp_sharded_mixed_flatten_amd")
+
+
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs a real MI355X (gfx950) and the built HIP library")
 

@@ -8,6 +8,7 @@ import re
 
 import pytest
 
+from conftest import import_zs
 from oracle.plan import plan_flat, plan_per_tensor
 from synth import shapes
 
@@ -17,19 +18,7 @@ HEADER = os.path.join(ROOT, "include", "zs.h")
 
 @pytest.fixture(scope="module")
 def zs():
-    lib = os.path.join(ROOT, "fsdp_sharded_mixed_flatten_amd", "libzs.so")
-    if not os.path.exists(lib):
-        from fsdp_sharded_mixed_flatten_amd import build as b  # noqa: F401 -- only when nothing is built
-    import importlib
-    try:
-        mod = importlib.import_module("fsdp_sharded_mixed_flatten_amd")
-    except ImportError:
-        import subprocess
-        import sys
-        subprocess.run([sys.executable, os.path.join(ROOT, "fsdp_sharded_mixed_flatten_amd", "build.py")],
-                       check=True)
-        mod = importlib.import_module("fsdp_sharded_mixed_flatten_amd")
-    return mod
+    return import_zs()
 
 
 def test_exports_every_declared_symbol(zs):

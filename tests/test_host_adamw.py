@@ -8,12 +8,12 @@ import pytest
 
 import oracle
 import synth
+from conftest import import_zs
 
 
 @pytest.fixture(scope="module")
 def zs():
-    import fsdp_sharded_mixed_flatten_amd as m
-    return m
+    return import_zs()
 
 
 def _grads(n, t, seed):
