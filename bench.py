@@ -65,9 +65,9 @@ def parse():
     ap.add_argument("--arena-pad-kb", type=int, default=-1,
                     help="allocate the N contributions (and master/m/v) as rows of one buffer whose "
                          "rows start this many KiB apart beyond their length (-1: separate tensors)")
-    ap.add_argument("--accum", type=int, default=0,
+    ap.add_argument("--accum", type=int, default=4,
                     help="also time an optimizer step with this many accumulated micro-batches, global-norm "
-                         "clipping and the non-finite skip (FLAT workloads)")
+                         "clipping and the non-finite skip (FLAT workloads; 0 skips it)")
     ap.add_argument("--clip", type=float, default=1.0, help="max norm of the --accum path")
     ap.add_argument("--quant", default="4:256",
                     help="BITS:BLOCK of the quantized-gather legs (fused step writing codes, and the "
