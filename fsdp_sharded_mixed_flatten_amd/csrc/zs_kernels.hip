@@ -122,6 +122,12 @@ constexpr int kAdamwU = ZS_ADAMW_U;
 constexpr int kFusedU = ZS_FUSED_U;
 constexpr unsigned kFusedLds = ZS_FUSED_LDS_KB * 1024u;
 constexpr unsigned kFusedNarrowLds = ZS_FUSED_NARROW_LDS_KB * 1024u;
+// Accumulation micro-steps at 4 or fewer ranks (reads 2N+4 bytes, writes 4
+// per element) run fastest with more resident waves than the fused kernel.
+#ifndef ZS_ACCUM_NARROW_LDS_KB
+#define ZS_ACCUM_NARROW_LDS_KB 8
+#endif
+constexpr unsigned kAccumNarrowLds = ZS_ACCUM_NARROW_LDS_KB * 1024u;
 constexpr unsigned kReduceLds = ZS_REDUCE_LDS_KB * 1024u;
 constexpr unsigned kReduceWideLds = ZS_REDUCE_WIDE_LDS_KB * 1024u;
 constexpr int kWideN = ZS_WIDE_N;
@@ -1125,11 +1131,12 @@ int launch_accum_t(const void* const* contribs, int n, float* acc, int first, in
     Ptrs<CAP> cp{};
     for (int q = 0; q < n; ++q) cp.p[q] = contribs[q];
     const int64_t n4 = len / 4;
+    const unsigned lds = n <= 4 ? kAccumNarrowLds : kFusedLds;
     if (first)
-        hipLaunchKernelGGL((k_accum<N, CAP, true>), dim3(grid_for(n4, kFusedU)), dim3(kBlock), kFusedLds, s, cp, n,
+        hipLaunchKernelGGL((k_accum<N, CAP, true>), dim3(grid_for(n4, kFusedU)), dim3(kBlock), lds, s, cp, n,
                            (float)n, reinterpret_cast<f32x4*>(acc), n4);
     else
-        hipLaunchKernelGGL((k_accum<N, CAP, false>), dim3(grid_for(n4, kFusedU)), dim3(kBlock), kFusedLds, s, cp, n,
+        hipLaunchKernelGGL((k_accum<N, CAP, false>), dim3(grid_for(n4, kFusedU)), dim3(kBlock), lds, s, cp, n,
                            (float)n, reinterpret_cast<f32x4*>(acc), n4);
     return (int)hipGetLastError();
 }
