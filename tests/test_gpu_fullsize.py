@@ -184,15 +184,26 @@ def test_llama7b_shape_ten_steps_bucketed_and_fused(zs):
     _release()
 
 
-def test_llama7b_wrap_stress_multi_tensor(zs):
+@pytest.mark.parametrize("persist", [0, 100_000])
+def test_llama7b_wrap_stress_multi_tensor(zs, persist):
+    """The 291-piece per-tensor plan; with persist=100,000 (the threshold the
+    pages suggest) the 65 norm vectors are replicated and updated whole with a
+    second hyperparameter group (no weight decay), as an FSDP2 model would
+    hold them."""
     import torch
     wl = synth.workloads()["llama7b_wrap"]
     if _free_gib() < 60:
         pytest.skip("needs ~50 GiB of free device memory")
-    plan = zs.zs_shard_plan(wl.numels, wl.world, wl.rank, 1, zs.ZS_LAYOUT_PER_TENSOR)
-    op = oracle.plan_per_tensor(wl.numels, wl.world, wl.rank)
+    groups = [1 if n < persist else 0 for n in wl.numels] if persist else None
+    if persist:
+        plan = zs.zs_shard_plan_ex(wl.numels, wl.world, wl.rank, persist_below_elems=persist, groups=groups)
+    else:
+        plan = zs.zs_shard_plan(wl.numels, wl.world, wl.rank, 1, zs.ZS_LAYOUT_PER_TENSOR)
+    op = oracle.plan_per_tensor(wl.numels, wl.world, wl.rank, persist)
     assert len(op.pieces) == 291
-    print(f"[llama7b_wrap] pieces={len(op.pieces)} S={plan.shard_numel:,}", flush=True)
+    assert sum(1 for i in range(291) if zs.lib().zs_plan_tensor_replicated(plan.handle, i) == 1) == \
+        (65 if persist else 0)
+    print(f"[llama7b_wrap persist={persist}] pieces={len(op.pieces)} S={plan.shard_numel:,}", flush=True)
     rng = np.random.default_rng(5)
     pieces, contribs, samples = [], [[] for _ in range(wl.world)], []
     for i, pc in enumerate(op.pieces):
@@ -216,11 +227,16 @@ def test_llama7b_wrap_stress_multi_tensor(zs):
     ws = torch.zeros(zs.zs_multi_workspace_bytes(plan, wl.world), dtype=torch.uint8, device="cuda")
     zs.zs_multi_bind(plan, pieces, contribs, ws)
     hp = _hp(zs, wl)
-    zs.zs_fused_shard_step_multi(plan, hp, ws)
+    hps = [hp, zs.AdamWHParams(wl.lr, wl.beta1, wl.beta2, wl.eps, 0.0, 1)]
+    if persist:
+        zs.zs_fused_shard_step_multi_groups(plan, hps, ws)
+    else:
+        zs.zs_fused_shard_step_multi(plan, hp, ws)
     torch.cuda.synchronize()
-    h = oracle.HParams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, 1)
     nd = 0
     for i, pc in enumerate(op.pieces):
+        x = hps[groups[pc.tensor]] if persist else hp
+        h = oracle.HParams(x.lr, x.beta1, x.beta2, x.eps, x.weight_decay, 1)
         s, valid = samples[i]
         gi = pc.full_off + s
         cs = [synth.cpu_at_bf16(gi, wl.contrib_spec(q, 1, valid)) for q in range(wl.world)]
