@@ -203,14 +203,21 @@ zs_status zs_shard_plan_ex(const int64_t* numels, int32_t n_tensors, int32_t wor
                     delete p;
                     return fail(ZS_EINVAL, "packed buffer exceeds 2^60 elements");
                 }
-                for (int64_t c = 0; c < Si; c += zs::kChunkElems)
-                    p->chunks.push_back(zs::Chunk{i, (int32_t)std::min<int64_t>(zs::kChunkElems, Si - c), c});
             }
             p->T = full;
             p->S = shard;
-            if (p->chunks.size() > (size_t)INT32_MAX) {
+            if (shard > kMaxShardElems) {  // checked before the chunk list is built
                 delete p;
-                return fail(ZS_EINVAL, "too many multi-tensor chunks");
+                return fail(ZS_EINVAL, "owned shard of %lld elements exceeds 2^38", (long long)shard);
+            }
+            static_assert(kMaxShardElems / zs::kChunkElems < INT32_MAX, "chunk count must fit the 32-bit grid");
+            int64_t n_chunks = 0;
+            for (const auto& t : p->tensors) n_chunks += (t.own_hi - t.own_lo + zs::kChunkElems - 1) / zs::kChunkElems;
+            p->chunks.reserve((size_t)n_chunks);
+            for (int32_t i = 0; i < n_tensors; ++i) {
+                const int64_t Si = p->tensors[(size_t)i].own_hi - p->tensors[(size_t)i].own_lo;
+                for (int64_t c = 0; c < Si; c += zs::kChunkElems)
+                    p->chunks.push_back(zs::Chunk{i, (int32_t)std::min<int64_t>(zs::kChunkElems, Si - c), c});
             }
         }
     } catch (const std::bad_alloc&) {

@@ -150,6 +150,11 @@ def test_plan_rejects_shards_beyond_any_device(zs):
         zs.zs_shard_plan([1 << 40], 2, 0)
     assert e.value.status == zs.ZS_EINVAL and "2^38" in e.value.message
     assert zs.zs_shard_plan([1 << 38], 1, 0).shard_numel == 1 << 38
+    # per-tensor: refused before a chunk list of billions of entries is built
+    for numels in ([1 << 45], [1 << 37, 1 << 37, 1 << 37]):
+        with pytest.raises(zs.ZsError) as e:
+            zs.zs_shard_plan(numels, 1, 0, layout=zs.ZS_LAYOUT_PER_TENSOR)
+        assert e.value.status == zs.ZS_EINVAL and "2^38" in e.value.message
 
 
 def test_empty_plan(zs):
