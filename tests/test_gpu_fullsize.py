@@ -394,3 +394,166 @@ def test_llama7b_shape_offloaded_step(zs):
     assert bool((full[S:S + 4096] == SENT).all())
     del run, full, grad, hm, hmm, hv, gh, ph
     _release()
+
+
+def test_shard_beyond_2pow32_elements(zs):
+    """The largest shard exercised: 4,295,032,832 owned elements (past 2^32)
+    at N=2, rank 1, so the owned slice of the gathered buffer also starts past
+    2^32; one tensor with 13 elements of tail padding. Every entry point runs
+    on the same state: bucketed reduce (bucket edges at 2^31 + 8 and
+    2^32 - 8), AdamW and gather at t=1; the fused step at t=2; one accumulated
+    micro-step, the squared norm, the clip factor and the step from the
+    accumulator at t=3; the quantized fused step (int4, B=256) at t=4 and the
+    dequantizing gather of two payloads into the 8.6 G-element buffer.
+    Samples are whole 256-element blocks: the first, the last, four on each
+    side of 2^31 and 2^32, and 600 random ones."""
+    import torch
+    N, r, B = 2, 1, 256
+    S = 2**32 + 65_536
+    T = N * S
+    numel = T - 13
+    if _free_gib() < 125:
+        pytest.skip("needs ~120 GiB of free device memory")
+    plan = zs.zs_shard_plan([numel], N, r, 1, zs.ZS_LAYOUT_FLAT)
+    assert (plan.shard_numel, plan.padded_numel) == (S, T)
+    base = r * S
+    seed = 0xB16
+    master_sp = synth.spec(seed, synth.STREAM_MASTER, 0, 0.02, numel)
+
+    def csp(q, t):
+        return synth.spec(seed, synth.STREAM_CONTRIB + q, t, 1e-3, numel)
+
+    nb = S // B
+    special = [0, nb - 1]
+    for e in (2**31, 2**32):
+        special += list(range(e // B - 4, e // B + 4))
+    blocks = np.unique(np.concatenate([special, np.random.default_rng(5).integers(0, nb, 600)])).astype(np.int64)
+    idx = (blocks[:, None] * B + np.arange(B)[None, :]).ravel()
+    didx = torch.from_numpy(idx).cuda()
+    gi = base + idx
+    print(f"[beyond 2^32] N={N} S={S:,} T={T:,} samples={idx.size:,}", flush=True)
+
+    contribs = [torch.empty(S, dtype=torch.int16, device="cuda") for _ in range(N)]
+    master = torch.empty(S, dtype=torch.float32, device="cuda")
+    synth.gpu_f32(master, base, master_sp)
+    m = torch.zeros(S, dtype=torch.float32, device="cuda")
+    v = torch.zeros(S, dtype=torch.float32, device="cuda")
+    grad = torch.empty(S, dtype=torch.int16, device="cuda")
+    param = torch.empty(S, dtype=torch.int16, device="cuda")
+    full = torch.empty(T, dtype=torch.int16, device="cuda")
+    synth.gpu_fill_u16(full, SENT)
+    K = idx.size
+    o = dict(master=synth.cpu_at_f32(gi, master_sp), m=np.zeros(K, np.float32), v=np.zeros(K, np.float32),
+             g=np.zeros(K, np.uint16), p=np.zeros(K, np.uint16))
+    hp = zs.AdamWHParams(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1)
+
+    def ora_hp(t):
+        return oracle.HParams(1e-3, 0.9, 0.95, 1e-8, 0.1, t)
+
+    def gen(t):
+        for q, c in enumerate(contribs):
+            synth.gpu_bf16(c, base, csp(q, t))
+        return [synth.cpu_at_bf16(gi, csp(q, t)) for q in range(N)]
+
+    def pick16(x, at=didx):
+        return x.index_select(0, at).cpu().numpy().view(np.uint16)
+
+    def pick32(x):
+        return x.index_select(0, didx).cpu().numpy()
+
+    def check(tag, with_grad):
+        torch.cuda.synchronize()
+        nd = check_f32(pick32(master), o["master"], f"{tag} master") + check_f32(pick32(m), o["m"], f"{tag} m")
+        nd += check_f32(pick32(v), o["v"], f"{tag} v") + check_bf16(pick16(param), o["p"], f"{tag} param")
+        if with_grad:
+            nd += check_bf16(pick16(grad), o["g"], f"{tag} grad")
+        assert nd == 0, f"{tag}: {nd} sampled elements not bit-identical"
+
+    own = torch.from_numpy(base + idx).cuda()
+    other = torch.from_numpy(np.array([0, 2**31 - 1, 2**31, 2**32 - 1, 2**32, S - 1], np.int64)).cuda()
+
+    # t=1: bucketed reduce, AdamW, gather
+    cs = gen(1)
+    edges = [0, 2**31 + 8, 2**32 - 8, S]
+    for a, b in zip(edges[:-1], edges[1:]):
+        zs.zs_reduce_shard(plan, contribs, grad, a, b - a)
+    zs.zs_adamw_shard_step(plan, hp.at(1), grad, master, m, v, param)
+    zs.zs_gather_params(plan, param, full)
+    oracle.reduce(cs, out=o["g"])
+    oracle.adamw(ora_hp(1), o["g"], o["master"], o["m"], o["v"], o["p"])
+    check("t=1 bucketed", True)
+    assert np.array_equal(pick16(full, own), o["p"])
+    assert np.all(pick16(full, other) == SENT), "the gather wrote into rank 0's slice"
+    assert np.all(o["p"][-13:] == 0) and np.all(o["master"][-13:] == 0)  # tail padding stays +0
+
+    # t=2: fused step
+    cs = gen(2)
+    zs.zs_fused_shard_step(plan, hp.at(2), contribs, master, m, v, grad=grad, param=param, full=full)
+    oracle.reduce(cs, out=o["g"])
+    oracle.adamw(ora_hp(2), o["g"], o["master"], o["m"], o["v"], o["p"])
+    check("t=2 fused", True)
+    assert np.array_equal(pick16(full, own), o["p"])
+
+    # t=3: one accumulated micro-step, norm, clip factor, step from the accumulator
+    cs = gen(3)
+    acc = torch.empty(S, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(zs.zs_grad_stats_workspace_bytes(plan), dtype=torch.uint8, device="cuda")
+    sumsq = torch.zeros(1, dtype=torch.float64, device="cuda")
+    flag = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    scale = torch.zeros(1, dtype=torch.float32, device="cuda")
+    skip = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    max_norm = 10.0  # the gradient's norm is ~46: clipping is active
+    zs.zs_accumulate_shard(plan, contribs, acc, first=True)
+    zs.zs_grad_stats(plan, acc, 1.0, sumsq, flag, ws)
+    zs.zs_clip_scale(sumsq, flag, max_norm, scale, skip)
+    zs.zs_adamw_shard_step_accum(plan, hp.at(3), acc, 1.0, master, m, v, scale=scale, skip=skip, param=param,
+                                 full=full)
+    o_acc = np.zeros(K, np.float32)
+    oracle.accumulate(cs, o_acc, first=True)
+    torch.cuda.synchronize()
+    assert check_f32(pick32(acc), o_acc, "t=3 acc") == 0
+    assert int(flag.cpu()[0]) == 0 and int(skip.cpu()[0]) == 0
+    got = float(sumsq.cpu()[0])
+    ref = sum(float(acc[a:a + 2**28].double().square().sum()) for a in range(0, S, 2**28))
+    assert abs(got - ref) <= 1e-12 * ref, (got, ref)
+    sc = float(scale.cpu()[0])
+    assert sc == oracle.clip_scale([got], max_norm) and 0.0 < sc < 1.0
+    oracle.adamw_f32grad(ora_hp(3), o_acc, 1.0, sc, False, o["master"], o["m"], o["v"], o["p"])
+    check("t=3 accumulated", False)
+    assert np.array_equal(pick16(full, own), o["p"])
+    del acc, ws
+    _release()
+
+    # t=4: quantized fused step, then the dequantizing gather of two payloads
+    cs = gen(4)
+    bits = 4
+    codes = torch.empty(zs.zs_quant_code_bytes(plan, bits), dtype=torch.uint8, device="cuda")
+    scales = torch.empty(zs.zs_quant_num_scales(plan, B), dtype=torch.float32, device="cuda")
+    assert codes.numel() == S // 2 and scales.numel() == S // B
+    zs.zs_fused_shard_step_quant(plan, hp.at(4), contribs, master, m, v, bits, B, codes, scales, grad=grad,
+                                 param=param)
+    oracle.reduce(cs, out=o["g"])
+    oracle.adamw(ora_hp(4), o["g"], o["master"], o["m"], o["v"], o["p"])
+    check("t=4 quantized", True)
+    o_codes, o_scales, o_dec = [], [], []
+    for k in range(blocks.size):
+        q, s = oracle.quantize(o["p"][k * B:(k + 1) * B], bits, B)
+        o_codes.append(q)
+        o_scales.append(s)
+        o_dec.append(oracle.dequantize(q, s, B, bits, B))
+    g_scales = scales.index_select(0, torch.from_numpy(blocks).cuda()).cpu().numpy()
+    assert np.array_equal(g_scales.view(np.uint32), np.concatenate(o_scales).view(np.uint32))
+    byte_idx = (blocks[:, None] * (B // 2) + np.arange(B // 2)[None, :]).ravel()
+    g_codes = codes.index_select(0, torch.from_numpy(byte_idx).cuda()).cpu().numpy()
+    assert np.array_equal(g_codes, np.concatenate(o_codes)), "code bytes differ"
+    for c in contribs:
+        c.set_(torch.empty(0, dtype=torch.int16, device="cuda"))
+    _release()
+    zs.zs_dequant_gather(plan, bits, B, codes.repeat(N), scales.repeat(N), full)
+    torch.cuda.synchronize()
+    o_dec = np.concatenate(o_dec)
+    for q in range(N):  # rank 0's payload is a copy of rank 1's
+        got = pick16(full, torch.from_numpy(q * S + idx).cuda())
+        assert check_bf16(got, o_dec, f"gathered slice of rank {q}") == 0
+    del master, m, v, grad, param, full, codes, scales, contribs
+    _release()
