@@ -557,3 +557,101 @@ def test_shard_beyond_2pow32_elements(zs):
         assert check_bf16(got, o_dec, f"gathered slice of rank {q}") == 0
     del master, m, v, grad, param, full, codes, scales, contribs
     _release()
+
+
+def test_multi_tensor_piece_beyond_2pow32(zs):
+    """Multi-tensor apply with one piece of 4,295,032,832 owned elements (a
+    tensor of 2^33 + 131,059 elements at N=2, rank 1, whose owned range of
+    the gathered tensor also starts past 2^32) between two small pieces: the
+    unfused calls (reduce, AdamW, gather) at t=1 and the fused call at t=2.
+    The big piece is sampled in whole 256-element runs (first, last, both
+    sides of 2^31 and 2^32, random); the small pieces are checked in full."""
+    import torch
+    N, r = 2, 1
+    numels = [77, 2**33 + 131_059, 4096]
+    if _free_gib() < 125:
+        pytest.skip("needs ~110 GiB of free device memory")
+    plan = zs.zs_shard_plan(numels, N, r, 1, zs.ZS_LAYOUT_PER_TENSOR)
+    oplan = oracle.plan_per_tensor(numels, N, r, 0)
+    sizes = [pc.own_hi - pc.own_lo for pc in oplan.pieces]
+    assert sizes[1] == 2**32 + 65_536 and oplan.pieces[1].own_lo == sizes[1]
+    seed = 0xB17
+    valid = [oplan.offsets[i] + numels[i] for i in range(3)]
+
+    def msp(i):
+        return synth.spec(seed, synth.STREAM_MASTER, 0, 0.02, valid[i])
+
+    def csp(i, q, t):
+        return synth.spec(seed, synth.STREAM_CONTRIB + q, t, 1e-3, valid[i])
+
+    S1 = sizes[1]
+    nb = S1 // 256
+    special = [0, nb - 1]
+    for e in (2**31, 2**32):
+        special += list(range(e // 256 - 4, e // 256 + 4))
+    runs = np.unique(np.concatenate([special, np.random.default_rng(6).integers(0, nb, 400)])).astype(np.int64)
+    samples = [np.arange(sizes[0]), (runs[:, None] * 256 + np.arange(256)[None, :]).ravel(), np.arange(sizes[2])]
+    dsamples = [torch.from_numpy(x).cuda() for x in samples]
+    bases = [pc.full_off for pc in oplan.pieces]  # packed global index of each piece's first owned element
+    print(f"[multi beyond 2^32] pieces={sizes} samples={[x.size for x in samples]}", flush=True)
+
+    pieces, o = [], []
+    for i, Si in enumerate(sizes):
+        d = dict(grad=torch.empty(Si, dtype=torch.int16, device="cuda"),
+                 master=torch.empty(Si, dtype=torch.float32, device="cuda"),
+                 m=torch.zeros(Si, dtype=torch.float32, device="cuda"),
+                 v=torch.zeros(Si, dtype=torch.float32, device="cuda"),
+                 param=torch.empty(Si, dtype=torch.int16, device="cuda"),
+                 full=torch.empty(oplan.padded[i], dtype=torch.int16, device="cuda"))
+        synth.gpu_f32(d["master"], bases[i], msp(i))
+        synth.gpu_fill_u16(d["full"], SENT)
+        pieces.append(d)
+        K = samples[i].size
+        o.append(dict(master=synth.cpu_at_f32(bases[i] + samples[i], msp(i)), m=np.zeros(K, np.float32),
+                      v=np.zeros(K, np.float32), g=np.zeros(K, np.uint16), p=np.zeros(K, np.uint16)))
+    contribs = [[torch.empty(Si, dtype=torch.int16, device="cuda") for Si in sizes] for _ in range(N)]
+    ws = torch.zeros(zs.zs_multi_workspace_bytes(plan, N), dtype=torch.uint8, device="cuda")
+    zs.zs_multi_bind(plan, pieces, contribs, ws)
+    hp = zs.AdamWHParams(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1)
+
+    def step_oracle(t):
+        for i in range(3):
+            cs = [synth.cpu_at_bf16(bases[i] + samples[i], csp(i, q, t)) for q in range(N)]
+            oracle.reduce(cs, out=o[i]["g"])
+            oracle.adamw(oracle.HParams(1e-3, 0.9, 0.95, 1e-8, 0.1, t), o[i]["g"], o[i]["master"], o[i]["m"],
+                         o[i]["v"], o[i]["p"])
+
+    def check(tag):
+        torch.cuda.synchronize()
+        nd = 0
+        for i, d in enumerate(pieces):
+            at = dsamples[i]
+
+            def pick(x):
+                return x.index_select(0, at).cpu().numpy()
+
+            nd += check_f32(pick(d["master"]), o[i]["master"], f"{tag} master[{i}]")
+            nd += check_f32(pick(d["m"]), o[i]["m"], f"{tag} m[{i}]") + check_f32(pick(d["v"]), o[i]["v"],
+                                                                                   f"{tag} v[{i}]")
+            nd += check_bf16(pick(d["grad"]).view(np.uint16), o[i]["g"], f"{tag} grad[{i}]")
+            nd += check_bf16(pick(d["param"]).view(np.uint16), o[i]["p"], f"{tag} param[{i}]")
+            own = torch.from_numpy(oplan.pieces[i].own_lo + samples[i]).cuda()
+            assert np.array_equal(d["full"].index_select(0, own).cpu().numpy().view(np.uint16), o[i]["p"])
+            assert int(d["full"][0]) & 0xFFFF == SENT  # rank 0's range untouched
+        assert nd == 0, f"{tag}: {nd} sampled elements not bit-identical"
+
+    for t in (1, 2):
+        for q in range(N):
+            for i in range(3):
+                synth.gpu_bf16(contribs[q][i], bases[i], csp(i, q, t))
+        if t == 1:
+            zs.zs_reduce_shard_multi(plan, ws)
+            zs.zs_adamw_shard_step_multi(plan, hp.at(t), ws)
+            zs.zs_gather_params_multi(plan, ws)
+        else:
+            zs.zs_fused_shard_step_multi(plan, hp.at(t), ws)
+        step_oracle(t)
+        check(f"t={t}")
+    zs.zs_multi_unbind(ws)
+    del pieces, contribs, ws
+    _release()
