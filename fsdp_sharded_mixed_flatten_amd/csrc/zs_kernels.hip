@@ -686,8 +686,10 @@ __global__ __launch_bounds__(kBlock) void k_dequant(const char* __restrict__ cod
             }
             x[e] = (float)q * sc[k];
         }
-        // A code is finite, so a product is NaN only when the block's scale is:
-        // round without the per-element NaN path, then replace the whole unit.
+        // A code is finite, so a product is NaN only when the block's scale is
+        // NaN (the whole unit is replaced below) or infinite with a zero code
+        // (the default NaN, which the rounding keeps a NaN): round without the
+        // per-element NaN path.
         u32x4 o;
         o.x = pack2_finite(x[0], x[1]);
         o.y = pack2_finite(x[2], x[3]);

@@ -88,7 +88,7 @@ def test_quantize_shard(zs, bits, block):
 
 
 @pytest.mark.parametrize("bits", [4, 8])
-@pytest.mark.parametrize("world,block", [(4, 64), (8, 256), (3, 16)])
+@pytest.mark.parametrize("world,block", [(4, 64), (8, 256), (3, 16), (5, 128)])
 def test_dequant_gather(zs, bits, world, block):
     import torch
     plan = zs.zs_shard_plan([123_457, 999], world, 0, 1)
@@ -105,6 +105,35 @@ def test_dequant_gather(zs, bits, world, block):
     got = host16(full)
     nd = check_bf16(got[:world * S], ref, "gathered")
     assert nd == 0
+    assert np.all(got[world * S:] == 0x5A5A)
+
+
+@pytest.mark.parametrize("bits,block,S", [(4, 256, 15_560), (4, 128, 24_896), (4, 8, 1_000), (8, 256, 15_560)])
+def test_dequant_gather_arbitrary_payload(zs, bits, block, S):
+    """Payloads no quantizer writes: every code value (the 4-bit -8 and the
+    8-bit -128 included) under scales that are random, zero, negative, tiny
+    (products round to bf16 subnormals), huge (products overflow to
+    infinity), infinite and NaN of either sign; shards whose last 16-unit
+    group is cut short (the 4-bit decode's lookup groups)."""
+    import torch
+    world = 3
+    plan = zs.zs_shard_plan([world * S], world, 0, 1)
+    assert plan.shard_numel == S
+    rng = np.random.default_rng(block + S)
+    nq = zs.zs_quant_code_bytes(plan, bits)
+    ns = zs.zs_quant_num_scales(plan, block)
+    codes_all = rng.integers(0, 256, world * nq, dtype=np.uint8)
+    sc = (rng.standard_normal(world * ns) * 1e-3).astype(np.float32)
+    special = np.array([0.0, -0.0, -1e-3, 1e-40, 2e-38, 3.0e38, -3.0e38, np.inf, -np.inf], np.float32)
+    sc[:special.size] = special
+    sc[special.size] = np.float32(np.nan)
+    sc[special.size + 1] = np.frombuffer(np.uint32(0xFFC00001).tobytes(), np.float32)[0]  # negative NaN
+    rng.shuffle(sc[:4 * special.size])
+    full = torch.full((world * S + 64,), 0x5A5A, dtype=torch.int16, device="cuda")
+    zs.zs_dequant_gather(plan, bits, block, torch.from_numpy(codes_all).cuda(), dev32(sc), full)
+    ref = oracle.dequant_gather(codes_all, sc, S, world, bits, block)
+    got = host16(full)
+    assert check_bf16(got[:world * S], ref, "gathered") == 0
     assert np.all(got[world * S:] == 0x5A5A)
 
 
