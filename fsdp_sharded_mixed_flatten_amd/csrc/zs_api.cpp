@@ -212,12 +212,14 @@ zs_status zs_shard_plan_ex(const int64_t* numels, int32_t n_tensors, int32_t wor
             }
             static_assert(kMaxShardElems / zs::kChunkElems < INT32_MAX, "chunk count must fit the 32-bit grid");
             int64_t n_chunks = 0;
-            for (const auto& t : p->tensors) n_chunks += (t.own_hi - t.own_lo + zs::kChunkElems - 1) / zs::kChunkElems;
-            p->chunks.reserve((size_t)n_chunks);
+            for (auto& t : p->tensors) {
+                t.first_chunk = n_chunks;
+                n_chunks += (t.own_hi - t.own_lo + zs::kChunkElems - 1) / zs::kChunkElems;
+            }
+            p->chunk_piece.reserve((size_t)n_chunks);
             for (int32_t i = 0; i < n_tensors; ++i) {
-                const int64_t Si = p->tensors[(size_t)i].own_hi - p->tensors[(size_t)i].own_lo;
-                for (int64_t c = 0; c < Si; c += zs::kChunkElems)
-                    p->chunks.push_back(zs::Chunk{i, (int32_t)std::min<int64_t>(zs::kChunkElems, Si - c), c});
+                const zs::TensorEntry& t = p->tensors[(size_t)i];
+                for (int64_t c = 0; c < t.own_hi - t.own_lo; c += zs::kChunkElems) p->chunk_piece.push_back(i);
             }
         }
     } catch (const std::bad_alloc&) {
@@ -578,7 +580,7 @@ MultiLayout multi_layout(const zs_plan* p, int32_t n_contribs) {
     L.pieces_off = al((int64_t)sizeof(zs::MultiHeader));
     L.contribs_off = al(L.pieces_off + n * (int64_t)sizeof(zs::PieceDev));
     L.chunks_off = al(L.contribs_off + n * (int64_t)n_contribs * (int64_t)sizeof(void*));
-    L.total = al(L.chunks_off + (int64_t)p->chunks.size() * (int64_t)sizeof(zs::Chunk));
+    L.total = al(L.chunks_off + (int64_t)p->chunk_piece.size() * (int64_t)sizeof(int32_t));
     return L;
 }
 
@@ -677,7 +679,7 @@ zs_status zs_multi_bind(const zs_plan* plan, const zs_piece_ptrs* pieces, const 
     zs::MultiHeader* h = reinterpret_cast<zs::MultiHeader*>(host.data());
     h->magic = zs::kMultiMagic;
     h->n_pieces = n;
-    h->n_chunks = (int32_t)plan->chunks.size();
+    h->n_chunks = (int32_t)plan->chunk_piece.size();
     h->n_contribs = n_contribs;
     h->flags = flags;
     h->pieces_off = L.pieces_off;
@@ -696,10 +698,10 @@ zs_status zs_multi_bind(const zs_plan* plan, const zs_piece_ptrs* pieces, const 
         pd[i].full_own = pc.full ? static_cast<char*>(pc.full) + 2 * t.own_lo : nullptr;
         pd[i].len = t.own_hi - t.own_lo;
         pd[i].group = t.group;
-        pd[i].pad_ = 0;
+        pd[i].first_chunk = (int32_t)t.first_chunk;
         for (int32_t q = 0; q < n_contribs; ++q) cd[(int64_t)i * n_contribs + q] = contribs[(int64_t)q * n + i];
     }
-    std::memcpy(host.data() + L.chunks_off, plan->chunks.data(), plan->chunks.size() * sizeof(zs::Chunk));
+    std::memcpy(host.data() + L.chunks_off, plan->chunk_piece.data(), plan->chunk_piece.size() * sizeof(int32_t));
     if (zs_status st = hip_status(zs::copy_h2d_sync(workspace, host.data(), L.total, stream), "workspace copy"))
         return st;
     std::lock_guard<std::mutex> lk(g_bind_mu);
@@ -721,7 +723,7 @@ zs_status zs_reduce_shard_multi(const zs_plan* plan, const void* workspace, void
     if (zs_status st = check_multi_plan(plan)) return st;
     Binding b;
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasContribs | zs::kHasGrad, &b)) return st;
-    return hip_status(zs::launch_multi(zs::kOpReduce, nullptr, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunks.size(), b.n_contribs, stream),
+    return hip_status(zs::launch_multi(zs::kOpReduce, nullptr, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunk_piece.size(), b.n_contribs, stream),
                       "multi reduce launch");
 }
 
@@ -733,7 +735,7 @@ zs_status zs_adamw_shard_step_multi(const zs_plan* plan, const zs_adamw_hparams*
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasGrad | zs::kHasState, &b)) return st;
     zs::CoefTable ct;
     for (auto& e : ct.c) e = zs::make_coef(*hp);
-    return hip_status(zs::launch_multi(zs::kOpAdamw, &ct, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunks.size(), b.n_contribs, stream),
+    return hip_status(zs::launch_multi(zs::kOpAdamw, &ct, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunk_piece.size(), b.n_contribs, stream),
                       "multi adamw launch");
 }
 
@@ -741,7 +743,7 @@ zs_status zs_gather_params_multi(const zs_plan* plan, const void* workspace, voi
     if (zs_status st = check_multi_plan(plan)) return st;
     Binding b;
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasParam | zs::kHasFull, &b)) return st;
-    return hip_status(zs::launch_multi(zs::kOpGather, nullptr, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunks.size(), b.n_contribs, stream),
+    return hip_status(zs::launch_multi(zs::kOpGather, nullptr, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunk_piece.size(), b.n_contribs, stream),
                       "multi gather launch");
 }
 
@@ -753,7 +755,7 @@ zs_status zs_fused_shard_step_multi(const zs_plan* plan, const zs_adamw_hparams*
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasContribs | zs::kHasState, &b)) return st;
     zs::CoefTable ct;
     for (auto& e : ct.c) e = zs::make_coef(*hp);
-    return hip_status(zs::launch_multi(zs::kOpFused, &ct, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunks.size(), b.n_contribs, stream),
+    return hip_status(zs::launch_multi(zs::kOpFused, &ct, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunk_piece.size(), b.n_contribs, stream),
                       "multi fused launch");
 }
 
@@ -782,7 +784,7 @@ zs_status zs_adamw_shard_step_multi_groups(const zs_plan* plan, const zs_adamw_h
     if (zs_status st = group_table(plan, hps, n_groups, &ct)) return st;
     Binding b;
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasGrad | zs::kHasState, &b)) return st;
-    return hip_status(zs::launch_multi(zs::kOpAdamw, &ct, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunks.size(), b.n_contribs, stream),
+    return hip_status(zs::launch_multi(zs::kOpAdamw, &ct, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunk_piece.size(), b.n_contribs, stream),
                       "multi adamw launch");
 }
 
@@ -793,7 +795,7 @@ zs_status zs_fused_shard_step_multi_groups(const zs_plan* plan, const zs_adamw_h
     if (zs_status st = group_table(plan, hps, n_groups, &ct)) return st;
     Binding b;
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasContribs | zs::kHasState, &b)) return st;
-    return hip_status(zs::launch_multi(zs::kOpFused, &ct, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunks.size(), b.n_contribs, stream),
+    return hip_status(zs::launch_multi(zs::kOpFused, &ct, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunk_piece.size(), b.n_contribs, stream),
                       "multi fused launch");
 }
 

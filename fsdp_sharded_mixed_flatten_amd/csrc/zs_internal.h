@@ -30,13 +30,7 @@ struct TensorEntry {
     int64_t padded;    // PER_TENSOR: T_i; FLAT: numel
     int64_t own_lo, own_hi;  // owned range, tensor-local coordinates
     int64_t shard_off;       // start of the owned range in the packed shard
-};
-
-// One multi-tensor-apply chunk: `len` elements of piece `piece` from `start`.
-struct Chunk {
-    int32_t piece;
-    int32_t len;
-    int64_t start;
+    int64_t first_chunk = 0; // PER_TENSOR: index of the owned piece's first multi-tensor chunk
 };
 
 }  // namespace zs
@@ -49,7 +43,9 @@ struct zs_plan {
     int64_t T;  // padded flat length (PER_TENSOR: sum of T_i)
     int64_t S;  // owned elements (PER_TENSOR: sum of S_i)
     std::vector<zs::TensorEntry> tensors;
-    std::vector<zs::Chunk> chunks;  // multi-tensor chunk list of the owned pieces
+    // Multi-tensor chunks (kChunkElems owned elements each, the last of a
+    // piece shorter), in order: the piece each one belongs to.
+    std::vector<int32_t> chunk_piece;
 };
 
 namespace zs {
@@ -76,7 +72,7 @@ struct MultiHeader {
     int32_t flags;
     int64_t pieces_off;    // byte offset of PieceDev[n_pieces]
     int64_t contribs_off;  // byte offset of const void*[n_pieces * n_contribs]
-    int64_t chunks_off;    // byte offset of Chunk[n_chunks]
+    int64_t chunks_off;    // byte offset of int32_t[n_chunks]: each chunk's piece
 };
 
 struct PieceDev {
@@ -86,9 +82,9 @@ struct PieceDev {
     float* v;
     void* param;
     void* full_own;  // gathered tensor + r*S_i (already offset)
-    int64_t len;     // S_i
-    int32_t group;   // index into the kernel's coefficient table
-    int32_t pad_;
+    int64_t len;          // S_i
+    int32_t group;        // index into the kernel's coefficient table
+    int32_t first_chunk;  // chunk c of the piece covers [(c - first_chunk) * kChunkElems, ...)
 };
 
 enum MultiFlags : int32_t {

@@ -712,20 +712,23 @@ __global__ __launch_bounds__(kBlock) void k_multi(CoefTable ct, const MultiHeade
     static_assert(OP == kOpAdamw || OP == kOpFused, "reduce and gather have kernels of their own");
     if (hdr->magic != kMultiMagic) return;  // not a bound table (e.g. reused memory): touch nothing
     const char* ws = reinterpret_cast<const char*>(hdr);
-    const Chunk ch = reinterpret_cast<const Chunk*>(ws + off.chunks)[blockIdx.x];
-    const PieceDev pc = reinterpret_cast<const PieceDev*>(ws + off.pieces)[ch.piece];
+    const int32_t piece = reinterpret_cast<const int32_t*>(ws + off.chunks)[blockIdx.x];
+    const PieceDev pc = reinterpret_cast<const PieceDev*>(ws + off.pieces)[piece];
     const AdamCoef c = ct.c[pc.group];
     const int flags = hdr->flags;
-    const int64_t u0 = ch.start >> 2;  // chunk start and length are multiples of 8
+    // the chunk's range in its piece; piece lengths are multiples of 8
+    const int64_t start = (int64_t)((int32_t)blockIdx.x - pc.first_chunk) * kChunkElems;
+    const int64_t len = pc.len - start < kChunkElems ? pc.len - start : kChunkElems;
+    const int64_t u0 = start >> 2;
     const int64_t base = u0 + threadIdx.x;
-    const int64_t limit = u0 + (ch.len >> 2);
+    const int64_t limit = u0 + (len >> 2);
     if constexpr (OP == kOpAdamw) {
         adamw_tile<kMultiU>(c, reinterpret_cast<const u32x2*>(pc.grad), reinterpret_cast<f32x4*>(pc.master),
                             reinterpret_cast<f32x4*>(pc.m), reinterpret_cast<f32x4*>(pc.v),
                             (flags & kHasParam) ? reinterpret_cast<u32x2*>(pc.param) : nullptr, nullptr, base, limit);
     } else {
         const void* const* cps =
-            reinterpret_cast<const void* const*>(ws + off.contribs) + (int64_t)ch.piece * (N > 0 ? N : n_rt);
+            reinterpret_cast<const void* const*>(ws + off.contribs) + (int64_t)piece * (N > 0 ? N : n_rt);
         fused_tile<N, kMultiU>(c, cps, n_rt, nf, reinterpret_cast<f32x4*>(pc.master), reinterpret_cast<f32x4*>(pc.m),
                                reinterpret_cast<f32x4*>(pc.v),
                                (flags & kHasGrad) ? reinterpret_cast<u32x2*>(pc.grad) : nullptr,
@@ -749,33 +752,35 @@ __global__ __launch_bounds__(kBlock) void k_multi_gather(const MultiHeader* __re
                                                          int n_chunks) {
     if (hdr->magic != kMultiMagic) return;
     const char* ws = reinterpret_cast<const char*>(hdr);
-    const Chunk* chunks = reinterpret_cast<const Chunk*>(ws + moff.chunks);
+    const int32_t* cpiece = reinterpret_cast<const int32_t*>(ws + moff.chunks);
     const PieceDev* pieces = reinterpret_cast<const PieceDev*>(ws + moff.pieces);
     const int lane = threadIdx.x;
     const int64_t first = (int64_t)blockIdx.x * kGatherChunksPerBlock + lane / kGatherLanesPerChunk;
     const int off = (lane % kGatherLanesPerChunk) * 8;
-    // phase 1: every row's chunk record (rows past the end read chunk 0 and are dropped)
-    int32_t piece[kGatherRows], len[kGatherRows];
-    int64_t start[kGatherRows];
+    // phase 1: every row's chunk and piece (rows past the end take chunk 0 and are dropped)
+    int32_t chunk[kGatherRows], piece[kGatherRows];
 #pragma unroll
     for (int r = 0; r < kGatherRows; ++r) {
         const int64_t c = first + (int64_t)r * kGatherChunksPerRow;
-        const Chunk* ch = chunks + (c < n_chunks ? c : 0);
-        piece[r] = ld_g(&ch->piece);
-        len[r] = c < n_chunks ? ld_g(&ch->len) : 0;
-        start[r] = ld_g(&ch->start);
+        chunk[r] = c < n_chunks ? (int32_t)c : 0;
+        piece[r] = ld_g(cpiece + chunk[r]);
     }
-    // phase 2: the pieces' pointers. A lane past its chunk's end reads the
+    // phase 2: the pieces' records. A lane past its chunk's end reads the
     // chunk's first vector instead (always inside the piece) and stores nothing,
     // so the loads below need no branch.
     const char* src[kGatherRows];
     char* dst[kGatherRows];
+    int64_t len[kGatherRows];
 #pragma unroll
     for (int r = 0; r < kGatherRows; ++r) {
         const PieceDev* pc = pieces + piece[r];
+        const int64_t start = (int64_t)(chunk[r] - ld_g(&pc->first_chunk)) * kChunkElems;
+        const int64_t rest = ld_g(&pc->len) - start;
+        const int64_t c = first + (int64_t)r * kGatherChunksPerRow;
+        len[r] = c < n_chunks ? (rest < kChunkElems ? rest : kChunkElems) : 0;
         const int o = off < len[r] ? off : 0;
-        src[r] = static_cast<const char*>(ld_g(&pc->param)) + 2 * (start[r] + o);
-        dst[r] = static_cast<char*>(ld_g(&pc->full_own)) + 2 * (start[r] + off);
+        src[r] = static_cast<const char*>(ld_g(&pc->param)) + 2 * (start + o);
+        dst[r] = static_cast<char*>(ld_g(&pc->full_own)) + 2 * (start + off);
     }
     // phase 3: loads, then stores
     u32x4 x[kGatherRows];
@@ -800,26 +805,31 @@ __global__ __launch_bounds__(kBlock) void k_multi_reduce(const MultiHeader* __re
                                                          int n_chunks, int n_rt, float nf) {
     if (hdr->magic != kMultiMagic) return;
     const char* ws = reinterpret_cast<const char*>(hdr);
-    const Chunk* chunks = reinterpret_cast<const Chunk*>(ws + moff.chunks);
+    const int32_t* cpiece = reinterpret_cast<const int32_t*>(ws + moff.chunks);
     const PieceDev* pieces = reinterpret_cast<const PieceDev*>(ws + moff.pieces);
     const void* const* cps = reinterpret_cast<const void* const*>(ws + moff.contribs);
     const int nq = N > 0 ? N : n_rt;
     const int lane = threadIdx.x;
     const int64_t first = (int64_t)blockIdx.x * kReduceChunksPerBlock + lane / kGatherLanesPerChunk;
     const int off = (lane % kGatherLanesPerChunk) * 8;
-    int32_t piece[kReduceRows], len[kReduceRows];
-    int64_t start[kReduceRows];
+    int32_t chunk[kReduceRows], piece[kReduceRows];
 #pragma unroll
     for (int r = 0; r < kReduceRows; ++r) {
         const int64_t c = first + (int64_t)r * kGatherChunksPerRow;
-        const Chunk* ch = chunks + (c < n_chunks ? c : 0);
-        piece[r] = ld_g(&ch->piece);
-        len[r] = c < n_chunks ? ld_g(&ch->len) : 0;
-        start[r] = ld_g(&ch->start);
+        chunk[r] = c < n_chunks ? (int32_t)c : 0;
+        piece[r] = ld_g(cpiece + chunk[r]);
     }
     char* grad[kReduceRows];
+    int64_t start[kReduceRows], len[kReduceRows];
 #pragma unroll
-    for (int r = 0; r < kReduceRows; ++r) grad[r] = static_cast<char*>(ld_g(&pieces[piece[r]].grad));
+    for (int r = 0; r < kReduceRows; ++r) {
+        const PieceDev* pc = pieces + piece[r];
+        grad[r] = static_cast<char*>(ld_g(&pc->grad));
+        start[r] = (int64_t)(chunk[r] - ld_g(&pc->first_chunk)) * kChunkElems;
+        const int64_t rest = ld_g(&pc->len) - start[r];
+        const int64_t c = first + (int64_t)r * kGatherChunksPerRow;
+        len[r] = c < n_chunks ? (rest < kChunkElems ? rest : kChunkElems) : 0;
+    }
 #pragma unroll
     for (int r = 0; r < kReduceRows; ++r) {
         // a lane past its chunk's end sums the chunk's first vector (inside the
