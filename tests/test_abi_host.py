@@ -266,3 +266,63 @@ def test_plan_workspace_bytes(zs):
     assert pt.workspace_bytes == zs.zs_multi_workspace_bytes(pt, 8) > 0
     assert zs.zs_shard_plan([4096], 8, 0).workspace_bytes == 0
     assert zs.lib().zs_plan_workspace_bytes(None) == -1
+
+
+def test_last_error_is_per_thread(zs):
+    """Failing calls from several threads at once: each thread reads back the
+    message of its own call, never another thread's."""
+    import threading
+    n = 8
+    barrier = threading.Barrier(n)
+    seen = [None] * n
+
+    def work(i):
+        for rep in range(20):
+            bad_rank = 1000 + 100 * i + rep
+            barrier.wait()
+            status = zs.lib().zs_shard_plan((ctypes.c_int64 * 1)(16), 1, 4, bad_rank, 1, 0,
+                                            ctypes.byref(ctypes.c_void_p()))
+            barrier.wait()  # every thread has failed before any reads its message
+            msg = zs.zs_last_error()
+            if status != zs.ZS_EINVAL or f"rank = {bad_rank}" not in msg:
+                seen[i] = (rep, status, msg)
+                return
+        seen[i] = "ok"
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(n)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=60)
+    assert seen == ["ok"] * n, seen
+
+
+def test_plans_built_concurrently(zs):
+    """Plans built in parallel threads equal the ones built one at a time."""
+    import threading
+    rng = random.Random(3)
+    cases = []
+    for _ in range(32):
+        w = rng.randint(1, 64)
+        cases.append(([rng.randint(1, 100_000) for _ in range(rng.randint(1, 40))], w, rng.randrange(w),
+                      rng.randint(0, 1)))
+
+    def describe(plan):
+        infos = [plan.tensor(i) for i in range(plan.num_tensors)]
+        return (plan.padded_numel, plan.shard_numel, plan.workspace_bytes,
+                [(t.numel, t.flat_off, t.padded_numel, t.own_lo, t.own_hi, t.shard_off) for t in infos])
+
+    want = [describe(zs.zs_shard_plan(n, w, r, 1, lay)) for n, w, r, lay in cases]
+    got = [None] * len(cases)
+
+    def work(k):
+        for j in range(k, len(cases), 4):
+            n, w, r, lay = cases[j]
+            got[j] = describe(zs.zs_shard_plan(n, w, r, 1, lay))
+
+    threads = [threading.Thread(target=work, args=(k,)) for k in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=60)
+    assert got == want
