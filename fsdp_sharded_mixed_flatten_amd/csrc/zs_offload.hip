@@ -28,7 +28,8 @@ namespace {
 struct DeviceCtx {
     hipStream_t out = nullptr;
     std::vector<hipEvent_t> events;  // grown on demand, reused across calls
-    hipEvent_t done = nullptr;
+    hipEvent_t done = nullptr;       // the last call's final copy-out
+    bool recorded = false;           // `done` has been recorded at least once
 };
 
 std::mutex g_ctx_mu;
@@ -75,6 +76,11 @@ int offload_adamw(const AdamCoef& c, const void* grad_dev, float* master, float*
     const char* gd = static_cast<const char*>(grad_dev);
     char* gh = static_cast<char*>(grad_host);
     char* ph = static_cast<char*>(param_host);
+    // The previous call's copy-outs may still read its staging buffers, which
+    // this call's host arithmetic overwrites; its caller waited for them, but
+    // this call may come on another stream: order this stream after them too.
+    if (ctx->recorded)
+        if (hipError_t e = hipStreamWaitEvent(stream, ctx->done, 0)) return (int)e;
     for (int64_t k = 0; k < n_chunks; ++k) {
         const int64_t off = k * chunk, n = off + chunk < len ? chunk : len - off;
         if (hipError_t e = hipMemcpyAsync(gh + 2 * off, gd + 2 * off, (size_t)(2 * n), hipMemcpyDeviceToHost, stream))
@@ -96,6 +102,7 @@ int offload_adamw(const AdamCoef& c, const void* grad_dev, float* master, float*
                 return (int)e;
     }
     if (hipError_t e = hipEventRecord(ctx->done, ctx->out)) return (int)e;
+    ctx->recorded = true;
     return (int)hipStreamWaitEvent(stream, ctx->done, 0);
 }
 

@@ -65,6 +65,51 @@ def test_offload_step_equals_oracle(zs, chunk, threads):
         assert np.array_equal(host16(full), o["full"]), "gathered buffer"
 
 
+def test_offload_steps_on_alternating_streams(zs):
+    """Consecutive steps on different streams, with no synchronization between
+    them: each step's host arithmetic overwrites the staging buffers the
+    previous step's copy-outs read, so a step must wait for those copies even
+    when its stream never saw them."""
+    import torch
+    world, rank, chunk = 2, 1, 2048
+    numels = [262_147]
+    plan = zs.zs_shard_plan(numels, world, rank, 1)
+    S, T = plan.shard_numel, plan.padded_numel
+    lo = rank * S
+    master0 = synth.cpu_f32(T, 0, synth.spec(72, synth.STREAM_MASTER, 0, 0.02, numels[0]))[lo:lo + S].copy()
+    hm, hmm, hv = _pinned(S, torch.float32), _pinned(S, torch.float32), _pinned(S, torch.float32)
+    hm.copy_(torch.from_numpy(master0))
+    gh, ph = _pinned(S, torch.int16), _pinned(S, torch.int16)
+    o = dict(g=np.zeros(S, np.uint16), master=master0.copy(), m=np.zeros(S, np.float32), v=np.zeros(S, np.float32),
+             p=np.zeros(S, np.uint16), full=np.full(T, SENT, np.uint16))
+    full = dev16(np.full(T, SENT, np.uint16))
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    steps = 4
+    cs = {t: [synth.cpu_bf16(T, 0, synth.spec(72, synth.STREAM_CONTRIB + q, t, 1e-3, numels[0]))[lo:lo + S].copy()
+              for q in range(world)] for t in range(1, steps + 1)}
+    dcs = {t: [dev16(c) for c in cs[t]] for t in cs}
+    gds = [torch.zeros(S, dtype=torch.int16, device="cuda") for _ in range(steps)]
+    pds = [torch.zeros(S, dtype=torch.int16, device="cuda") for _ in range(steps)]
+    want_p = []
+    torch.cuda.synchronize()
+    for t in range(1, steps + 1):
+        s = streams[t % len(streams)]
+        hp = zs.AdamWHParams(lr=2e-4, weight_decay=0.1, step=t)
+        zs.zs_reduce_shard(plan, dcs[t], gds[t - 1], stream=s)
+        zs.zs_offload_adamw_step(plan, hp, gds[t - 1], hm, hmm, hv, gh, ph, param_dev=pds[t - 1], full_dev=full,
+                                 chunk_elems=chunk, n_threads=4, stream=s)
+        oracle.shard_step(oracle.HParams(lr=2e-4, weight_decay=0.1, step=t), cs[t], o["g"], o["master"], o["m"],
+                          o["v"], o["p"], o["full"], rank)
+        want_p.append(o["p"].copy())  # each step copies its parameters into a device buffer of its own
+    torch.cuda.synchronize()
+    for t in range(1, steps + 1):
+        assert check_bf16(host16(pds[t - 1]), want_p[t - 1], f"param on device, step {t}") == 0
+    nd = check_f32(hm.numpy(), o["master"], "master") + check_f32(hmm.numpy(), o["m"], "m")
+    nd += check_f32(hv.numpy(), o["v"], "v")
+    assert nd == 0
+    assert np.array_equal(host16(full), o["full"]), "gathered buffer"
+
+
 def test_offload_rejects_pageable_staging(zs):
     import torch
     plan = zs.zs_shard_plan([8192], 2, 0)
