@@ -343,7 +343,9 @@ zs_status zs_host_adamw_step(const zs_adamw_hparams* hp, const void* grad_bf16, 
  * param_bf16_host must be page-locked (hipHostMalloc or pinned tensors);
  * chunk_elems is a multiple of 8, at least 1024. The call returns once the
  * host arithmetic is done (it waits on the copies it needs). Calls are
- * serialized process-wide. Unlike the other calls, a ZS_EHIP return in the
+ * serialized process-wide, and each call's work on `stream` is ordered after
+ * the previous call's copies to the device (whose staging buffer it reuses),
+ * whatever stream that call used. Unlike the other calls, a ZS_EHIP return in the
  * middle of the pipeline may leave a prefix of the chunks updated. */
 zs_status zs_offload_adamw_step(const zs_plan* plan, const zs_adamw_hparams* hp, const void* grad_bf16_dev,
                                 float* master_host, float* m_host, float* v_host, void* grad_bf16_host,
