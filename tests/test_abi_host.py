@@ -277,23 +277,28 @@ def test_last_error_is_per_thread(zs):
     seen = [None] * n
 
     def work(i):
-        for rep in range(20):
-            bad_rank = 1000 + 100 * i + rep
-            barrier.wait()
-            status = zs.lib().zs_shard_plan((ctypes.c_int64 * 1)(16), 1, 4, bad_rank, 1, 0,
-                                            ctypes.byref(ctypes.c_void_p()))
-            barrier.wait()  # every thread has failed before any reads its message
-            msg = zs.zs_last_error()
-            if status != zs.ZS_EINVAL or f"rank = {bad_rank}" not in msg:
-                seen[i] = (rep, status, msg)
-                return
-        seen[i] = "ok"
+        try:
+            for rep in range(20):
+                bad_rank = 1000 + 100 * i + rep
+                barrier.wait(timeout=30)
+                status = zs.lib().zs_shard_plan((ctypes.c_int64 * 1)(16), 1, 4, bad_rank, 1, 0,
+                                                ctypes.byref(ctypes.c_void_p()))
+                barrier.wait(timeout=30)  # every thread has failed before any reads its message
+                msg = zs.zs_last_error()
+                if status != zs.ZS_EINVAL or f"rank = {bad_rank}" not in msg:
+                    seen[i] = (rep, status, msg)
+                    barrier.abort()
+                    return
+            seen[i] = "ok"
+        except threading.BrokenBarrierError:
+            seen[i] = "barrier broken"
 
     threads = [threading.Thread(target=work, args=(i,)) for i in range(n)]
     for th in threads:
         th.start()
     for th in threads:
-        th.join(timeout=60)
+        th.join(timeout=120)
+        assert not th.is_alive()
     assert seen == ["ok"] * n, seen
 
 
@@ -324,5 +329,6 @@ def test_plans_built_concurrently(zs):
     for th in threads:
         th.start()
     for th in threads:
-        th.join(timeout=60)
+        th.join(timeout=120)
+        assert not th.is_alive()
     assert got == want

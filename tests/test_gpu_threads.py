@@ -66,10 +66,10 @@ def test_threads_with_own_streams(zs):
                         zs.zs_multi_unbind(ws)
                     # a failing call: the message must name this thread's arguments
                     bad_rank = 1000 + 10 * i + t
-                    barrier.wait()
+                    barrier.wait(timeout=60)
                     with pytest.raises(zs.ZsError) as e:
                         zs.zs_shard_plan([16], 4, bad_rank)
-                    barrier.wait()
+                    barrier.wait(timeout=60)
                     assert f"rank = {bad_rank}" in zs.zs_last_error(), zs.zs_last_error()
                     assert f"rank = {bad_rank}" in e.value.message
                 stream.synchronize()
