@@ -209,6 +209,47 @@ def test_fused_equals_unfused_bit_exact(zs):
         assert np.array_equal(a.d[k].cpu().numpy(), b.d[k].cpu().numpy()), k
 
 
+@pytest.mark.parametrize("N", [4, 64])
+@pytest.mark.parametrize("outs", range(8), ids=lambda o: f"grad{o & 1}-param{(o >> 1) & 1}-full{(o >> 2) & 1}")
+def test_fused_optional_outputs(zs, N, outs):
+    """Every subset of the fused step's optional outputs (grad shard, param
+    shard, gathered slice), in the one-pass form (N=4) and at N=64, where
+    the step runs as two passes when the grad shard is written: enabled
+    outputs equal the oracle's, disabled ones keep their sentinel bytes."""
+    import torch
+    want_g, want_p, want_f = bool(outs & 1), bool(outs & 2), bool(outs & 4)
+    run = FlatRun(zs, [40_003, 77], N, N - 1, 1, 2, 300 + outs, _hp(zs), fused=True)
+    S, T = run.S, run.T
+    for buf in ("g", "p", "full"):
+        run.d[buf].fill_(SENT)
+    d = run.d
+    for t in (1, 2):
+        hp = run.hp.at(t)
+        zs.zs_fused_shard_step(run.plan, hp, run.dc[t], d["master"], d["m"], d["v"], grad=d["g"] if want_g else None,
+                               param=d["p"] if want_p else None, full=d["full"] if want_f else None)
+        o = run.o
+        oracle.shard_step(oracle.HParams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, t), run.mine[t],
+                          o["g"], o["master"], o["m"], o["v"], o["p"], o["full"], run.rank)
+    torch.cuda.synchronize()
+    nd = check_f32(host32(d["master"])[:S], o["master"], "master") + check_f32(host32(d["m"])[:S], o["m"], "m")
+    nd += check_f32(host32(d["v"])[:S], o["v"], "v")
+    g, p, full = host16(d["g"]), host16(d["p"]), host16(d["full"])
+    if want_g:
+        nd += check_bf16(g[:S], o["g"], "grad")
+    else:
+        assert np.all(g == SENT), "grad written although not requested"
+    if want_p:
+        nd += check_bf16(p[:S], o["p"], "param")
+    else:
+        assert np.all(p == SENT), "param written although not requested"
+    if want_f:
+        assert np.array_equal(full[:T], o["full"]), "gathered buffer"
+    else:
+        assert np.all(full == SENT), "gathered buffer written although not requested"
+    assert np.all(g[S:] == SENT) and np.all(p[S:] == SENT) and np.all(full[T:] == SENT), "guard bands"
+    assert nd == 0
+
+
 def test_edge_values(zs):
     """Signed zeros, subnormals, huge values, inf and NaN in the contributions."""
     import torch
