@@ -135,6 +135,50 @@ def test_non_finite_skips_step(zs):
     assert oracle.grad_sumsq(o)[1] == 1
 
 
+@pytest.mark.parametrize("divisor", [2.0, 3.0])
+@pytest.mark.parametrize("outs", range(4), ids=lambda o: f"param{o & 1}-full{o >> 1}")
+def test_accum_step_without_clipping(zs, divisor, outs):
+    """The step from the accumulator with no clip factor and no skip flag
+    (NULL: factor 1, never skipped), a divisor other than the number of
+    micro-steps, and each subset of the optional outputs; disabled outputs
+    keep their sentinels."""
+    import torch
+    numels, N, r, G = [200_003], 4, 3, 2
+    plan = zs.zs_shard_plan(numels, N, r, 1)
+    T, S = plan.padded_numel, plan.shard_numel
+    micro = [_contribs(T, N, k + 1, 77, numels[0]) for k in range(G)]
+    master0 = synth.cpu_f32(T, 0, synth.spec(77, synth.STREAM_MASTER, 0, 0.02, numels[0]))[r * S:(r + 1) * S].copy()
+    acc = torch.zeros(S, device="cuda")
+    for k in range(G):
+        zs.zs_accumulate_shard(plan, [dev16(c[r * S:(r + 1) * S]) for c in micro[k]], acc, first=(k == 0))
+    master, m, v = dev32(master0), torch.zeros(S, device="cuda"), torch.zeros(S, device="cuda")
+    param = dev16(np.full(S + 64, 0x5A5A, np.uint16))
+    full = dev16(np.full(T + 64, 0x5A5A, np.uint16))
+    hp = zs.AdamWHParams(lr=1e-3, weight_decay=0.1, step=1)
+    zs.zs_adamw_shard_step_accum(plan, hp, acc, divisor, master, m, v, param=param if outs & 1 else None,
+                                 full=full if outs & 2 else None)
+    torch.cuda.synchronize()
+    o_acc = np.zeros(S, np.float32)
+    for k in range(G):
+        oracle.accumulate([c[r * S:(r + 1) * S].copy() for c in micro[k]], o_acc, first=(k == 0))
+    om, ov, op = np.zeros(S, np.float32), np.zeros(S, np.float32), np.zeros(S, np.uint16)
+    omaster = master0.copy()
+    oracle.adamw_f32grad(oracle.HParams(1e-3, 0.9, 0.95, 1e-8, 0.1, 1), o_acc, divisor, 1.0, False, omaster, om, ov,
+                         op)
+    nd = check_f32(host32(master), omaster, "master") + check_f32(host32(m), om, "m") + check_f32(host32(v), ov, "v")
+    p, f = host16(param), host16(full)
+    if outs & 1:
+        nd += check_bf16(p[:S], op, "param")
+        assert np.all(p[S:] == 0x5A5A)
+    else:
+        assert np.all(p == 0x5A5A)
+    f_o = np.full(T + 64, 0x5A5A, np.uint16)
+    if outs & 2:
+        f_o[r * S:(r + 1) * S] = op
+    assert np.array_equal(f, f_o), "gathered buffer"
+    assert nd == 0
+
+
 def test_stats_deterministic(zs):
     import torch
     plan = zs.zs_shard_plan([3_000_000 * 8], 8, 0, 1)
