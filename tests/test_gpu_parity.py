@@ -423,6 +423,50 @@ def test_multi_tensor_apply(zs, fused):
         run.check()
 
 
+@pytest.mark.parametrize("outs", range(8), ids=lambda o: f"grad{o & 1}-param{(o >> 1) & 1}-full{(o >> 2) & 1}")
+def test_multi_tensor_fused_optional_fields(zs, outs):
+    """The fused multi-tensor step bound with every subset of its optional
+    fields (grad, param, gathered tensor): bound outputs equal the oracle's,
+    unbound ones are never written."""
+    import torch
+    run = MultiRun(zs, _small_model(), 8, 5, 2, 90 + outs, _hp(zs))
+    keep = dict(grad=bool(outs & 1), param=bool(outs & 2), full=bool(outs & 4))
+    for d in run.pieces:
+        for k in keep:
+            d[k].fill_(SENT)
+    for t in (1, 2):
+        ws = torch.zeros(zs.zs_multi_workspace_bytes(run.plan, run.n_contribs), dtype=torch.uint8, device="cuda")
+        zs.zs_multi_bind(run.plan, [{k: (v if keep.get(k, True) else None) for k, v in d.items()}
+                                    for d in run.pieces], run.dcontribs[t], ws)
+        zs.zs_fused_shard_step_multi(run.plan, run.hp.at(t), ws)
+        h = oracle.HParams(run.hp.lr, run.hp.beta1, run.hp.beta2, run.hp.eps, run.hp.weight_decay, t)
+        for i, pc in enumerate(run.oplan.pieces):
+            o = run.o[i]
+            cs = [run.contribs[t][q][i] for q in range(run.n_contribs)]
+            oracle.reduce(cs, out=o["g"])
+            oracle.adamw(h, o["g"], o["master"], o["m"], o["v"], o["p"])
+            o["full"][pc.own_lo:pc.own_hi] = o["p"]
+    torch.cuda.synchronize()
+    nd = 0
+    for i, (o, d) in enumerate(zip(run.o, run.pieces)):
+        nd += check_f32(host32(d["master"]), o["master"], f"master[{i}]")
+        nd += check_f32(host32(d["m"]), o["m"], f"m[{i}]") + check_f32(host32(d["v"]), o["v"], f"v[{i}]")
+        g, p, f = host16(d["grad"]), host16(d["param"]), host16(d["full"])
+        if keep["grad"]:
+            nd += check_bf16(g, o["g"], f"grad[{i}]")
+        else:
+            assert np.all(g == SENT), f"grad[{i}] written although not bound"
+        if keep["param"]:
+            nd += check_bf16(p, o["p"], f"param[{i}]")
+        else:
+            assert np.all(p == SENT), f"param[{i}] written although not bound"
+        if keep["full"]:
+            assert np.array_equal(f, o["full"]), f"gathered tensor {i}"
+        else:
+            assert np.all(f == SENT), f"gathered tensor {i} written although not bound"
+    assert nd == 0
+
+
 def test_multi_tensor_unbound_workspace_is_inert(zs):
     """A workspace whose table was unbound, or whose memory was overwritten
     after binding, launches nothing that touches the pieces."""
