@@ -44,12 +44,15 @@
  *
  * Execution: every zs_* call that touches device memory only validates its
  * arguments on the host and enqueues kernels on `stream` (a hipStream_t; NULL
- * is the default stream). It never synchronizes; a device-side fault is seen
- * at the caller's next synchronization. Calls on different streams that
- * write the same memory race.
+ * is the default stream). It never synchronizes (exceptions, documented
+ * below: zs_multi_bind and zs_multi_unbind, which copy into their workspace,
+ * and zs_offload_adamw_step, which waits for the copies its host arithmetic
+ * needs); a device-side fault is seen at the caller's next synchronization.
+ * Calls on different streams that write the same memory race.
  *
  * Errors: a call that returns anything but ZS_OK has enqueued nothing and
- * changed nothing; zs_last_error() then returns a thread-local description.
+ * changed nothing (except a ZS_EHIP in the middle of zs_offload_adamw_step's
+ * pipeline); zs_last_error() then returns a thread-local description.
  */
 #ifndef ZS_H
 #define ZS_H
