@@ -417,6 +417,22 @@ def main():
                                        "bytes_per_param": unfused_bytes_per_param(N),
                                        "launches_per_step": (S + B - 1) // B + 2,
                                        "reduce_buckets": (S + B - 1) // B}
+            if B < S:
+                # the fused step bucket by bucket, as it would run behind a bucketed exchange
+                def fused_buckets(t, timer):
+                    e = timer.start() if timer else None
+                    for off in range(0, S, B):
+                        zs.zs_fused_shard_step_bucket(plan, hp0.at(t), st["contribs"], st["master"], st["m"],
+                                                      st["v"], off, min(B, S - off), grad=grad_out, full=st["full"])
+                    if timer:
+                        timer.stop(e)
+
+                b_wall, b_dev, b_ev = time_loop(fused_buckets, 1, max(3, args.steps // 2))
+                result_paths["fused_bucketed"] = {"ms_per_step": b_wall, "device_ms_per_step": b_dev,
+                                                  "events_ms_median": statistics.median(b_ev),
+                                                  "bytes_per_param": bpp,
+                                                  "gbps": S * bpp / (b_dev / 1e3) / 1e9,
+                                                  "buckets": (S + B - 1) // B}
         if args.quant != "none":
             bits, qblock = (int(x) for x in args.quant.split(":"))
             nq, ns = zs.zs_quant_code_bytes(plan, bits), zs.zs_quant_num_scales(plan, qblock)

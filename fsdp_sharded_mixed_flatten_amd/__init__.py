@@ -90,6 +90,8 @@ def _load():
         "zs_gather_params": (st, [vp, vp, vp, vp]),
         "zs_fused_shard_step": (st, [vp, ctypes.POINTER(AdamWHParams), ctypes.POINTER(vp), i32, vp, vp,
                                      vp, vp, vp, vp, vp]),
+        "zs_fused_shard_step_bucket": (st, [vp, ctypes.POINTER(AdamWHParams), ctypes.POINTER(vp), i32, vp, vp,
+                                            vp, vp, vp, vp, i64, i64, vp]),
         "zs_multi_workspace_bytes": (i64, [vp, i32]),
         "zs_plan_workspace_bytes": (i64, [vp]),
         "zs_multi_bind": (st, [vp, ctypes.POINTER(PiecePtrs), ctypes.POINTER(vp), i32, vp, i64, vp]),
@@ -130,7 +132,8 @@ EXPORTED = ("zs_shard_plan", "zs_shard_plan_ex", "zs_plan_tensor_group", "zs_pla
             "zs_plan_destroy", "zs_plan_padded_numel", "zs_plan_shard_numel",
             "zs_plan_persistent_bytes", "zs_plan_num_tensors", "zs_plan_world_size", "zs_plan_rank",
             "zs_plan_layout", "zs_plan_tensor", "zs_reduce_shard", "zs_adamw_shard_step",
-            "zs_gather_params", "zs_fused_shard_step", "zs_multi_workspace_bytes", "zs_plan_workspace_bytes",
+            "zs_gather_params", "zs_fused_shard_step", "zs_fused_shard_step_bucket", "zs_multi_workspace_bytes",
+            "zs_plan_workspace_bytes",
             "zs_multi_bind", "zs_multi_unbind",
             "zs_reduce_shard_multi", "zs_adamw_shard_step_multi", "zs_gather_params_multi",
             "zs_fused_shard_step_multi", "zs_adamw_shard_step_multi_groups",
@@ -329,6 +332,19 @@ def zs_fused_shard_step(plan, hp, contribs, master, m, v, grad=None, param=None,
                                     _ptr(v, "f32", S, "v"), _ptr(grad, "bf16", S, "grad"),
                                     _ptr(param, "bf16", S, "param"),
                                     _ptr(full, "bf16", (r + 1) * S, "full"), _stream(stream)))
+
+
+def zs_fused_shard_step_bucket(plan, hp, contribs, master, m, v, off=0, length=None, grad=None, param=None,
+                               full=None, stream=None):
+    S, r = plan.shard_numel, plan.rank
+    length = S - off if length is None else length
+    end = min(max(off + length, 0), S)  # a bucket outside the shard is the library's ZS_ERANGE
+    ptrs = [_ptr(c, "bf16", end, f"contribs[{q}]") for q, c in enumerate(contribs)]
+    _check(_lib.zs_fused_shard_step_bucket(plan.handle, ctypes.byref(hp), _ptr_array(ptrs), len(ptrs),
+                                           _ptr(master, "f32", end, "master"), _ptr(m, "f32", end, "m"),
+                                           _ptr(v, "f32", end, "v"), _ptr(grad, "bf16", end, "grad"),
+                                           _ptr(param, "bf16", end, "param"),
+                                           _ptr(full, "bf16", r * S + end, "full"), off, length, _stream(stream)))
 
 
 # ---------------------------------------------------------------- quantized parameter gather

@@ -335,6 +335,14 @@ zs_status zs_fused_shard_step(const zs_plan* plan, const zs_adamw_hparams* hp, c
                               int32_t n_contribs, float* master, float* m, float* v, void* grad_bf16,
                               void* param_bf16, void* full_bf16, void* stream) {
     if (zs_status st = check_plan(plan)) return st;
+    return zs_fused_shard_step_bucket(plan, hp, contribs, n_contribs, master, m, v, grad_bf16, param_bf16, full_bf16,
+                                      0, plan->S, stream);
+}
+
+zs_status zs_fused_shard_step_bucket(const zs_plan* plan, const zs_adamw_hparams* hp, const void* const* contribs,
+                                     int32_t n_contribs, float* master, float* m, float* v, void* grad_bf16,
+                                     void* param_bf16, void* full_bf16, int64_t off, int64_t len, void* stream) {
+    if (zs_status st = check_plan(plan)) return st;
     if (zs_status st = check_hp(hp)) return st;
     if (zs_status st = check_contribs(plan, contribs, n_contribs)) return st;
     if (zs_status st = check_ptr(master, "master")) return st;
@@ -346,10 +354,16 @@ zs_status zs_fused_shard_step(const zs_plan* plan, const zs_adamw_hparams* hp, c
     if (full_bf16 && plan->layout != ZS_LAYOUT_FLAT)
         return fail(ZS_EINVAL, "a gather into full_bf16 needs a FLAT plan; PER_TENSOR plans use "
                                "zs_fused_shard_step_multi");
-    if (plan->S == 0) return ZS_OK;
-    char* own = full_bf16 ? static_cast<char*>(full_bf16) + 2 * (int64_t)plan->rank * plan->S : nullptr;
-    return hip_status(zs::launch_fused(zs::make_coef(*hp), contribs, n_contribs, master, m, v, grad_bf16,
-                                       param_bf16, own, plan->S, stream),
+    if (off < 0 || len < 0 || off % 8 || len % 8 || off > plan->S || len > plan->S - off)
+        return fail(ZS_ERANGE, "bucket [%lld, %lld) must be multiples of 8 inside the shard [0, %lld)",
+                    (long long)off, (long long)(off + len), (long long)plan->S);
+    if (len == 0) return ZS_OK;
+    const void* shifted[ZS_MAX_CONTRIBS];
+    for (int32_t q = 0; q < n_contribs; ++q) shifted[q] = static_cast<const char*>(contribs[q]) + 2 * off;
+    auto at16 = [off](void* p) { return p ? static_cast<void*>(static_cast<char*>(p) + 2 * off) : nullptr; };
+    char* own = full_bf16 ? static_cast<char*>(full_bf16) + 2 * ((int64_t)plan->rank * plan->S + off) : nullptr;
+    return hip_status(zs::launch_fused(zs::make_coef(*hp), shifted, n_contribs, master + off, m + off, v + off,
+                                       at16(grad_bf16), at16(param_bf16), own, len, stream),
                       "fused launch");
 }
 

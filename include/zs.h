@@ -216,6 +216,22 @@ zs_status zs_fused_shard_step(const zs_plan* plan, const zs_adamw_hparams* hp,
                               float* m, float* v, void* grad_bf16, void* param_bf16,
                               void* full_bf16, void* stream);
 
+/* zs_fused_shard_step over the bucket [off, off+len) of the shard only, with
+ * zs_reduce_shard's bucket rules (off and len multiples of 8, off + len <= S,
+ * len == 0 does nothing). The buffers are the whole-shard ones: bucket
+ * element j is element off + j of every contribution, of master/m/v and of
+ * grad_bf16/param_bf16, and is written to full_bf16[r*S + off + j]. Buckets
+ * give the same bytes as one call over the whole shard, so the step of a
+ * bucket can run as soon as its contributions have arrived, while later
+ * buckets are still being exchanged (reduce-scatter bucketed as gradients
+ * become ready: "从 Data Parallel 到 ZeRO/FSDP", section "ReduceScatter 必须尽早
+ * 释放 Gradient"); without global-norm clipping AdamW needs nothing from
+ * the other buckets. */
+zs_status zs_fused_shard_step_bucket(const zs_plan* plan, const zs_adamw_hparams* hp,
+                                     const void* const* contribs, int32_t n_contribs, float* master, float* m,
+                                     float* v, void* grad_bf16, void* param_bf16, void* full_bf16, int64_t off,
+                                     int64_t len, void* stream);
+
 /* ------------------------------------------------------------------ multi-tensor
  * Multi-tensor apply over the owned pieces of a PER_TENSOR plan whose
  * per-tensor state lives in separate allocations (FSDP2's per-parameter

@@ -205,6 +205,14 @@ def test_validation_without_device(zs):
     assert L.zs_adamw_shard_step(h, ctypes.byref(hp), FAKE, FAKE + 8, FAKE, FAKE, FAKE, None) == zs.ZS_EALIGN
     assert L.zs_gather_params(h, FAKE, None, None) == zs.ZS_EINVAL
     assert L.zs_fused_shard_step(h, ctypes.byref(hp), good, 4, FAKE, FAKE, FAKE, FAKE + 1, None, None, None) == zs.ZS_EALIGN
+    # fused step over a bucket: zs_reduce_shard's bucket rules
+    fb = L.zs_fused_shard_step_bucket
+    for off, n in ((0, S + 8), (4, 8), (-8, 8), (8, 4), (S, 8)):
+        assert fb(h, ctypes.byref(hp), good, 4, FAKE, FAKE, FAKE, None, None, None, off, n, None) == zs.ZS_ERANGE
+    assert fb(h, ctypes.byref(hp), good, 4, FAKE, FAKE, FAKE, None, None, None, S, 0, None) == zs.ZS_OK
+    assert fb(h, ctypes.byref(hp), good, 3, FAKE, FAKE, FAKE, None, None, None, 0, 8, None) == zs.ZS_EINVAL
+    assert fb(h, ctypes.byref(zs.AdamWHParams(step=0)), good, 4, FAKE, FAKE, FAKE, None, None, None, 0, 8,
+              None) == zs.ZS_EINVAL
     assert L.zs_plan_shard_numel(None) == -1
 
 

@@ -210,6 +210,34 @@ def test_fused_equals_unfused_bit_exact(zs):
 
 
 @pytest.mark.parametrize("N", [4, 64])
+def test_fused_buckets_equal_whole_shard(zs, N):
+    """The fused step bucket by bucket (ragged buckets and an empty one, in a
+    shuffled order) leaves the same bytes as the whole-shard call, which
+    matches the oracle; at N=64 each bucket runs in the two-pass form."""
+    import torch
+    whole = FlatRun(zs, [70_001, 77], N, 1, 1, 2, 400 + N, _hp(zs), fused=True)
+    part = FlatRun(zs, [70_001, 77], N, 1, 1, 2, 400 + N, _hp(zs), fused=True)
+    S = whole.S
+    rng = random.Random(N)
+    edges = sorted({0, S} | {8 * k for k in rng.sample(range(1, S // 8), 5)})
+    buckets = list(zip(edges[:-1], edges[1:])) + [(edges[2], edges[2])]
+    rng.shuffle(buckets)
+    d = part.d
+    for t in (1, 2):
+        whole.step(t)
+        for lo, hi in buckets:
+            zs.zs_fused_shard_step_bucket(part.plan, part.hp.at(t), part.dc[t], d["master"], d["m"], d["v"], lo,
+                                          hi - lo, grad=d["g"], param=d["p"], full=d["full"])
+    whole.check()
+    torch.cuda.synchronize()
+    for k in ("g", "master", "m", "v", "p", "full"):
+        a, b = whole.d[k], d[k]
+        if a.dtype == torch.float32:
+            a, b = a.view(torch.int32), b.view(torch.int32)
+        assert torch.equal(a, b), f"bucketed != whole shard: {k}"
+
+
+@pytest.mark.parametrize("N", [4, 64])
 @pytest.mark.parametrize("outs", range(8), ids=lambda o: f"grad{o & 1}-param{(o >> 1) & 1}-full{(o >> 2) & 1}")
 def test_fused_optional_outputs(zs, N, outs):
     """Every subset of the fused step's optional outputs (grad shard, param
