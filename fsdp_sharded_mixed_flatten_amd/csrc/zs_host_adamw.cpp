@@ -43,7 +43,16 @@ inline uint16_t to_bf16(float f) {
     return (u & 0x7FFFFFFFu) > 0x7F800000u ? (uint16_t)((u >> 16) | 0x40u) : (uint16_t)r;
 }
 
-__attribute__((target_clones("avx512f", "avx2", "default"))) void adamw_range(
+// Compiled for AVX-512, AVX2 and baseline x86-64, the variant picked when the
+// library loads. ZS_HOST_ONE_ISA builds the baseline only, for runtimes that
+// cannot resolve the variants at load time (the thread sanitizer's).
+#ifdef ZS_HOST_ONE_ISA
+#define ZS_ISA_CLONES
+#else
+#define ZS_ISA_CLONES __attribute__((target_clones("avx512f", "avx2", "default")))
+#endif
+
+ZS_ISA_CLONES void adamw_range(
     const AdamCoef c, const uint16_t* __restrict__ g, float* __restrict__ master, float* __restrict__ m,
     float* __restrict__ v, uint16_t* __restrict__ p, int64_t n) {
     const float b1 = c.b1, omb1 = c.omb1, b2 = c.b2, omb2 = c.omb2;
