@@ -198,6 +198,34 @@ def per_tensor_setup(zs, synth, oracle, wl, packed=True):
     return plan, dict(pieces=pieces, contribs=contribs, ws=ws, ws_fused=ws_fused)
 
 
+GRAPH_MAX_ELEMS = 1 << 24  # shards up to this size are launch-bound: also time their steps from a HIP graph
+
+
+def graph_time(torch, fn, steps_per_graph, replays):
+    """fn(t, None) for t = 1 .. steps_per_graph captured once into one HIP
+    graph (PyTorch's CUDAGraph drives HIP graphs on ROCm) and replayed
+    `replays` times back to back; returns device ms per step from one event
+    pair around the replays. Kernel arguments are fixed at capture, so every
+    replay repeats the same step counts on the evolving state."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for t in range(1, steps_per_graph + 1):
+            fn(t, None)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(replays):
+        graph.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / (replays * steps_per_graph)
+
+
 def time_loop(fn, warmup, steps):
     """Runs fn(t, timer) for `warmup` untimed steps, then `steps` timed steps
     launched back to back. Returns (wall ms per step, bracketed by device
@@ -398,6 +426,7 @@ def main():
                                  "bytes_per_param": bpp, "launches_per_step": 2 if write_grad else 1,
                                  "kernel": "k_reduce+k_adamw" if write_grad else "k_fused"}
         main_path = "fused"
+        graphable = {"fused": fused}
         if not args.no_unfused:
             B = wl.bucket_elems or S
 
@@ -412,6 +441,7 @@ def main():
                     timer.stop(e)
 
             u_wall, u_dev, u_ev = time_loop(unfused, 1, max(3, args.steps // 2))
+            graphable["unfused"] = unfused
             result_paths["unfused"] = {"ms_per_step": u_wall, "device_ms_per_step": u_dev,
                                        "events_ms_median": statistics.median(u_ev),
                                        "bytes_per_param": unfused_bytes_per_param(N),
@@ -506,11 +536,18 @@ def main():
                     timer.stop(e)
 
             a_wall, a_dev, a_ev = time_loop(accum_step, 1, max(3, args.steps // 2))
+            graphable["accum_clip"] = accum_step
             a_bytes = G * (2 * N + 8) - 4 + 4 + 30  # micro-steps (first one does not read acc), stats, AdamW
             result_paths["accum_clip"] = {"micro_steps": G, "max_norm": args.clip, "ms_per_step": a_wall,
                                           "device_ms_per_step": a_dev, "events_ms_median": statistics.median(a_ev),
                                           "bytes_per_param": a_bytes,
                                           "gbps": S * a_bytes / (a_dev / 1e3) / 1e9}
+        if S <= GRAPH_MAX_ELEMS:
+            # launch-bound: the same steps replayed from a HIP graph, 20 per graph
+            for name, fn in graphable.items():
+                g_ms = graph_time(torch, fn, 20, max(5, args.steps // 20))
+                result_paths[name]["graph_ms_per_step"] = g_ms
+                result_paths[name]["graph_speedup_over_eager"] = result_paths[name]["ms_per_step"] / g_ms
     else:
         import oracle
         plan, st = per_tensor_setup(zs, synth, oracle, wl)
