@@ -47,6 +47,16 @@ class AdamWHParams(ctypes.Structure):
         return AdamWHParams(self.lr, self.beta1, self.beta2, self.eps, self.weight_decay, step)
 
 
+class AdamWCoefs(ctypes.Structure):
+    """The fp32 scalars of one AdamW step (zs_adamw_coefs)."""
+    _fields_ = [(name, ctypes.c_float) for name in
+                ("beta1", "one_minus_beta1", "beta2", "one_minus_beta2", "lr", "eps", "decay", "bias_correction1",
+                 "bias_correction2")]
+
+    def values(self):
+        return [getattr(self, name) for name, _ in self._fields_]
+
+
 class TensorInfo(ctypes.Structure):
     _fields_ = [("numel", ctypes.c_int64), ("flat_off", ctypes.c_int64),
                 ("padded_numel", ctypes.c_int64), ("own_lo", ctypes.c_int64),
@@ -117,6 +127,11 @@ def _load():
         "zs_clip_scale": (st, [vp, vp, i32, ctypes.c_double, vp, vp, vp]),
         "zs_adamw_shard_step_accum": (st, [vp, ctypes.POINTER(AdamWHParams), vp, ctypes.c_float, vp, vp, vp, vp,
                                            vp, vp, vp, vp]),
+        "zs_adamw_coefs_compute": (st, [ctypes.POINTER(AdamWHParams), ctypes.POINTER(AdamWCoefs)]),
+        "zs_fused_shard_step_dc": (st, [vp, vp, ctypes.POINTER(vp), i32, vp, vp, vp, vp, vp, vp, vp]),
+        "zs_adamw_shard_step_dc": (st, [vp, vp, vp, vp, vp, vp, vp, vp]),
+        "zs_adamw_shard_step_accum_dc": (st, [vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "zs_fused_shard_step_multi_dc": (st, [vp, vp, i32, vp, vp]),
         "zs_last_error": (ctypes.c_char_p, []),
         "zs_version": (ctypes.c_char_p, []),
     }
@@ -140,7 +155,9 @@ EXPORTED = ("zs_shard_plan", "zs_shard_plan_ex", "zs_plan_tensor_group", "zs_pla
             "zs_fused_shard_step_multi_groups", "zs_quant_code_bytes", "zs_quant_num_scales", "zs_quantize_shard",
             "zs_fused_shard_step_quant", "zs_dequant_gather", "zs_host_adamw_step", "zs_offload_adamw_step",
             "zs_accumulate_shard", "zs_grad_stats_workspace_bytes",
-            "zs_grad_stats", "zs_clip_scale", "zs_adamw_shard_step_accum", "zs_last_error", "zs_version")
+            "zs_grad_stats", "zs_clip_scale", "zs_adamw_shard_step_accum", "zs_adamw_coefs_compute",
+            "zs_fused_shard_step_dc", "zs_adamw_shard_step_dc", "zs_adamw_shard_step_accum_dc",
+            "zs_fused_shard_step_multi_dc", "zs_last_error", "zs_version")
 
 
 def lib():
@@ -573,6 +590,54 @@ def zs_adamw_shard_step_accum(plan, hp, acc, grad_divisor, master, m, v, scale=N
                                           _ptr(master, "f32", S, "master"), _ptr(m, "f32", S, "m"),
                                           _ptr(v, "f32", S, "v"), _ptr(param, "bf16", S, "param"),
                                           _ptr(full, "bf16", (r + 1) * S, "full"), _stream(stream)))
+
+
+# ---------------------------------------------------------------- scalars in device memory
+
+
+def zs_adamw_coefs_compute(hp):
+    """The fp32 scalars of hp's step (an AdamWCoefs; .values() lists them in
+    the order a device buffer holds them)."""
+    out = AdamWCoefs()
+    _check(_lib.zs_adamw_coefs_compute(ctypes.byref(hp), ctypes.byref(out)))
+    return out
+
+
+def _coefs_ptr(coefs, n_sets=1):
+    return _ptr(coefs, "f32", 9 * n_sets, "coefs")
+
+
+def zs_fused_shard_step_dc(plan, coefs, contribs, master, m, v, grad=None, param=None, full=None, stream=None):
+    S, r = plan.shard_numel, plan.rank
+    ptrs = [_ptr(c, "bf16", S, f"contribs[{q}]") for q, c in enumerate(contribs)]
+    _check(_lib.zs_fused_shard_step_dc(plan.handle, _coefs_ptr(coefs), _ptr_array(ptrs), len(ptrs),
+                                       _ptr(master, "f32", S, "master"), _ptr(m, "f32", S, "m"),
+                                       _ptr(v, "f32", S, "v"), _ptr(grad, "bf16", S, "grad"),
+                                       _ptr(param, "bf16", S, "param"), _ptr(full, "bf16", (r + 1) * S, "full"),
+                                       _stream(stream)))
+
+
+def zs_adamw_shard_step_dc(plan, coefs, grad, master, m, v, param, stream=None):
+    S = plan.shard_numel
+    _check(_lib.zs_adamw_shard_step_dc(plan.handle, _coefs_ptr(coefs), _ptr(grad, "bf16", S, "grad"),
+                                       _ptr(master, "f32", S, "master"), _ptr(m, "f32", S, "m"),
+                                       _ptr(v, "f32", S, "v"), _ptr(param, "bf16", S, "param"), _stream(stream)))
+
+
+def zs_adamw_shard_step_accum_dc(plan, coefs, acc, grad_divisor, master, m, v, scale=None, skip=None, param=None,
+                                 full=None, stream=None):
+    S, r = plan.shard_numel, plan.rank
+    _check(_lib.zs_adamw_shard_step_accum_dc(plan.handle, _coefs_ptr(coefs), _ptr(acc, "f32", S, "acc"),
+                                             grad_divisor, _scalar_ptr(scale, "float32", "scale"),
+                                             _scalar_ptr(skip, "int32", "skip"), _ptr(master, "f32", S, "master"),
+                                             _ptr(m, "f32", S, "m"), _ptr(v, "f32", S, "v"),
+                                             _ptr(param, "bf16", S, "param"), _ptr(full, "bf16", (r + 1) * S, "full"),
+                                             _stream(stream)))
+
+
+def zs_fused_shard_step_multi_dc(plan, coefs, n_groups, workspace, stream=None):
+    _check(_lib.zs_fused_shard_step_multi_dc(plan.handle, _coefs_ptr(coefs, n_groups), n_groups,
+                                             workspace.data_ptr(), _stream(stream)))
 
 
 def zs_last_error():

@@ -61,6 +61,13 @@ zs_status check_hp(const zs_adamw_hparams* hp) {
     return ZS_OK;
 }
 
+// A device pointer to zs_adamw_coefs scalars.
+zs_status check_coefs(const zs_adamw_coefs* coefs) {
+    if (!coefs) return fail(ZS_EINVAL, "coefs is NULL");
+    if (reinterpret_cast<uintptr_t>(coefs) & 3) return fail(ZS_EALIGN, "coefs must be 4-byte aligned");
+    return ZS_OK;
+}
+
 zs_status check_contribs(const zs_plan* plan, const void* const* contribs, int32_t n) {
     if (!contribs) return fail(ZS_EINVAL, "contribs is NULL");
     if (n < 1 || n > ZS_MAX_CONTRIBS)
@@ -305,18 +312,46 @@ zs_status zs_reduce_shard(const zs_plan* plan, const void* const* contribs, int3
                       "reduce launch");
 }
 
-zs_status zs_adamw_shard_step(const zs_plan* plan, const zs_adamw_hparams* hp, const void* grad_bf16,
-                              float* master, float* m, float* v, void* param_bf16, void* stream) {
-    if (zs_status st = check_plan(plan)) return st;
-    if (zs_status st = check_hp(hp)) return st;
+namespace {
+
+// The AdamW calls below, after their scalars were validated: by value (c) or
+// in device memory (cdev).
+zs_status adamw_impl(const zs_plan* plan, const zs::AdamCoef& c, const zs::AdamCoef* cdev, const void* grad_bf16,
+                     float* master, float* m, float* v, void* param_bf16, void* stream) {
     if (zs_status st = check_ptr(grad_bf16, "grad_bf16")) return st;
     if (zs_status st = check_ptr(master, "master")) return st;
     if (zs_status st = check_ptr(m, "m")) return st;
     if (zs_status st = check_ptr(v, "v")) return st;
     if (zs_status st = check_ptr(param_bf16, "param_bf16")) return st;
     if (plan->S == 0) return ZS_OK;
-    return hip_status(zs::launch_adamw(zs::make_coef(*hp), grad_bf16, master, m, v, param_bf16, nullptr, plan->S, stream),
+    return hip_status(zs::launch_adamw(c, grad_bf16, master, m, v, param_bf16, nullptr, plan->S, stream, nullptr, cdev),
                       "adamw launch");
+}
+
+const zs::AdamCoef* dev_coef(const zs_adamw_coefs* coefs) { return reinterpret_cast<const zs::AdamCoef*>(coefs); }
+
+}  // namespace
+
+zs_status zs_adamw_shard_step(const zs_plan* plan, const zs_adamw_hparams* hp, const void* grad_bf16,
+                              float* master, float* m, float* v, void* param_bf16, void* stream) {
+    if (zs_status st = check_plan(plan)) return st;
+    if (zs_status st = check_hp(hp)) return st;
+    return adamw_impl(plan, zs::make_coef(*hp), nullptr, grad_bf16, master, m, v, param_bf16, stream);
+}
+
+zs_status zs_adamw_shard_step_dc(const zs_plan* plan, const zs_adamw_coefs* coefs, const void* grad_bf16,
+                                 float* master, float* m, float* v, void* param_bf16, void* stream) {
+    if (zs_status st = check_plan(plan)) return st;
+    if (zs_status st = check_coefs(coefs)) return st;
+    return adamw_impl(plan, zs::AdamCoef{}, dev_coef(coefs), grad_bf16, master, m, v, param_bf16, stream);
+}
+
+zs_status zs_adamw_coefs_compute(const zs_adamw_hparams* hp, zs_adamw_coefs* out) {
+    if (zs_status st = check_hp(hp)) return st;
+    if (!out) return fail(ZS_EINVAL, "out is NULL");
+    const zs::AdamCoef c = zs::make_coef(*hp);
+    *out = zs_adamw_coefs{c.b1, c.omb1, c.b2, c.omb2, c.lr, c.eps, c.decay, c.bc1, c.bc2};
+    return ZS_OK;
 }
 
 zs_status zs_gather_params(const zs_plan* plan, const void* param_bf16, void* full_bf16, void* stream) {
@@ -339,11 +374,37 @@ zs_status zs_fused_shard_step(const zs_plan* plan, const zs_adamw_hparams* hp, c
                                       0, plan->S, stream);
 }
 
+namespace {
+
+zs_status fused_impl(const zs_plan* plan, const zs::AdamCoef& c, const zs::AdamCoef* cdev,
+                     const void* const* contribs, int32_t n_contribs, float* master, float* m, float* v,
+                     void* grad_bf16, void* param_bf16, void* full_bf16, int64_t off, int64_t len, void* stream);
+
+}  // namespace
+
 zs_status zs_fused_shard_step_bucket(const zs_plan* plan, const zs_adamw_hparams* hp, const void* const* contribs,
                                      int32_t n_contribs, float* master, float* m, float* v, void* grad_bf16,
                                      void* param_bf16, void* full_bf16, int64_t off, int64_t len, void* stream) {
     if (zs_status st = check_plan(plan)) return st;
     if (zs_status st = check_hp(hp)) return st;
+    return fused_impl(plan, zs::make_coef(*hp), nullptr, contribs, n_contribs, master, m, v, grad_bf16, param_bf16,
+                      full_bf16, off, len, stream);
+}
+
+zs_status zs_fused_shard_step_dc(const zs_plan* plan, const zs_adamw_coefs* coefs, const void* const* contribs,
+                                 int32_t n_contribs, float* master, float* m, float* v, void* grad_bf16,
+                                 void* param_bf16, void* full_bf16, void* stream) {
+    if (zs_status st = check_plan(plan)) return st;
+    if (zs_status st = check_coefs(coefs)) return st;
+    return fused_impl(plan, zs::AdamCoef{}, dev_coef(coefs), contribs, n_contribs, master, m, v, grad_bf16,
+                      param_bf16, full_bf16, 0, plan->S, stream);
+}
+
+namespace {
+
+zs_status fused_impl(const zs_plan* plan, const zs::AdamCoef& c, const zs::AdamCoef* cdev,
+                     const void* const* contribs, int32_t n_contribs, float* master, float* m, float* v,
+                     void* grad_bf16, void* param_bf16, void* full_bf16, int64_t off, int64_t len, void* stream) {
     if (zs_status st = check_contribs(plan, contribs, n_contribs)) return st;
     if (zs_status st = check_ptr(master, "master")) return st;
     if (zs_status st = check_ptr(m, "m")) return st;
@@ -362,10 +423,12 @@ zs_status zs_fused_shard_step_bucket(const zs_plan* plan, const zs_adamw_hparams
     for (int32_t q = 0; q < n_contribs; ++q) shifted[q] = static_cast<const char*>(contribs[q]) + 2 * off;
     auto at16 = [off](void* p) { return p ? static_cast<void*>(static_cast<char*>(p) + 2 * off) : nullptr; };
     char* own = full_bf16 ? static_cast<char*>(full_bf16) + 2 * ((int64_t)plan->rank * plan->S + off) : nullptr;
-    return hip_status(zs::launch_fused(zs::make_coef(*hp), shifted, n_contribs, master + off, m + off, v + off,
-                                       at16(grad_bf16), at16(param_bf16), own, len, stream),
+    return hip_status(zs::launch_fused(c, shifted, n_contribs, master + off, m + off, v + off, at16(grad_bf16),
+                                       at16(param_bf16), own, len, stream, nullptr, cdev),
                       "fused launch");
 }
+
+}  // namespace
 
 // ------------------------------------------------------------------ quantized parameter gather
 
@@ -555,11 +618,11 @@ zs_status zs_clip_scale(const double* sumsq, const int32_t* nonfinite, int32_t n
                       "clip scale launch");
 }
 
-zs_status zs_adamw_shard_step_accum(const zs_plan* plan, const zs_adamw_hparams* hp, const float* acc_f32,
-                                    float grad_divisor, const float* scale, const int32_t* skip, float* master,
-                                    float* m, float* v, void* param_bf16, void* full_bf16, void* stream) {
-    if (zs_status st = check_plan(plan)) return st;
-    if (zs_status st = check_hp(hp)) return st;
+namespace {
+
+zs_status accum_step_impl(const zs_plan* plan, const zs::AdamCoef& c, const zs::AdamCoef* cdev, const float* acc_f32,
+                          float grad_divisor, const float* scale, const int32_t* skip, float* master, float* m,
+                          float* v, void* param_bf16, void* full_bf16, void* stream) {
     if (zs_status st = check_ptr(acc_f32, "acc_f32")) return st;
     if (!std::isfinite(grad_divisor) || grad_divisor == 0.0f)
         return fail(ZS_EINVAL, "grad_divisor = %g must be finite and nonzero", (double)grad_divisor);
@@ -574,9 +637,29 @@ zs_status zs_adamw_shard_step_accum(const zs_plan* plan, const zs_adamw_hparams*
         return fail(ZS_EINVAL, "a gather into full_bf16 needs a FLAT plan");
     if (plan->S == 0) return ZS_OK;
     char* own = full_bf16 ? static_cast<char*>(full_bf16) + 2 * (int64_t)plan->rank * plan->S : nullptr;
-    return hip_status(zs::launch_adamw_accum(zs::make_coef(*hp), acc_f32, grad_divisor, scale, skip, master, m, v,
-                                             param_bf16, own, plan->S, stream),
+    return hip_status(zs::launch_adamw_accum(c, acc_f32, grad_divisor, scale, skip, master, m, v, param_bf16, own,
+                                             plan->S, stream, cdev),
                       "adamw accum launch");
+}
+
+}  // namespace
+
+zs_status zs_adamw_shard_step_accum(const zs_plan* plan, const zs_adamw_hparams* hp, const float* acc_f32,
+                                    float grad_divisor, const float* scale, const int32_t* skip, float* master,
+                                    float* m, float* v, void* param_bf16, void* full_bf16, void* stream) {
+    if (zs_status st = check_plan(plan)) return st;
+    if (zs_status st = check_hp(hp)) return st;
+    return accum_step_impl(plan, zs::make_coef(*hp), nullptr, acc_f32, grad_divisor, scale, skip, master, m, v,
+                           param_bf16, full_bf16, stream);
+}
+
+zs_status zs_adamw_shard_step_accum_dc(const zs_plan* plan, const zs_adamw_coefs* coefs, const float* acc_f32,
+                                       float grad_divisor, const float* scale, const int32_t* skip, float* master,
+                                       float* m, float* v, void* param_bf16, void* full_bf16, void* stream) {
+    if (zs_status st = check_plan(plan)) return st;
+    if (zs_status st = check_coefs(coefs)) return st;
+    return accum_step_impl(plan, zs::AdamCoef{}, dev_coef(coefs), acc_f32, grad_divisor, scale, skip, master, m, v,
+                           param_bf16, full_bf16, stream);
 }
 
 // ------------------------------------------------------------------ multi-tensor
@@ -800,6 +883,23 @@ zs_status zs_adamw_shard_step_multi_groups(const zs_plan* plan, const zs_adamw_h
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasGrad | zs::kHasState, &b)) return st;
     return hip_status(zs::launch_multi(zs::kOpAdamw, &ct, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunk_piece.size(), b.n_contribs, stream),
                       "multi adamw launch");
+}
+
+zs_status zs_fused_shard_step_multi_dc(const zs_plan* plan, const zs_adamw_coefs* coefs, int32_t n_groups,
+                                       const void* workspace, void* stream) {
+    if (zs_status st = check_multi_plan(plan)) return st;
+    if (zs_status st = check_coefs(coefs)) return st;
+    if (n_groups < 1 || n_groups > ZS_MAX_GROUPS)
+        return fail(ZS_EINVAL, "n_groups = %d outside [1, %d]", n_groups, ZS_MAX_GROUPS);
+    for (const auto& t : plan->tensors)
+        if (t.group >= n_groups)
+            return fail(ZS_EINVAL, "the plan uses group %d but only %d sets of scalars were given", t.group, n_groups);
+    Binding b;
+    if (zs_status st = lookup_binding(plan, workspace, zs::kHasContribs | zs::kHasState, &b)) return st;
+    const zs::CoefTable unused{};
+    return hip_status(zs::launch_multi(zs::kOpFused, &unused, workspace, multi_offsets(plan, b.n_contribs),
+                                       (int)plan->chunk_piece.size(), b.n_contribs, stream, dev_coef(coefs)),
+                      "multi fused launch");
 }
 
 zs_status zs_fused_shard_step_multi_groups(const zs_plan* plan, const zs_adamw_hparams* hps, int32_t n_groups,

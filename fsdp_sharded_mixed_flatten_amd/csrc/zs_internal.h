@@ -10,10 +10,12 @@
 
 namespace zs {
 
-// fp32 scalars of one AdamW step, each rounded once from double.
+// fp32 scalars of one AdamW step, each rounded once from double. The same
+// layout as the public zs_adamw_coefs.
 struct AdamCoef {
     float b1, omb1, b2, omb2, lr, eps, decay, bc1, bc2;
 };
+static_assert(sizeof(AdamCoef) == sizeof(zs_adamw_coefs), "AdamCoef mirrors zs_adamw_coefs");
 
 AdamCoef make_coef(const zs_adamw_hparams& hp);
 
@@ -111,12 +113,15 @@ constexpr int32_t kQuantMaxBlock = 256;
 int launch_reduce(const void* const* contribs, int n, void* grad, int64_t len, void* stream);
 // launch_adamw / launch_fused: q (optional) also writes the updated shard's
 // codes and scales.
+// cdev (optional): read the AdamW scalars from device memory when the kernels
+// run instead of taking c (one AdamCoef; one per group for launch_multi).
 int launch_adamw(const AdamCoef& c, const void* grad, float* master, float* m, float* v,
-                 void* param, void* full_at_own, int64_t len, void* stream, const QuantOut* q = nullptr);
+                 void* param, void* full_at_own, int64_t len, void* stream, const QuantOut* q = nullptr,
+                 const AdamCoef* cdev = nullptr);
 int launch_gather(const void* param, void* full_at_own, int64_t len, void* stream);
 int launch_fused(const AdamCoef& c, const void* const* contribs, int n, float* master, float* m,
                  float* v, void* grad, void* param, void* full_at_own, int64_t len, void* stream,
-                 const QuantOut* q = nullptr);
+                 const QuantOut* q = nullptr, const AdamCoef* cdev = nullptr);
 int launch_quantize(const QuantOut& q, const void* param, int64_t len, void* stream);
 // Dequantizes n_ranks payloads (codes end to end, code_bytes each; scales end
 // to end, n_scales each) into full[r*S, (r+1)*S) for every rank r.
@@ -133,7 +138,8 @@ int launch_grad_stats(const float* acc, float divisor, double* sumsq_out, int32_
 int launch_clip_scale(const double* sumsq, const int32_t* nonfinite, int n_ranks, double max_norm, float* scale_out,
                       int32_t* skip_out, void* stream);
 int launch_adamw_accum(const AdamCoef& c, const float* acc, float divisor, const float* scale, const int32_t* skip,
-                       float* master, float* m, float* v, void* param, void* full_at_own, int64_t len, void* stream);
+                       float* master, float* m, float* v, void* param, void* full_at_own, int64_t len, void* stream,
+                       const AdamCoef* cdev = nullptr);
 
 enum MultiOp : int32_t { kOpReduce = 0, kOpAdamw = 1, kOpGather = 2, kOpFused = 3 };
 // Byte offsets of the tables in a bound workspace (the header holds the same
@@ -144,7 +150,7 @@ struct MultiOffsets {
     int64_t chunks;
 };
 int launch_multi(int op, const CoefTable* c, const void* workspace, const MultiOffsets& off, int n_chunks,
-                 int n_contribs, void* stream);
+                 int n_contribs, void* stream, const AdamCoef* cdev = nullptr);
 int copy_h2d_sync(void* dst, const void* src, int64_t bytes, void* stream);
 
 // Host AdamW over n elements with n_threads host threads (zs_host_adamw.cpp);

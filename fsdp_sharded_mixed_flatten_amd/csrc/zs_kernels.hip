@@ -211,6 +211,24 @@ __device__ __forceinline__ void st_nt(T* p, T x) { __builtin_nontemporal_store(x
 template <typename T>
 __device__ __forceinline__ T ld_g(const T* p) { return *(gptr<const T>)p; }
 
+// The step's AdamW scalars: the launch's own (by value), or, when `dev` is
+// set, the ones in device memory at the time the kernel runs (so a captured
+// graph can be replayed with new scalars). Uniform across the grid.
+__device__ __forceinline__ AdamCoef pick_coef(const AdamCoef& c, const AdamCoef* dev) {
+    if (!dev) return c;
+    AdamCoef d;
+    d.b1 = ld_g(&dev->b1);
+    d.omb1 = ld_g(&dev->omb1);
+    d.b2 = ld_g(&dev->b2);
+    d.omb2 = ld_g(&dev->omb2);
+    d.lr = ld_g(&dev->lr);
+    d.eps = ld_g(&dev->eps);
+    d.decay = ld_g(&dev->decay);
+    d.bc1 = ld_g(&dev->bc1);
+    d.bc2 = ld_g(&dev->bc2);
+    return d;
+}
+
 template <typename T>
 __device__ __forceinline__ T ld_in(const T* p) {
     if constexpr (ZS_NT_IN) return ld_nt(p); else return *(gptr<const T>)p;
@@ -604,11 +622,12 @@ __global__ __launch_bounds__(kBlock) void k_reduce(Ptrs<CAP> cp, int n_rt, float
 }
 
 template <int U, int QB>
-__global__ __launch_bounds__(kBlock) void k_adamw(AdamCoef c, const u32x2* __restrict__ g,
-                                                  f32x4* __restrict__ master, f32x4* __restrict__ m,
-                                                  f32x4* __restrict__ v, u32x2* __restrict__ param,
-                                                  u32x2* __restrict__ full, int64_t n4, QuantOut qo) {
-    adamw_tile<U, QB>(c, g, master, m, v, param, full, tile_base(U), n4, qo);
+__global__ __launch_bounds__(kBlock) void k_adamw(AdamCoef c, const AdamCoef* __restrict__ cdev,
+                                                  const u32x2* __restrict__ g, f32x4* __restrict__ master,
+                                                  f32x4* __restrict__ m, f32x4* __restrict__ v,
+                                                  u32x2* __restrict__ param, u32x2* __restrict__ full, int64_t n4,
+                                                  QuantOut qo) {
+    adamw_tile<U, QB>(pick_coef(c, cdev), g, master, m, v, param, full, tile_base(U), n4, qo);
 }
 
 __global__ __launch_bounds__(kBlock) void k_gather(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
@@ -617,12 +636,13 @@ __global__ __launch_bounds__(kBlock) void k_gather(const u32x4* __restrict__ src
 }
 
 template <int N, int CAP, int U, int QB>
-__global__ __launch_bounds__(kBlock) void k_fused(AdamCoef c, Ptrs<CAP> cp, int n_rt, float nf,
-                                                  f32x4* __restrict__ master, f32x4* __restrict__ m,
-                                                  f32x4* __restrict__ v, u32x2* __restrict__ grad,
-                                                  u32x2* __restrict__ param, u32x2* __restrict__ full,
-                                                  int64_t n4, QuantOut qo) {
-    fused_tile<N, U, QB>(c, cp.p, n_rt, nf, master, m, v, grad, param, full, tile_base(U), n4, qo);
+__global__ __launch_bounds__(kBlock) void k_fused(AdamCoef c, const AdamCoef* __restrict__ cdev, Ptrs<CAP> cp,
+                                                  int n_rt, float nf, f32x4* __restrict__ master,
+                                                  f32x4* __restrict__ m, f32x4* __restrict__ v,
+                                                  u32x2* __restrict__ grad, u32x2* __restrict__ param,
+                                                  u32x2* __restrict__ full, int64_t n4, QuantOut qo) {
+    fused_tile<N, U, QB>(pick_coef(c, cdev), cp.p, n_rt, nf, master, m, v, grad, param, full, tile_base(U), n4,
+                         qo);
 }
 
 // Codes of a bf16 shard, 8 elements per lane.
@@ -707,14 +727,15 @@ __global__ __launch_bounds__(kBlock) void k_dequant(const char* __restrict__ cod
 // piece supplies every pointer and its hyperparameter group; the
 // contributions of piece i are cps[i * N .. i * N + N).
 template <int OP, int N>
-__global__ __launch_bounds__(kBlock) void k_multi(CoefTable ct, const MultiHeader* __restrict__ hdr, MultiOffsets off,
-                                                  int n_rt, float nf) {
+__global__ __launch_bounds__(kBlock) void k_multi(CoefTable ct, const AdamCoef* __restrict__ cdev,
+                                                  const MultiHeader* __restrict__ hdr, MultiOffsets off, int n_rt,
+                                                  float nf) {
     static_assert(OP == kOpAdamw || OP == kOpFused, "reduce and gather have kernels of their own");
     if (hdr->magic != kMultiMagic) return;  // not a bound table (e.g. reused memory): touch nothing
     const char* ws = reinterpret_cast<const char*>(hdr);
     const int32_t piece = reinterpret_cast<const int32_t*>(ws + off.chunks)[blockIdx.x];
     const PieceDev pc = reinterpret_cast<const PieceDev*>(ws + off.pieces)[piece];
-    const AdamCoef c = ct.c[pc.group];
+    const AdamCoef c = pick_coef(ct.c[pc.group], cdev ? cdev + pc.group : nullptr);
     const int flags = hdr->flags;
     // the chunk's range in its piece; piece lengths are multiples of 8
     const int64_t start = (int64_t)((int32_t)blockIdx.x - pc.first_chunk) * kChunkElems;
@@ -1042,7 +1063,8 @@ __device__ __forceinline__ void adamw_accum_tile(const AdamCoef& c, const f32x4*
 }
 
 template <int U>
-__global__ __launch_bounds__(kBlock) void k_adamw_accum(AdamCoef c, const f32x4* __restrict__ acc, float divisor,
+__global__ __launch_bounds__(kBlock) void k_adamw_accum(AdamCoef c, const AdamCoef* __restrict__ cdev,
+                                                        const f32x4* __restrict__ acc, float divisor,
                                                         const float* __restrict__ scale_p,
                                                         const int32_t* __restrict__ skip_p,
                                                         f32x4* __restrict__ master, f32x4* __restrict__ m,
@@ -1050,7 +1072,7 @@ __global__ __launch_bounds__(kBlock) void k_adamw_accum(AdamCoef c, const f32x4*
                                                         u32x2* __restrict__ full, int64_t n4) {
     if (skip_p && *skip_p) return;  // uniform: the whole grid skips the step
     const float scale = scale_p ? *scale_p : 1.0f;
-    adamw_accum_tile<U>(c, acc, divisor, scale, master, m, v, param, full, tile_base(U), n4);
+    adamw_accum_tile<U>(pick_coef(c, cdev), acc, divisor, scale, master, m, v, param, full, tile_base(U), n4);
 }
 
 // ------------------------------------------------------------------ launch helpers
@@ -1075,13 +1097,14 @@ int launch_reduce_t(const void* const* contribs, int n, void* grad, int64_t len,
 }
 
 template <int N, int CAP, int QB>
-int launch_fused_q(const AdamCoef& c, const void* const* contribs, int n, float* master, float* m,
-                   float* v, void* grad, void* param, void* full, int64_t len, const QuantOut& qo, hipStream_t s) {
+int launch_fused_q(const AdamCoef& c, const AdamCoef* cdev, const void* const* contribs, int n, float* master,
+                   float* m, float* v, void* grad, void* param, void* full, int64_t len, const QuantOut& qo,
+                   hipStream_t s) {
     Ptrs<CAP> cp{};
     for (int q = 0; q < n; ++q) cp.p[q] = contribs[q];
     const int64_t n4 = len / 4;
     hipLaunchKernelGGL((k_fused<N, CAP, kFusedU, QB>), dim3(grid_for(n4, kFusedU)), dim3(kBlock),
-                       n <= 4 ? kFusedNarrowLds : kFusedLds, s, c,
+                       n <= 4 ? kFusedNarrowLds : kFusedLds, s, c, cdev,
                        cp, n, (float)n, reinterpret_cast<f32x4*>(master), reinterpret_cast<f32x4*>(m),
                        reinterpret_cast<f32x4*>(v), reinterpret_cast<u32x2*>(grad),
                        reinterpret_cast<u32x2*>(param), reinterpret_cast<u32x2*>(full), n4, qo);
@@ -1089,16 +1112,20 @@ int launch_fused_q(const AdamCoef& c, const void* const* contribs, int n, float*
 }
 
 template <int N, int CAP>
-int launch_fused_t(const AdamCoef& c, const void* const* contribs, int n, float* master, float* m,
-                   float* v, void* grad, void* param, void* full, int64_t len, const QuantOut* q, hipStream_t s) {
-    if (!q) return launch_fused_q<N, CAP, 0>(c, contribs, n, master, m, v, grad, param, full, len, QuantOut{}, s);
-    if (q->bits == 8) return launch_fused_q<N, CAP, 8>(c, contribs, n, master, m, v, grad, param, full, len, *q, s);
-    return launch_fused_q<N, CAP, 4>(c, contribs, n, master, m, v, grad, param, full, len, *q, s);
+int launch_fused_t(const AdamCoef& c, const AdamCoef* cdev, const void* const* contribs, int n, float* master,
+                   float* m, float* v, void* grad, void* param, void* full, int64_t len, const QuantOut* q,
+                   hipStream_t s) {
+    if (!q)
+        return launch_fused_q<N, CAP, 0>(c, cdev, contribs, n, master, m, v, grad, param, full, len, QuantOut{}, s);
+    if (q->bits == 8)
+        return launch_fused_q<N, CAP, 8>(c, cdev, contribs, n, master, m, v, grad, param, full, len, *q, s);
+    return launch_fused_q<N, CAP, 4>(c, cdev, contribs, n, master, m, v, grad, param, full, len, *q, s);
 }
 
 template <int OP, int N>
-int launch_multi_t(const CoefTable& c, const void* ws, const MultiOffsets& off, int n_chunks, int n, hipStream_t s) {
-    hipLaunchKernelGGL((k_multi<OP, N>), dim3((unsigned)n_chunks), dim3(kBlock), kMultiLds, s, c,
+int launch_multi_t(const CoefTable& c, const AdamCoef* cdev, const void* ws, const MultiOffsets& off, int n_chunks,
+                   int n, hipStream_t s) {
+    hipLaunchKernelGGL((k_multi<OP, N>), dim3((unsigned)n_chunks), dim3(kBlock), kMultiLds, s, c, cdev,
                        reinterpret_cast<const MultiHeader*>(ws), off, n, (float)n);
     return (int)hipGetLastError();
 }
@@ -1125,16 +1152,17 @@ int launch_multi_reduce(const void* ws, const MultiOffsets& off, int n_chunks, i
 }
 
 template <int OP>
-int launch_multi_op(const CoefTable& c, const void* ws, const MultiOffsets& off, int n_chunks, int n, hipStream_t s) {
+int launch_multi_op(const CoefTable& c, const AdamCoef* cdev, const void* ws, const MultiOffsets& off, int n_chunks,
+                    int n, hipStream_t s) {
     switch (n) {
-        case 1: return launch_multi_t<OP, 1>(c, ws, off, n_chunks, n, s);
-        case 2: return launch_multi_t<OP, 2>(c, ws, off, n_chunks, n, s);
-        case 4: return launch_multi_t<OP, 4>(c, ws, off, n_chunks, n, s);
-        case 8: return launch_multi_t<OP, 8>(c, ws, off, n_chunks, n, s);
-        case 16: return launch_multi_t<OP, 16>(c, ws, off, n_chunks, n, s);
-        case 32: return launch_multi_t<OP, 32>(c, ws, off, n_chunks, n, s);
-        case 64: return launch_multi_t<OP, 64>(c, ws, off, n_chunks, n, s);
-        default: return launch_multi_t<OP, 0>(c, ws, off, n_chunks, n, s);
+        case 1: return launch_multi_t<OP, 1>(c, cdev, ws, off, n_chunks, n, s);
+        case 2: return launch_multi_t<OP, 2>(c, cdev, ws, off, n_chunks, n, s);
+        case 4: return launch_multi_t<OP, 4>(c, cdev, ws, off, n_chunks, n, s);
+        case 8: return launch_multi_t<OP, 8>(c, cdev, ws, off, n_chunks, n, s);
+        case 16: return launch_multi_t<OP, 16>(c, cdev, ws, off, n_chunks, n, s);
+        case 32: return launch_multi_t<OP, 32>(c, cdev, ws, off, n_chunks, n, s);
+        case 64: return launch_multi_t<OP, 64>(c, cdev, ws, off, n_chunks, n, s);
+        default: return launch_multi_t<OP, 0>(c, cdev, ws, off, n_chunks, n, s);
     }
 }
 
@@ -1154,10 +1182,10 @@ int launch_accum_t(const void* const* contribs, int n, float* acc, int first, in
 }
 
 template <int QB>
-int launch_adamw_q(const AdamCoef& c, const void* grad, float* master, float* m, float* v, void* param,
-                   void* full_at_own, int64_t len, const QuantOut& qo, hipStream_t s) {
+int launch_adamw_q(const AdamCoef& c, const AdamCoef* cdev, const void* grad, float* master, float* m, float* v,
+                   void* param, void* full_at_own, int64_t len, const QuantOut& qo, hipStream_t s) {
     const int64_t n4 = len / 4;
-    hipLaunchKernelGGL((k_adamw<kAdamwU, QB>), dim3(grid_for(n4, kAdamwU)), dim3(kBlock), kAdamwLds, s, c,
+    hipLaunchKernelGGL((k_adamw<kAdamwU, QB>), dim3(grid_for(n4, kAdamwU)), dim3(kBlock), kAdamwLds, s, c, cdev,
                        reinterpret_cast<const u32x2*>(grad), reinterpret_cast<f32x4*>(master),
                        reinterpret_cast<f32x4*>(m), reinterpret_cast<f32x4*>(v), reinterpret_cast<u32x2*>(param),
                        reinterpret_cast<u32x2*>(full_at_own), n4, qo);
@@ -1184,12 +1212,12 @@ int launch_reduce(const void* const* contribs, int n, void* grad, int64_t len, v
 }
 
 int launch_adamw(const AdamCoef& c, const void* grad, float* master, float* m, float* v, void* param,
-                 void* full_at_own, int64_t len, void* stream, const QuantOut* q) {
+                 void* full_at_own, int64_t len, void* stream, const QuantOut* q, const AdamCoef* cdev) {
     if (len <= 0) return 0;
     hipStream_t s = (hipStream_t)stream;
-    if (!q) return launch_adamw_q<0>(c, grad, master, m, v, param, full_at_own, len, QuantOut{}, s);
-    if (q->bits == 8) return launch_adamw_q<8>(c, grad, master, m, v, param, full_at_own, len, *q, s);
-    return launch_adamw_q<4>(c, grad, master, m, v, param, full_at_own, len, *q, s);
+    if (!q) return launch_adamw_q<0>(c, cdev, grad, master, m, v, param, full_at_own, len, QuantOut{}, s);
+    if (q->bits == 8) return launch_adamw_q<8>(c, cdev, grad, master, m, v, param, full_at_own, len, *q, s);
+    return launch_adamw_q<4>(c, cdev, grad, master, m, v, param, full_at_own, len, *q, s);
 }
 
 int launch_quantize(const QuantOut& q, const void* param, int64_t len, void* stream) {
@@ -1232,43 +1260,44 @@ int launch_gather(const void* param, void* full_at_own, int64_t len, void* strea
 }
 
 int launch_fused(const AdamCoef& c, const void* const* contribs, int n, float* master, float* m, float* v,
-                 void* grad, void* param, void* full_at_own, int64_t len, void* stream, const QuantOut* q) {
+                 void* grad, void* param, void* full_at_own, int64_t len, void* stream, const QuantOut* q,
+                 const AdamCoef* cdev) {
     if (len <= 0) return 0;
     if (kSplitMinN > 0 && n >= kSplitMinN && grad) {
         // Large N: a nearly read-only reduce, then AdamW writing the outputs.
         // Same bytes in every buffer as the one-pass kernel.
         if (int e = launch_reduce(contribs, n, grad, len, stream)) return e;
-        return launch_adamw(c, grad, master, m, v, param, full_at_own, len, stream, q);
+        return launch_adamw(c, grad, master, m, v, param, full_at_own, len, stream, q, cdev);
     }
     hipStream_t s = (hipStream_t)stream;
     void* f = full_at_own;
     switch (n) {
-        case 1: return launch_fused_t<1, 1>(c, contribs, n, master, m, v, grad, param, f, len, q, s);
-        case 2: return launch_fused_t<2, 2>(c, contribs, n, master, m, v, grad, param, f, len, q, s);
-        case 4: return launch_fused_t<4, 4>(c, contribs, n, master, m, v, grad, param, f, len, q, s);
-        case 8: return launch_fused_t<8, 8>(c, contribs, n, master, m, v, grad, param, f, len, q, s);
-        case 16: return launch_fused_t<16, 16>(c, contribs, n, master, m, v, grad, param, f, len, q, s);
-        case 32: return launch_fused_t<32, 32>(c, contribs, n, master, m, v, grad, param, f, len, q, s);
-        case 64: return launch_fused_t<64, 64>(c, contribs, n, master, m, v, grad, param, f, len, q, s);
-        default: return launch_fused_t<0, ZS_MAX_CONTRIBS>(c, contribs, n, master, m, v, grad, param, f, len, q, s);
+        case 1: return launch_fused_t<1, 1>(c, cdev, contribs, n, master, m, v, grad, param, f, len, q, s);
+        case 2: return launch_fused_t<2, 2>(c, cdev, contribs, n, master, m, v, grad, param, f, len, q, s);
+        case 4: return launch_fused_t<4, 4>(c, cdev, contribs, n, master, m, v, grad, param, f, len, q, s);
+        case 8: return launch_fused_t<8, 8>(c, cdev, contribs, n, master, m, v, grad, param, f, len, q, s);
+        case 16: return launch_fused_t<16, 16>(c, cdev, contribs, n, master, m, v, grad, param, f, len, q, s);
+        case 32: return launch_fused_t<32, 32>(c, cdev, contribs, n, master, m, v, grad, param, f, len, q, s);
+        case 64: return launch_fused_t<64, 64>(c, cdev, contribs, n, master, m, v, grad, param, f, len, q, s);
+        default: return launch_fused_t<0, ZS_MAX_CONTRIBS>(c, cdev, contribs, n, master, m, v, grad, param, f, len, q, s);
     }
 }
 
 int launch_multi(int op, const CoefTable* c, const void* workspace, const MultiOffsets& off, int n_chunks,
-                 int n_contribs, void* stream) {
+                 int n_contribs, void* stream, const AdamCoef* cdev) {
     if (n_chunks <= 0) return 0;
     const CoefTable cc = c ? *c : CoefTable{};
     hipStream_t s = (hipStream_t)stream;
     switch (op) {
         case kOpReduce: return launch_multi_reduce(workspace, off, n_chunks, n_contribs, s);
-        case kOpAdamw: return launch_multi_t<kOpAdamw, 1>(cc, workspace, off, n_chunks, 1, s);
+        case kOpAdamw: return launch_multi_t<kOpAdamw, 1>(cc, cdev, workspace, off, n_chunks, 1, s);
         case kOpGather:
             hipLaunchKernelGGL(k_multi_gather, dim3((unsigned)((n_chunks + kGatherChunksPerBlock - 1) /
                                                                kGatherChunksPerBlock)),
                                dim3(kBlock), kMultiLds, s, reinterpret_cast<const MultiHeader*>(workspace), off,
                                n_chunks);
             return (int)hipGetLastError();
-        default: return launch_multi_op<kOpFused>(cc, workspace, off, n_chunks, n_contribs, s);
+        default: return launch_multi_op<kOpFused>(cc, cdev, workspace, off, n_chunks, n_contribs, s);
     }
 }
 
@@ -1309,11 +1338,12 @@ int launch_clip_scale(const double* sumsq, const int32_t* nonfinite, int n_ranks
 }
 
 int launch_adamw_accum(const AdamCoef& c, const float* acc, float divisor, const float* scale, const int32_t* skip,
-                       float* master, float* m, float* v, void* param, void* full_at_own, int64_t len, void* stream) {
+                       float* master, float* m, float* v, void* param, void* full_at_own, int64_t len, void* stream,
+                       const AdamCoef* cdev) {
     if (len <= 0) return 0;
     const int64_t n4 = len / 4;
     hipLaunchKernelGGL((k_adamw_accum<kAdamwU>), dim3(grid_for(n4, kAdamwU)), dim3(kBlock), kAdamwLds,
-                       (hipStream_t)stream, c, reinterpret_cast<const f32x4*>(acc), divisor, scale, skip,
+                       (hipStream_t)stream, c, cdev, reinterpret_cast<const f32x4*>(acc), divisor, scale, skip,
                        reinterpret_cast<f32x4*>(master), reinterpret_cast<f32x4*>(m), reinterpret_cast<f32x4*>(v),
                        reinterpret_cast<u32x2*>(param), reinterpret_cast<u32x2*>(full_at_own), n4);
     return (int)hipGetLastError();

@@ -416,6 +416,51 @@ zs_status zs_adamw_shard_step_accum(const zs_plan* plan, const zs_adamw_hparams*
                                     float grad_divisor, const float* scale, const int32_t* skip, float* master,
                                     float* m, float* v, void* param_bf16, void* full_bf16, void* stream);
 
+/* ------------------------------------------------------------------ scalars in device memory
+ * Kernel arguments are fixed when a stream is captured into a HIP graph, so a
+ * replayed step would repeat its step count t (and learning rate). The _dc
+ * calls below are the corresponding calls with the AdamW scalars read from
+ * device memory when the kernels run: capture the step once, and before each
+ * replay write that step's scalars into the buffer (for example a captured
+ * copy from page-locked host memory that the host refills). Launch-bound
+ * shards gain most: replayed steps avoid the host's launch cost. */
+
+/* The fp32 AdamW scalars of one step, each rounded once from double exactly
+ * as the by-value calls compute them:
+ *   beta1, 1-beta1, beta2, 1-beta2, lr, eps, 1-lr*wd, 1-beta1^t, 1-beta2^t. */
+typedef struct zs_adamw_coefs {
+    float beta1;
+    float one_minus_beta1;
+    float beta2;
+    float one_minus_beta2;
+    float lr;
+    float eps;
+    float decay;
+    float bias_correction1;
+    float bias_correction2;
+} zs_adamw_coefs;
+
+/* Host only: the scalars of hp (same validation as the step calls). */
+zs_status zs_adamw_coefs_compute(const zs_adamw_hparams* hp, zs_adamw_coefs* out);
+
+/* As zs_fused_shard_step, zs_adamw_shard_step and zs_adamw_shard_step_accum,
+ * with coefs a DEVICE pointer (4-byte aligned) to the step's scalars, read by
+ * the kernels at run time; results are bit-identical to the by-value call
+ * with the hparams the scalars were computed from. The values are not
+ * checked: fill the buffer with zs_adamw_coefs_compute's output. */
+zs_status zs_fused_shard_step_dc(const zs_plan* plan, const zs_adamw_coefs* coefs, const void* const* contribs,
+                                 int32_t n_contribs, float* master, float* m, float* v, void* grad_bf16,
+                                 void* param_bf16, void* full_bf16, void* stream);
+zs_status zs_adamw_shard_step_dc(const zs_plan* plan, const zs_adamw_coefs* coefs, const void* grad_bf16,
+                                 float* master, float* m, float* v, void* param_bf16, void* stream);
+zs_status zs_adamw_shard_step_accum_dc(const zs_plan* plan, const zs_adamw_coefs* coefs, const float* acc_f32,
+                                       float grad_divisor, const float* scale, const int32_t* skip, float* master,
+                                       float* m, float* v, void* param_bf16, void* full_bf16, void* stream);
+/* As zs_fused_shard_step_multi_groups with coefs a DEVICE array of n_groups
+ * scalar sets (piece i uses coefs[group of tensor i]). */
+zs_status zs_fused_shard_step_multi_dc(const zs_plan* plan, const zs_adamw_coefs* coefs, int32_t n_groups,
+                                       const void* workspace, void* stream);
+
 /* ------------------------------------------------------------------ misc */
 
 /* Thread-local text describing the last non-OK status of this thread. */

@@ -126,6 +126,14 @@ void validation(Fake& fake) {
     CHECK(zs_clip_scale(reinterpret_cast<double*>(d), reinterpret_cast<int32_t*>(d + 8), 1, -1.0, f,
                         reinterpret_cast<int32_t*>(d + 16), nullptr) == ZS_EINVAL);
     CHECK(zs_adamw_shard_step_accum(p, &hp, f, 2.0f, f, nullptr, f, f, f, d, d, nullptr) == ZS_OK);
+    // the same calls with the scalars in (stand-in) device memory
+    zs_adamw_coefs co;
+    CHECK(zs_adamw_coefs_compute(&hp, &co) == ZS_OK && co.bias_correction1 > 0.0f);
+    const zs_adamw_coefs* cd = reinterpret_cast<const zs_adamw_coefs*>(d + 32768);
+    CHECK(zs_fused_shard_step_dc(p, cd, c4, 4, f, f, f, nullptr, nullptr, d, nullptr) == ZS_OK);
+    CHECK(zs_fused_shard_step_dc(p, nullptr, c4, 4, f, f, f, nullptr, nullptr, d, nullptr) == ZS_EINVAL);
+    CHECK(zs_adamw_shard_step_dc(p, cd, d, f, f, f, d, nullptr) == ZS_OK);
+    CHECK(zs_adamw_shard_step_accum_dc(p, cd, f, 2.0f, nullptr, nullptr, f, f, f, d, nullptr, nullptr) == ZS_OK);
     CHECK(zs::g_launches.load() > before);
     zs_plan_destroy(p);
 }
@@ -178,6 +186,9 @@ void multi_table(Fake& fake) {
     CHECK(zs_fused_shard_step_multi(p, &hps[0], ws, nullptr) == ZS_OK);
     CHECK(zs_fused_shard_step_multi_groups(p, hps, 2, ws, nullptr) == ZS_OK);
     CHECK(zs_fused_shard_step_multi_groups(p, hps, 1, ws, nullptr) == ZS_EINVAL);  // group 1 has no hparams
+    const zs_adamw_coefs* cd = reinterpret_cast<const zs_adamw_coefs*>(d + 32768);
+    CHECK(zs_fused_shard_step_multi_dc(p, cd, 2, ws, nullptr) == ZS_OK);
+    CHECK(zs_fused_shard_step_multi_dc(p, cd, 1, ws, nullptr) == ZS_EINVAL);
     CHECK(zs_reduce_shard_multi(p, ws, nullptr) == ZS_OK);
     CHECK(zs_adamw_shard_step_multi(p, &hps[0], ws, nullptr) == ZS_OK);
     CHECK(zs_gather_params_multi(p, ws, nullptr) == ZS_OK);

@@ -16,12 +16,12 @@ std::atomic<int> g_launches{0};
 
 int launch_reduce(const void* const*, int, void*, int64_t, void*) { return ++g_launches, 0; }
 int launch_adamw(const AdamCoef&, const void*, float*, float*, float*, void*, void*, int64_t, void*,
-                 const QuantOut*) {
+                 const QuantOut*, const AdamCoef*) {
     return ++g_launches, 0;
 }
 int launch_gather(const void*, void*, int64_t, void*) { return ++g_launches, 0; }
 int launch_fused(const AdamCoef&, const void* const*, int, float*, float*, float*, void*, void*, void*, int64_t,
-                 void*, const QuantOut*) {
+                 void*, const QuantOut*, const AdamCoef*) {
     return ++g_launches, 0;
 }
 int launch_quantize(const QuantOut&, const void*, int64_t, void*) { return ++g_launches, 0; }
@@ -34,10 +34,10 @@ int launch_clip_scale(const double*, const int32_t*, int, double, float*, int32_
     return ++g_launches, 0;
 }
 int launch_adamw_accum(const AdamCoef&, const float*, float, const float*, const int32_t*, float*, float*, float*,
-                       void*, void*, int64_t, void*) {
+                       void*, void*, int64_t, void*, const AdamCoef*) {
     return ++g_launches, 0;
 }
-int launch_multi(int, const CoefTable*, const void*, const MultiOffsets&, int, int, void*) {
+int launch_multi(int, const CoefTable*, const void*, const MultiOffsets&, int, int, void*, const AdamCoef*) {
     return ++g_launches, 0;
 }
 int copy_h2d_sync(void* dst, const void* src, int64_t bytes, void*) {

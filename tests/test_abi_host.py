@@ -340,3 +340,41 @@ def test_plans_built_concurrently(zs):
         th.join(timeout=120)
         assert not th.is_alive()
     assert got == want
+
+
+def test_adamw_coefs_equal_oracle_scalars(zs):
+    """The host-computed scalars of the device-scalar calls equal the oracle's,
+    bit for bit, over a spread of hyperparameters and step counts."""
+    import numpy as np
+
+    import oracle
+    rng = random.Random(11)
+    for _ in range(300):
+        hp = zs.AdamWHParams(lr=10 ** rng.uniform(-6, -1), beta1=rng.choice([0.0, 0.5, 0.9, 0.99]),
+                             beta2=rng.choice([0.9, 0.95, 0.999, 0.9999]), eps=rng.choice([0.0, 1e-8, 1e-6]),
+                             weight_decay=rng.choice([0.0, 0.01, 0.1]), step=rng.choice([1, 2, 3, 10, 1000, 10**6]))
+        got = np.array(zs.zs_adamw_coefs_compute(hp).values(), dtype=np.float32)
+        want = oracle.adamw_coef(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.step)
+        assert got.tobytes() == want.tobytes(), (hp.lr, hp.beta1, hp.beta2, hp.step)
+    with pytest.raises(zs.ZsError):
+        zs.zs_adamw_coefs_compute(zs.AdamWHParams(step=0))
+
+
+def test_device_scalar_calls_validate_without_device(zs):
+    L = zs.lib()
+    plan = zs.zs_shard_plan([1000], 4, 1)
+    h = plan.handle
+    good = (ctypes.c_void_p * 4)(FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288)
+    assert L.zs_fused_shard_step_dc(h, None, good, 4, FAKE, FAKE, FAKE, None, None, None, None) == zs.ZS_EINVAL
+    assert L.zs_fused_shard_step_dc(h, FAKE + 2, good, 4, FAKE, FAKE, FAKE, None, None, None, None) == zs.ZS_EALIGN
+    assert L.zs_fused_shard_step_dc(h, FAKE + 4, good, 3, FAKE, FAKE, FAKE, None, None, None, None) == zs.ZS_EINVAL
+    assert L.zs_adamw_shard_step_dc(h, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == zs.ZS_EINVAL
+    assert L.zs_adamw_shard_step_accum_dc(h, None, FAKE, 1.0, None, None, FAKE, FAKE, FAKE, None, None,
+                                          None) == zs.ZS_EINVAL
+    assert L.zs_adamw_shard_step_accum_dc(h, FAKE, FAKE, 0.0, None, None, FAKE, FAKE, FAKE, None, None,
+                                          None) == zs.ZS_EINVAL  # zero divisor
+    pt = zs.zs_shard_plan([4096], 8, 0, 1, zs.ZS_LAYOUT_PER_TENSOR)
+    assert L.zs_fused_shard_step_multi_dc(pt.handle, FAKE, 0, FAKE, None) == zs.ZS_EINVAL  # n_groups
+    assert L.zs_fused_shard_step_multi_dc(pt.handle, FAKE, 1, FAKE, None) == zs.ZS_EINVAL  # never bound
+    assert b"never bound" in L.zs_last_error()
+    assert L.zs_fused_shard_step_multi_dc(h, FAKE, 1, FAKE, None) == zs.ZS_EINVAL  # FLAT plan

@@ -5,7 +5,9 @@ host synchronization and no memset nodes. A caller can therefore capture a
 whole step once and replay it as one graph launch per step (worthwhile for
 launch-bound shards such as the 1M-element one here, whose kernels run for a
 few microseconds). Kernel arguments are fixed at capture, so a captured step
-keeps the hyperparameters (step t included) it was captured with.
+keeps the hyperparameters (step t included) it was captured with; the _dc
+calls read the AdamW scalars from device memory instead, so a step captured
+once can take each replay's own.
 
 Each test captures a step on one copy of the state, then replays it several
 times. Before every replay new gradients are copied into the captured
@@ -254,4 +256,135 @@ def test_multi_tensor_step_in_graph(zs):
         full_o = np.full(oplan.padded[i], SENT, np.uint16)
         full_o[oplan.pieces[i].own_lo:oplan.pieces[i].own_hi] = oi["p"]
         assert np.array_equal(host16(d["full"]), full_o), f"full[{i}]"
+    assert nd == 0
+
+
+def _dev_coefs(zs, hps):
+    import torch
+    vals = [x for hp in hps for x in zs.zs_adamw_coefs_compute(hp).values()]
+    return torch.tensor(vals, dtype=torch.float32, device="cuda")
+
+
+def test_device_scalar_calls_equal_by_value(zs):
+    """The _dc calls (AdamW scalars read from device memory) leave the same
+    bytes as the by-value calls: fused step (one- and two-pass), AdamW, the
+    step from the accumulator and the multi-tensor step with two groups."""
+    import torch
+    hp = zs.AdamWHParams(lr=2e-3, beta1=0.9, beta2=0.99, eps=1e-7, weight_decay=0.05, step=7)
+    for N in (4, 64):
+        numels = [30_011, 77]
+        plan = zs.zs_shard_plan(numels, N, N - 1, 1)
+        T, S = plan.padded_numel, plan.shard_numel
+        rng = np.random.default_rng(N)
+        cs = [dev16(oracle.f32_to_bf16((rng.standard_normal(S) * 1e-3).astype(np.float32))) for _ in range(N)]
+        master0 = (rng.standard_normal(S) * 0.02).astype(np.float32)
+
+        def state():
+            return dict(master=dev32(master0), m=torch.zeros(S, device="cuda"), v=torch.zeros(S, device="cuda"),
+                        g=torch.zeros(S, dtype=torch.int16, device="cuda"),
+                        p=torch.zeros(S, dtype=torch.int16, device="cuda"),
+                        full=dev16(np.full(T, SENT, np.uint16)), acc=dev32(master0 * 1e-2))
+
+        a, b = state(), state()
+        coefs = _dev_coefs(zs, [hp])
+        zs.zs_fused_shard_step(plan, hp, cs, a["master"], a["m"], a["v"], grad=a["g"], param=a["p"], full=a["full"])
+        zs.zs_fused_shard_step_dc(plan, coefs, cs, b["master"], b["m"], b["v"], grad=b["g"], param=b["p"],
+                                  full=b["full"])
+        zs.zs_adamw_shard_step(plan, hp.at(8), a["g"], a["master"], a["m"], a["v"], a["p"])
+        coefs8 = _dev_coefs(zs, [hp.at(8)])
+        zs.zs_adamw_shard_step_dc(plan, coefs8, b["g"], b["master"], b["m"], b["v"], b["p"])
+        zs.zs_adamw_shard_step_accum(plan, hp.at(9), a["acc"], 3.0, a["master"], a["m"], a["v"], param=a["p"],
+                                     full=a["full"])
+        zs.zs_adamw_shard_step_accum_dc(plan, _dev_coefs(zs, [hp.at(9)]), b["acc"], 3.0, b["master"], b["m"],
+                                        b["v"], param=b["p"], full=b["full"])
+        torch.cuda.synchronize()
+        for k in a:
+            _same(a[k], b[k], f"N={N}: {k}")
+    # multi-tensor with two hyperparameter groups
+    numels, N, r = [4096 * 3, 512, 1000, 77], 4, 2
+    plan = zs.zs_shard_plan_ex(numels, N, r, groups=[0, 1, 0, 1])
+    oplan = oracle.plan_per_tensor(numels, N, r, 0)
+    sizes = [pc.own_hi - pc.own_lo for pc in oplan.pieces]
+    rng = np.random.default_rng(5)
+    host = [dict(master=(rng.standard_normal(Si) * 0.02).astype(np.float32)) for Si in sizes]
+    contribs = [[dev16(oracle.f32_to_bf16((rng.standard_normal(Si) * 1e-3).astype(np.float32))) for Si in sizes]
+                for _ in range(N)]
+
+    def pieces():
+        return [dict(grad=torch.zeros(Si, dtype=torch.int16, device="cuda"), master=dev32(host[i]["master"]),
+                     m=torch.zeros(Si, device="cuda"), v=torch.zeros(Si, device="cuda"),
+                     param=torch.zeros(Si, dtype=torch.int16, device="cuda"),
+                     full=dev16(np.full(oplan.padded[i], SENT, np.uint16))) for i, Si in enumerate(sizes)]
+
+    pa, pb = pieces(), pieces()
+    wsa = torch.zeros(zs.zs_multi_workspace_bytes(plan, N), dtype=torch.uint8, device="cuda")
+    wsb = torch.zeros_like(wsa)
+    zs.zs_multi_bind(plan, pa, contribs, wsa)
+    zs.zs_multi_bind(plan, pb, contribs, wsb)
+    hps = [hp, zs.AdamWHParams(lr=1e-3, weight_decay=0.0, step=7)]
+    zs.zs_fused_shard_step_multi_groups(plan, hps, wsa)
+    zs.zs_fused_shard_step_multi_dc(plan, _dev_coefs(zs, hps), 2, wsb)
+    torch.cuda.synchronize()
+    for i in range(len(sizes)):
+        for k in pa[i]:
+            _same(pa[i][k], pb[i][k], f"piece {i}: {k}")
+
+
+def test_graph_replays_with_new_scalars(zs):
+    """A training loop on a captured graph: captured once are a copy of the
+    AdamW scalars from page-locked host memory into a device buffer and the
+    fused step that reads them; before each replay the host writes the next
+    step's scalars (t = 1, 2, 3, 4 and a learning-rate change) and new
+    gradients. Every replay equals the eager by-value step with those
+    hyperparameters, and the end state equals the oracle's."""
+    import torch
+    numels, N, r, valid, seed = [1_000_003], 4, 1, 1_000_003, 2718
+    plan = zs.zs_shard_plan(numels, N, r, 1)
+    T, S = plan.padded_numel, plan.shard_numel
+    lo = r * S
+    master0 = synth.cpu_f32(T, 0, synth.spec(seed, synth.STREAM_MASTER, 0, 0.02, valid))[lo:lo + S].copy()
+
+    def grads(k):
+        return [synth.cpu_bf16(T, 0, synth.spec(seed, synth.STREAM_CONTRIB + q, k, 1e-3, valid))[lo:lo + S].copy()
+                for q in range(N)]
+
+    def state():
+        return dict(master=dev32(master0), m=torch.zeros(S, device="cuda"), v=torch.zeros(S, device="cuda"),
+                    p=torch.zeros(S, dtype=torch.int16, device="cuda"), full=dev16(np.full(T, SENT, np.uint16)))
+
+    contribs = [torch.zeros(S, dtype=torch.int16, device="cuda") for _ in range(N)]
+    host_coefs = torch.zeros(9, dtype=torch.float32, pin_memory=True)
+    dev_coefs = torch.zeros(9, dtype=torch.float32, device="cuda")
+    A, B = state(), state()
+
+    def step_dc(d):
+        dev_coefs.copy_(host_coefs, non_blocking=True)
+        zs.zs_fused_shard_step_dc(plan, dev_coefs, contribs, d["master"], d["m"], d["v"], param=d["p"],
+                                  full=d["full"])
+
+    warm = state()
+    host_coefs.copy_(torch.tensor(zs.zs_adamw_coefs_compute(zs.AdamWHParams()).values()))
+    step_dc(warm)
+    torch.cuda.synchronize()
+    graph = _capture(lambda: step_dc(A))
+    o = dict(g=np.zeros(S, np.uint16), master=master0.copy(), m=np.zeros(S, np.float32), v=np.zeros(S, np.float32),
+             p=np.zeros(S, np.uint16), full=np.full(T, SENT, np.uint16))
+    schedule = [(1, 1e-3), (2, 1e-3), (3, 5e-4), (4, 2.5e-4)]
+    for k, (t, lr) in enumerate(schedule, start=1):
+        hp = zs.AdamWHParams(lr=lr, weight_decay=0.1, step=t)
+        gk = grads(k)
+        for q in range(N):
+            contribs[q].copy_(dev16(gk[q]))
+        host_coefs.copy_(torch.tensor(zs.zs_adamw_coefs_compute(hp).values()))
+        torch.cuda.synchronize()
+        graph.replay()
+        zs.zs_fused_shard_step(plan, hp, contribs, B["master"], B["m"], B["v"], param=B["p"], full=B["full"])
+        torch.cuda.synchronize()
+        for key in A:
+            _same(A[key], B[key], f"replay {k}: {key}")
+        oracle.shard_step(oracle.HParams(lr, 0.9, 0.95, 1e-8, 0.1, t), gk, o["g"], o["master"], o["m"], o["v"],
+                          o["p"], o["full"], r)
+    nd = check_f32(host32(A["master"]), o["master"], "master") + check_f32(host32(A["m"]), o["m"], "m")
+    nd += check_f32(host32(A["v"]), o["v"], "v") + check_bf16(host16(A["p"]), o["p"], "param")
+    assert np.array_equal(host16(A["full"]), o["full"])
     assert nd == 0
