@@ -501,6 +501,8 @@ zs_status zs_dequant_gather(const zs_plan* plan, int32_t bits, int32_t block, co
     if (plan->S == 0) return ZS_OK;
     if ((plan->S / 8 + zs::kBlockThreads - 1) / zs::kBlockThreads > INT32_MAX)
         return fail(ZS_EINVAL, "shard of %lld elements is too long for one dequantizing launch", (long long)plan->S);
+    if (plan->world > 65535)  // one launch row per rank: the grid's second dimension
+        return fail(ZS_EINVAL, "the dequantizing gather handles at most 65535 ranks, the plan has %d", plan->world);
     return hip_status(zs::launch_dequant(bits, block, codes_all, scales_all, zs_quant_code_bytes(plan, bits),
                                          zs_quant_num_scales(plan, block), plan->world, full_bf16, plan->S, stream),
                       "dequantize launch");

@@ -333,7 +333,8 @@ zs_status zs_fused_shard_step_quant(const zs_plan* plan, const zs_adamw_hparams*
 
 /* The receiving side: codes_all holds the N ranks' codes end to end (rank q
  * at q * zs_quant_code_bytes), scales_all their scales end to end (rank q at
- * q * zs_quant_num_scales); writes every element of full_bf16[0, T). */
+ * q * zs_quant_num_scales); writes every element of full_bf16[0, T).
+ * N <= 65535. */
 zs_status zs_dequant_gather(const zs_plan* plan, int32_t bits, int32_t block, const void* codes_all,
                             const float* scales_all, void* full_bf16, void* stream);
 

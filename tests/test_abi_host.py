@@ -269,6 +269,13 @@ def test_quant_validation_without_device(zs):
     assert L.zs_quantize_shard(empty.handle, 8, 64, FAKE, FAKE, FAKE, None) == zs.ZS_OK  # nothing to launch
 
 
+def test_dequant_gather_rank_limit(zs):
+    plan = zs.zs_shard_plan([8 * 70000], 70000, 0, 1)
+    L = zs.lib()
+    assert L.zs_dequant_gather(plan.handle, 8, 8, FAKE, FAKE, FAKE, None) == zs.ZS_EINVAL
+    assert "65535" in zs.zs_last_error()
+
+
 def test_plan_workspace_bytes(zs):
     pt = zs.zs_shard_plan([4096, 512, 77], 8, 2, 1, zs.ZS_LAYOUT_PER_TENSOR)
     assert pt.workspace_bytes == zs.zs_multi_workspace_bytes(pt, 8) > 0
