@@ -28,9 +28,10 @@ zs_status fail(zs_status st, const char* fmt, ...) {
 }
 
 constexpr int64_t kMaxElems = int64_t(1) << 60;
-// Largest owned shard: 2^38 elements (512 GiB of bf16, beyond any one GPU's
-// memory) keeps every launch grid within 32-bit block counts.
-constexpr int64_t kMaxShardElems = int64_t(1) << 38;
+// Largest owned shard: 2^34 - 256 elements. A kernel launch covers at most
+// 2^32 - 1 work-items and the step kernels give each work-item 4 elements
+// (16 B/param of state alone is then 256 GiB: about all one MI355X holds).
+constexpr int64_t kMaxShardElems = (int64_t(1) << 34) - 256;
 
 int64_t roundup(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
@@ -215,13 +216,18 @@ zs_status zs_shard_plan_ex(const int64_t* numels, int32_t n_tensors, int32_t wor
             p->S = shard;
             if (shard > kMaxShardElems) {  // checked before the chunk list is built
                 delete p;
-                return fail(ZS_EINVAL, "owned shard of %lld elements exceeds 2^38", (long long)shard);
+                return fail(ZS_EINVAL, "owned shard of %lld elements exceeds the limit of 2^34 - 256",
+                            (long long)shard);
             }
-            static_assert(kMaxShardElems / zs::kChunkElems < INT32_MAX, "chunk count must fit the 32-bit grid");
             int64_t n_chunks = 0;
             for (auto& t : p->tensors) {
                 t.first_chunk = n_chunks;
                 n_chunks += (t.own_hi - t.own_lo + zs::kChunkElems - 1) / zs::kChunkElems;
+            }
+            // one block per chunk: the launch's work-items must stay below 2^32
+            if (n_chunks > (int64_t)UINT32_MAX / zs::kBlockThreads) {
+                delete p;
+                return fail(ZS_EINVAL, "%lld multi-tensor chunks exceed one launch", (long long)n_chunks);
             }
             p->chunk_piece.reserve((size_t)n_chunks);
             for (int32_t i = 0; i < n_tensors; ++i) {
@@ -236,7 +242,7 @@ zs_status zs_shard_plan_ex(const int64_t* numels, int32_t n_tensors, int32_t wor
     if (p->S > kMaxShardElems) {
         const long long S = (long long)p->S;
         delete p;
-        return fail(ZS_EINVAL, "owned shard of %lld elements exceeds 2^38", S);
+        return fail(ZS_EINVAL, "owned shard of %lld elements exceeds the limit of 2^34 - 256", S);
     }
     *out = p;
     return ZS_OK;

@@ -128,8 +128,9 @@ typedef struct zs_tensor_info {
  *   padded tensors (T = sum T_i). tensor_align_elems is ignored.
  * Padding elements are part of the shards; they hold +0 and stay +0 under
  * the step when their contributions are +0.
- * The owned shard may hold at most 2^38 elements (beyond any one GPU's
- * memory; it bounds every launch grid).
+ * The owned shard may hold at most 2^34 - 256 elements (a launch covers at
+ * most 2^32 - 1 work-items of 4 elements; 16 B/param of state for that many
+ * is 256 GiB, about all one MI355X holds).
  * Host only. On success *out owns a new plan; on error *out is untouched. */
 zs_status zs_shard_plan(const int64_t* numels, int32_t n_tensors, int32_t world_size, int32_t rank,
                         int32_t tensor_align_elems, int32_t layout, zs_plan** out);

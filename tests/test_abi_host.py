@@ -148,13 +148,24 @@ def test_plan_rejects_bad_arguments(zs):
 def test_plan_rejects_shards_beyond_any_device(zs):
     with pytest.raises(zs.ZsError) as e:
         zs.zs_shard_plan([1 << 40], 2, 0)
-    assert e.value.status == zs.ZS_EINVAL and "2^38" in e.value.message
-    assert zs.zs_shard_plan([1 << 38], 1, 0).shard_numel == 1 << 38
+    assert e.value.status == zs.ZS_EINVAL and "2^34 - 256" in e.value.message
+    limit = (1 << 34) - 256
+    assert zs.zs_shard_plan([limit], 1, 0).shard_numel == limit
+    assert zs.zs_shard_plan([limit * 4], 4, 3).shard_numel == limit
+    for numels, world in (([limit + 8], 1), ([1 << 34], 1), ([(limit + 8) * 2], 2)):
+        with pytest.raises(zs.ZsError):
+            zs.zs_shard_plan(numels, world, 0)
+    # per-tensor: one block per 256-element chunk, the last of every piece
+    # partial: near the limit, many small pieces push the chunk count past
+    # what one launch covers
+    with pytest.raises(zs.ZsError) as e:
+        zs.zs_shard_plan([limit - 8 * 4000] + [8] * 4000, 1, 0, layout=zs.ZS_LAYOUT_PER_TENSOR)
+    assert "chunks exceed one launch" in e.value.message
     # per-tensor: refused before a chunk list of billions of entries is built
-    for numels in ([1 << 45], [1 << 37, 1 << 37, 1 << 37]):
+    for numels in ([1 << 45], [1 << 33, 1 << 33, 1 << 33]):
         with pytest.raises(zs.ZsError) as e:
             zs.zs_shard_plan(numels, 1, 0, layout=zs.ZS_LAYOUT_PER_TENSOR)
-        assert e.value.status == zs.ZS_EINVAL and "2^38" in e.value.message
+        assert e.value.status == zs.ZS_EINVAL and "2^34 - 256" in e.value.message
 
 
 def test_empty_plan(zs):
