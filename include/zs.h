@@ -127,7 +127,8 @@ typedef struct zs_tensor_info {
  *   its pieces (S = sum S_i) and the packed gathered buffer concatenates the
  *   padded tensors (T = sum T_i). tensor_align_elems is ignored.
  * Padding elements are part of the shards; they hold +0 and stay +0 under
- * the step when their contributions are +0.
+ * the step when their contributions are +0 and eps > 0 (with eps = 0 a zero
+ * gradient over a zero second moment is 0/0 = NaN, as in any AdamW).
  * The owned shard may hold at most 2^34 - 256 elements (a launch covers at
  * most 2^32 - 1 work-items of 4 elements; 16 B/param of state for that many
  * is 256 GiB, about all one MI355X holds).
