@@ -208,3 +208,133 @@ def test_random_per_tensor(zs, seed):
                                                                               f"param[{i}]")
         nd += check_bf16(host16(d["full"]), oi["full"], f"gathered tensor {i}")
     assert nd == 0
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_accum_clip(zs, seed):
+    """G micro-steps (bucketed at random), norm, clip factor and skip, then the
+    step from the accumulator by value or with device scalars; sometimes a
+    NaN in one contribution (the step must be skipped)."""
+    import torch
+    rnd = random.Random(200 + seed)
+    rng = np.random.default_rng(200 + seed)
+    numels = [rnd.choice([9, 4093, 30_011, 70_000]) for _ in range(rnd.randint(1, 4))]
+    world = rnd.choice([1, 2, 4, 5, 8, 64])
+    rank = rnd.randrange(world)
+    plan = zs.zs_shard_plan(numels, world, rank, 1)
+    oplan = oracle.plan_flat(numels, world, rank, 1)
+    T, S = plan.padded_numel, plan.shard_numel
+    lo = rank * S
+    G = rnd.randint(1, 4)
+    max_norm = rnd.choice([1e-4, 1e-2, 1e3])
+    poison = rnd.random() < 0.25
+    master0 = (rng.standard_normal(S) * 0.02).astype(np.float32)
+    micro = []
+    for k in range(G):
+        cs = [_bf16(rng, S, 1e-3) for _ in range(world)]
+        if poison and k == G - 1:
+            cs[0][rnd.randrange(S)] = 0x7FC0
+        micro.append(cs)
+    acc = torch.full((S,), float("nan"), device="cuda")
+    for k in range(G):
+        dc = [dev16(c) for c in micro[k]]
+        B = 8 * rnd.randint(1, max(1, S // 8))
+        for b in range(0, S, B):
+            zs.zs_accumulate_shard(plan, dc, acc, b, min(B, S - b), first=(k == 0))
+    sumsq = torch.zeros(1, dtype=torch.float64, device="cuda")
+    flag = torch.full((1,), 9, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(zs.zs_grad_stats_workspace_bytes(plan), dtype=torch.uint8, device="cuda")
+    zs.zs_grad_stats(plan, acc, float(G), sumsq, flag, ws)
+    scale = torch.zeros(1, device="cuda")
+    skip = torch.full((1,), 9, dtype=torch.int32, device="cuda")
+    zs.zs_clip_scale(sumsq, flag, max_norm, scale, skip)
+    hp = _random_hp(zs, rnd, rnd.choice([1, 3, 100]))
+    master, m, v = dev32(master0), torch.zeros(S, device="cuda"), torch.zeros(S, device="cuda")
+    param = dev16(np.full(S, SENT, np.uint16))
+    full = dev16(np.full(T, SENT, np.uint16))
+    if rnd.random() < 0.5:
+        zs.zs_adamw_shard_step_accum(plan, hp, acc, float(G), master, m, v, scale=scale, skip=skip, param=param,
+                                     full=full)
+    else:
+        zs.zs_adamw_shard_step_accum_dc(plan, _coefs(zs, [hp]), acc, float(G), master, m, v, scale=scale, skip=skip,
+                                        param=param, full=full)
+    torch.cuda.synchronize()
+    o_acc = np.zeros(S, np.float32)
+    for k in range(G):
+        oracle.accumulate(micro[k], o_acc, first=(k == 0))
+    nd = check_f32(host32(acc), o_acc, "acc")
+    o_sumsq, o_flag = oracle.grad_sumsq(o_acc, float(G))
+    assert int(flag.cpu()[0]) == o_flag == (1 if poison else 0)
+    got = float(sumsq.cpu()[0])
+    if not poison:
+        assert abs(got - o_sumsq) <= 1e-12 * o_sumsq
+        assert float(scale.cpu()[0]) == oracle.clip_scale([got], max_norm)
+    assert int(skip.cpu()[0]) == o_flag
+    om, ov, op = np.zeros(S, np.float32), np.zeros(S, np.float32), np.full(S, SENT, np.uint16)
+    omaster = master0.copy()
+    oracle.adamw_f32grad(_ohp(hp), o_acc, float(G), float(scale.cpu()[0]), o_flag, omaster, om, ov, op)
+    nd += check_f32(host32(master), omaster, "master") + check_f32(host32(m), om, "m") + check_f32(host32(v), ov, "v")
+    nd += check_bf16(host16(param), op, "param")
+    f_o = np.full(T, SENT, np.uint16)
+    if not poison:
+        f_o[lo:lo + S] = op
+    nd += check_bf16(host16(full), f_o, "gathered buffer")
+    assert nd == 0
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_quant(zs, seed):
+    """The fused step writing codes (one- or two-pass, grad/param optional) on
+    random shards with special blocks, then the dequantizing gather of every
+    rank's payload."""
+    import torch
+    rnd = random.Random(300 + seed)
+    rng = np.random.default_rng(300 + seed)
+    numels = [rnd.choice([9, 4093, 30_011, 70_000]) for _ in range(rnd.randint(1, 4))]
+    world = rnd.choice([1, 3, 4, 8, 64])
+    rank = rnd.randrange(world)
+    bits, block = rnd.choice([4, 8]), rnd.choice([8, 32, 128, 256])
+    plan = zs.zs_shard_plan(numels, world, rank, 1)
+    T, S = plan.padded_numel, plan.shard_numel
+    master0 = (rng.standard_normal(S) * 0.02).astype(np.float32)
+    if S >= 64:
+        master0[:8] = 0.0  # an all-zero first block at B = 8
+        master0[rnd.randrange(S)] = np.float32(np.inf) if rnd.random() < 0.3 else master0[0]
+    cs = [_bf16(rng, S, 1e-3) for _ in range(world)]
+    hp = _random_hp(zs, rnd, rnd.choice([1, 2, 9]))
+    hp.eps = 1e-8  # keep padding finite
+    nq, ns = zs.zs_quant_code_bytes(plan, bits), zs.zs_quant_num_scales(plan, block)
+    codes = torch.zeros(nq, dtype=torch.uint8, device="cuda")
+    scales = torch.zeros(ns, dtype=torch.float32, device="cuda")
+    master, m, v = dev32(master0), torch.zeros(S, device="cuda"), torch.zeros(S, device="cuda")
+    grad = dev16(np.full(S, SENT, np.uint16)) if rnd.random() < 0.5 else None
+    param = dev16(np.full(S, SENT, np.uint16)) if rnd.random() < 0.5 else None
+    zs.zs_fused_shard_step_quant(plan, hp, [dev16(c) for c in cs], master, m, v, bits, block, codes, scales, grad=grad,
+                                 param=param)
+    g = np.zeros(S, np.uint16)
+    oracle.reduce(cs, out=g)
+    om, ov, op = np.zeros(S, np.float32), np.zeros(S, np.float32), np.zeros(S, np.uint16)
+    omaster = master0.copy()
+    oracle.adamw(_ohp(hp), g, omaster, om, ov, op)
+    q, sc = oracle.quantize(op, bits, block)
+    torch.cuda.synchronize()
+    nd = check_f32(host32(master), omaster, "master") + check_f32(host32(m), om, "m") + check_f32(host32(v), ov, "v")
+    if grad is not None:
+        nd += check_bf16(host16(grad), g, "grad")
+    if param is not None:
+        nd += check_bf16(host16(param), op, "param")
+    assert np.array_equal(codes.cpu().numpy(), q), "codes"
+    got_sc = scales.cpu().numpy()
+    assert np.array_equal(np.isnan(got_sc), np.isnan(sc))
+    assert np.array_equal(got_sc[~np.isnan(sc)].view(np.uint32), sc[~np.isnan(sc)].view(np.uint32)), "scales"
+    # every rank's payload (this rank's with its bytes rotated stands in for the others)
+    payload_q = [np.roll(q, 3 * r) for r in range(world)]
+    payload_s = [np.roll(sc, r) for r in range(world)]
+    full = dev16(np.full(T + 64, SENT, np.uint16))
+    zs.zs_dequant_gather(plan, bits, block, torch.from_numpy(np.concatenate(payload_q)).cuda(),
+                         dev32(np.concatenate(payload_s)), full)
+    ref = oracle.dequant_gather(np.concatenate(payload_q), np.concatenate(payload_s), S, world, bits, block)
+    got = host16(full)
+    nd += check_bf16(got[:T], ref, "gathered buffer")
+    assert np.all(got[T:] == SENT)
+    assert nd == 0
