@@ -1,9 +1,11 @@
 // Host side of the C ABI: shard plan, argument validation, error reporting
 // and the multi-tensor workspace binding. Every device-touching entry point
 // validates all of its arguments before it enqueues anything.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -80,6 +82,28 @@ zs_status check_contribs(const zs_plan* plan, const void* const* contribs, int32
         if (!aligned16(contribs[q])) return fail(ZS_EALIGN, "contribs[%d] is not 16-byte aligned", q);
     }
     return ZS_OK;
+}
+
+// Per-call trace, on when ZS_LOG is set (and not "0"): one line on stderr for
+// every call that enqueues work, with a process-wide sequence number, the
+// entry point, the plan's world size and rank, the contributions and the
+// range it covers, and the stream -- enough to line a stuck or failing step
+// up with the other ranks' logs.
+bool log_enabled() {
+    static const bool on = [] {
+        const char* e = std::getenv("ZS_LOG");
+        return e && *e && std::strcmp(e, "0") != 0;
+    }();
+    return on;
+}
+
+std::atomic<uint64_t> g_seq{0};
+
+void trace(const char* op, const zs_plan* p, int32_t n_contribs, int64_t off, int64_t len, const void* stream) {
+    if (!log_enabled()) return;
+    std::fprintf(stderr, "zs %llu %s world=%d rank=%d contribs=%d off=%lld len=%lld stream=%p\n",
+                 (unsigned long long)++g_seq, op, p ? p->world : -1, p ? p->rank : -1, n_contribs, (long long)off,
+                 (long long)len, stream);
 }
 
 zs_status hip_status(int err, const char* what) {
@@ -314,6 +338,7 @@ zs_status zs_reduce_shard(const zs_plan* plan, const void* const* contribs, int3
     if (len == 0) return ZS_OK;
     const void* shifted[ZS_MAX_CONTRIBS];
     for (int32_t q = 0; q < n_contribs; ++q) shifted[q] = static_cast<const char*>(contribs[q]) + 2 * off;
+    trace("zs_reduce_shard", plan, n_contribs, off, len, stream);
     return hip_status(zs::launch_reduce(shifted, n_contribs, static_cast<char*>(grad_bf16) + 2 * off, len, stream),
                       "reduce launch");
 }
@@ -330,6 +355,7 @@ zs_status adamw_impl(const zs_plan* plan, const zs::AdamCoef& c, const zs::AdamC
     if (zs_status st = check_ptr(v, "v")) return st;
     if (zs_status st = check_ptr(param_bf16, "param_bf16")) return st;
     if (plan->S == 0) return ZS_OK;
+    trace(cdev ? "zs_adamw_shard_step_dc" : "zs_adamw_shard_step", plan, 0, 0, plan->S, stream);
     return hip_status(zs::launch_adamw(c, grad_bf16, master, m, v, param_bf16, nullptr, plan->S, stream, nullptr, cdev),
                       "adamw launch");
 }
@@ -369,6 +395,7 @@ zs_status zs_gather_params(const zs_plan* plan, const void* param_bf16, void* fu
     if (zs_status st = check_ptr(full_bf16, "full_bf16")) return st;
     if (plan->S == 0) return ZS_OK;
     char* own = static_cast<char*>(full_bf16) + 2 * (int64_t)plan->rank * plan->S;
+    trace("zs_gather_params", plan, 0, 0, plan->S, stream);
     return hip_status(zs::launch_gather(param_bf16, own, plan->S, stream), "gather launch");
 }
 
@@ -429,6 +456,7 @@ zs_status fused_impl(const zs_plan* plan, const zs::AdamCoef& c, const zs::AdamC
     for (int32_t q = 0; q < n_contribs; ++q) shifted[q] = static_cast<const char*>(contribs[q]) + 2 * off;
     auto at16 = [off](void* p) { return p ? static_cast<void*>(static_cast<char*>(p) + 2 * off) : nullptr; };
     char* own = full_bf16 ? static_cast<char*>(full_bf16) + 2 * ((int64_t)plan->rank * plan->S + off) : nullptr;
+    trace(cdev ? "zs_fused_shard_step_dc" : "zs_fused_shard_step", plan, n_contribs, off, len, stream);
     return hip_status(zs::launch_fused(c, shifted, n_contribs, master + off, m + off, v + off, at16(grad_bf16),
                                        at16(param_bf16), own, len, stream, nullptr, cdev),
                       "fused launch");
@@ -474,6 +502,7 @@ zs_status zs_quantize_shard(const zs_plan* plan, int32_t bits, int32_t block, co
     if (zs_status st = check_ptr(scales, "scales")) return st;
     if (plan->S == 0) return ZS_OK;
     const zs::QuantOut q{codes, scales, bits, block};
+    trace("zs_quantize_shard", plan, 0, 0, plan->S, stream);
     return hip_status(zs::launch_quantize(q, param_bf16, plan->S, stream), "quantize launch");
 }
 
@@ -493,6 +522,7 @@ zs_status zs_fused_shard_step_quant(const zs_plan* plan, const zs_adamw_hparams*
     if (zs_status st = check_ptr(scales, "scales")) return st;
     if (plan->S == 0) return ZS_OK;
     const zs::QuantOut q{codes, scales, bits, block};
+    trace("zs_fused_shard_step_quant", plan, n_contribs, 0, plan->S, stream);
     return hip_status(zs::launch_fused(zs::make_coef(*hp), contribs, n_contribs, master, m, v, grad_bf16, param_bf16,
                                        nullptr, plan->S, stream, &q),
                       "fused quantized launch");
@@ -509,6 +539,7 @@ zs_status zs_dequant_gather(const zs_plan* plan, int32_t bits, int32_t block, co
         return fail(ZS_EINVAL, "shard of %lld elements is too long for one dequantizing launch", (long long)plan->S);
     if (plan->world > 65535)  // one launch row per rank: the grid's second dimension
         return fail(ZS_EINVAL, "the dequantizing gather handles at most 65535 ranks, the plan has %d", plan->world);
+    trace("zs_dequant_gather", plan, plan->world, 0, plan->S, stream);
     return hip_status(zs::launch_dequant(bits, block, codes_all, scales_all, zs_quant_code_bytes(plan, bits),
                                          zs_quant_num_scales(plan, block), plan->world, full_bf16, plan->S, stream),
                       "dequantize launch");
@@ -567,6 +598,7 @@ zs_status zs_offload_adamw_step(const zs_plan* plan, const zs_adamw_hparams* hp,
         return fail(ZS_EINVAL, "grad_bf16_host and param_bf16_host must be page-locked host memory "
                                "(hipHostMalloc, or a pinned tensor)");
     char* own = full_bf16_dev ? static_cast<char*>(full_bf16_dev) + 2 * (int64_t)plan->rank * plan->S : nullptr;
+    trace("zs_offload_adamw_step", plan, 0, 0, plan->S, stream);
     return hip_status(zs::offload_adamw(zs::make_coef(*hp), grad_bf16_dev, master_host, m_host, v_host,
                                         grad_bf16_host, param_bf16_host, param_bf16_dev, own, plan->S, chunk_elems,
                                         n_threads, stream),
@@ -586,6 +618,7 @@ zs_status zs_accumulate_shard(const zs_plan* plan, const void* const* contribs, 
     if (len == 0) return ZS_OK;
     const void* shifted[ZS_MAX_CONTRIBS];
     for (int32_t q = 0; q < n_contribs; ++q) shifted[q] = static_cast<const char*>(contribs[q]) + 2 * off;
+    trace("zs_accumulate_shard", plan, n_contribs, off, len, stream);
     return hip_status(zs::launch_accumulate(shifted, n_contribs, acc_f32 + off, first ? 1 : 0, len, stream),
                       "accumulate launch");
 }
@@ -610,6 +643,7 @@ zs_status zs_grad_stats(const zs_plan* plan, const float* acc_f32, float grad_di
     if (workspace_bytes < need)
         return fail(ZS_ENOMEM, "workspace holds %lld bytes, zs_grad_stats needs %lld", (long long)workspace_bytes,
                     (long long)need);
+    trace("zs_grad_stats", plan, 0, 0, plan->S, stream);
     return hip_status(zs::launch_grad_stats(acc_f32, grad_divisor, sumsq_out, nonfinite_out, workspace, plan->S, stream),
                       "grad stats launch");
 }
@@ -622,6 +656,7 @@ zs_status zs_clip_scale(const double* sumsq, const int32_t* nonfinite, int32_t n
         return fail(ZS_EALIGN, "sumsq needs 8-byte, the others 4-byte alignment");
     if (n_ranks < 1) return fail(ZS_EINVAL, "n_ranks = %d must be >= 1", n_ranks);
     if (!std::isfinite(max_norm) || max_norm <= 0.0) return fail(ZS_EINVAL, "max_norm = %g must be positive", max_norm);
+    trace("zs_clip_scale", nullptr, n_ranks, 0, 0, stream);
     return hip_status(zs::launch_clip_scale(sumsq, nonfinite, n_ranks, max_norm, scale_out, skip_out, stream),
                       "clip scale launch");
 }
@@ -645,6 +680,7 @@ zs_status accum_step_impl(const zs_plan* plan, const zs::AdamCoef& c, const zs::
         return fail(ZS_EINVAL, "a gather into full_bf16 needs a FLAT plan");
     if (plan->S == 0) return ZS_OK;
     char* own = full_bf16 ? static_cast<char*>(full_bf16) + 2 * (int64_t)plan->rank * plan->S : nullptr;
+    trace(cdev ? "zs_adamw_shard_step_accum_dc" : "zs_adamw_shard_step_accum", plan, 0, 0, plan->S, stream);
     return hip_status(zs::launch_adamw_accum(c, acc_f32, grad_divisor, scale, skip, master, m, v, param_bf16, own,
                                              plan->S, stream, cdev),
                       "adamw accum launch");
@@ -807,6 +843,7 @@ zs_status zs_multi_bind(const zs_plan* plan, const zs_piece_ptrs* pieces, const 
         for (int32_t q = 0; q < n_contribs; ++q) cd[(int64_t)i * n_contribs + q] = contribs[(int64_t)q * n + i];
     }
     std::memcpy(host.data() + L.chunks_off, plan->chunk_piece.data(), plan->chunk_piece.size() * sizeof(int32_t));
+    trace("zs_multi_bind", plan, n_contribs, 0, plan->S, stream);
     if (zs_status st = hip_status(zs::copy_h2d_sync(workspace, host.data(), L.total, stream), "workspace copy"))
         return st;
     std::lock_guard<std::mutex> lk(g_bind_mu);
@@ -821,6 +858,7 @@ zs_status zs_multi_unbind(void* workspace, void* stream) {
         if (g_bind.erase(workspace) == 0) return fail(ZS_EINVAL, "workspace %p is not bound", workspace);
     }
     const uint64_t zero = 0;  // clear the table's magic: later launches on it do nothing
+    trace("zs_multi_unbind", nullptr, 0, 0, 0, stream);
     return hip_status(zs::copy_h2d_sync(workspace, &zero, sizeof zero, stream), "workspace clear");
 }
 
@@ -828,6 +866,7 @@ zs_status zs_reduce_shard_multi(const zs_plan* plan, const void* workspace, void
     if (zs_status st = check_multi_plan(plan)) return st;
     Binding b;
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasContribs | zs::kHasGrad, &b)) return st;
+    trace("zs_reduce_shard_multi", plan, b.n_contribs, 0, plan->S, stream);
     return hip_status(zs::launch_multi(zs::kOpReduce, nullptr, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunk_piece.size(), b.n_contribs, stream),
                       "multi reduce launch");
 }
@@ -840,6 +879,7 @@ zs_status zs_adamw_shard_step_multi(const zs_plan* plan, const zs_adamw_hparams*
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasGrad | zs::kHasState, &b)) return st;
     zs::CoefTable ct;
     for (auto& e : ct.c) e = zs::make_coef(*hp);
+    trace("zs_adamw_shard_step_multi", plan, b.n_contribs, 0, plan->S, stream);
     return hip_status(zs::launch_multi(zs::kOpAdamw, &ct, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunk_piece.size(), b.n_contribs, stream),
                       "multi adamw launch");
 }
@@ -848,6 +888,7 @@ zs_status zs_gather_params_multi(const zs_plan* plan, const void* workspace, voi
     if (zs_status st = check_multi_plan(plan)) return st;
     Binding b;
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasParam | zs::kHasFull, &b)) return st;
+    trace("zs_gather_params_multi", plan, b.n_contribs, 0, plan->S, stream);
     return hip_status(zs::launch_multi(zs::kOpGather, nullptr, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunk_piece.size(), b.n_contribs, stream),
                       "multi gather launch");
 }
@@ -860,6 +901,7 @@ zs_status zs_fused_shard_step_multi(const zs_plan* plan, const zs_adamw_hparams*
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasContribs | zs::kHasState, &b)) return st;
     zs::CoefTable ct;
     for (auto& e : ct.c) e = zs::make_coef(*hp);
+    trace("zs_fused_shard_step_multi", plan, b.n_contribs, 0, plan->S, stream);
     return hip_status(zs::launch_multi(zs::kOpFused, &ct, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunk_piece.size(), b.n_contribs, stream),
                       "multi fused launch");
 }
@@ -889,6 +931,7 @@ zs_status zs_adamw_shard_step_multi_groups(const zs_plan* plan, const zs_adamw_h
     if (zs_status st = group_table(plan, hps, n_groups, &ct)) return st;
     Binding b;
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasGrad | zs::kHasState, &b)) return st;
+    trace("zs_adamw_shard_step_multi", plan, b.n_contribs, 0, plan->S, stream);
     return hip_status(zs::launch_multi(zs::kOpAdamw, &ct, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunk_piece.size(), b.n_contribs, stream),
                       "multi adamw launch");
 }
@@ -905,6 +948,7 @@ zs_status zs_fused_shard_step_multi_dc(const zs_plan* plan, const zs_adamw_coefs
     Binding b;
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasContribs | zs::kHasState, &b)) return st;
     const zs::CoefTable unused{};
+    trace("zs_fused_shard_step_multi", plan, b.n_contribs, 0, plan->S, stream);
     return hip_status(zs::launch_multi(zs::kOpFused, &unused, workspace, multi_offsets(plan, b.n_contribs),
                                        (int)plan->chunk_piece.size(), b.n_contribs, stream, dev_coef(coefs)),
                       "multi fused launch");
@@ -917,6 +961,7 @@ zs_status zs_fused_shard_step_multi_groups(const zs_plan* plan, const zs_adamw_h
     if (zs_status st = group_table(plan, hps, n_groups, &ct)) return st;
     Binding b;
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasContribs | zs::kHasState, &b)) return st;
+    trace("zs_fused_shard_step_multi", plan, b.n_contribs, 0, plan->S, stream);
     return hip_status(zs::launch_multi(zs::kOpFused, &ct, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunk_piece.size(), b.n_contribs, stream),
                       "multi fused launch");
 }

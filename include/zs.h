@@ -53,6 +53,11 @@
  * Errors: a call that returns anything but ZS_OK has enqueued nothing and
  * changed nothing (except a ZS_EHIP in the middle of zs_offload_adamw_step's
  * pipeline); zs_last_error() then returns a thread-local description.
+ *
+ * Trace: with ZS_LOG set in the environment (to anything but "0"), every call
+ * that enqueues work writes one line to stderr: a process-wide sequence
+ * number, the entry point, the plan's world size and rank, the number of
+ * contributions, the element range and the stream.
  */
 #ifndef ZS_H
 #define ZS_H

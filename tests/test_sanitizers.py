@@ -56,11 +56,35 @@ def test_oracle_under_asan_ubsan(tmp_path):
     assert "oracle driver ok" in _run(exe)
 
 
-def test_host_library_under_asan_ubsan(tmp_path):
-    exe = str(tmp_path / "host_san")
+@pytest.fixture(scope="module")
+def host_asan(tmp_path_factory):
+    exe = str(tmp_path_factory.mktemp("host") / "host_san")
     _build(["g++", "-std=c++17", "-O1", "-g", "-ffp-contract=off", "-pthread", *ASAN_UBSAN,
             f"-I{os.path.join(ROOT, 'include')}", *_host_sources(), "-o", exe])
-    assert "host driver ok (all)" in _run(exe, "all")
+    return exe
+
+
+def test_host_library_under_asan_ubsan(host_asan):
+    assert "host driver ok (all)" in _run(host_asan, "all")
+
+
+def test_call_trace(host_asan):
+    """ZS_LOG=1: one stderr line per call that enqueues work, numbered in
+    order, naming the entry point, world size, rank, contributions and range."""
+    env = dict(os.environ, ZS_LOG="1")
+    res = subprocess.run([host_asan, "all"], capture_output=True, text=True, env=env, timeout=600)
+    assert res.returncode == 0, res.stderr[-4000:]
+    lines = [ln for ln in res.stderr.splitlines() if ln.startswith("zs ")]
+    seqs = [int(ln.split()[1]) for ln in lines]
+    assert seqs == list(range(1, len(seqs) + 1))
+    ops = {ln.split()[2] for ln in lines}
+    for op in ("zs_reduce_shard", "zs_fused_shard_step", "zs_fused_shard_step_dc", "zs_accumulate_shard",
+               "zs_grad_stats", "zs_clip_scale", "zs_multi_bind", "zs_fused_shard_step_multi", "zs_multi_unbind"):
+        assert op in ops, (op, sorted(ops))
+    assert any("zs_reduce_shard world=4 rank=1 contribs=4 off=0" in ln for ln in lines)
+    # off by default: no trace lines
+    res = subprocess.run([host_asan, "all"], capture_output=True, text=True, timeout=600)
+    assert not [ln for ln in res.stderr.splitlines() if ln.startswith("zs ")]
 
 
 def test_host_library_under_tsan(tmp_path):
