@@ -396,3 +396,15 @@ def test_device_scalar_calls_validate_without_device(zs):
     assert L.zs_fused_shard_step_multi_dc(pt.handle, FAKE, 1, FAKE, None) == zs.ZS_EINVAL  # never bound
     assert b"never bound" in L.zs_last_error()
     assert L.zs_fused_shard_step_multi_dc(h, FAKE, 1, FAKE, None) == zs.ZS_EINVAL  # FLAT plan
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """No fallback path: without the built library the binding raises on
+    import, and so does everything that runs the step through it."""
+    import subprocess
+    import sys
+    env = dict(os.environ, ZS_LIB=str(tmp_path / "missing" / "libzs.so"))
+    res = subprocess.run([sys.executable, "-c", "import fsdp_sharded_mixed_flatten_amd"], cwd=ROOT, env=env,
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode != 0
+    assert "ImportError" in res.stderr and "is not built" in res.stderr, res.stderr
