@@ -6,23 +6,28 @@
  *   zs_c_step IN OUT
  *
  * IN (little-endian, packed):
- *   int64  n_tensors, world, rank, align, steps, S
+ *   int64  n_tensors, world, rank, align, steps, S, layout
  *   int64  numels[n_tensors]
  *   double lr, beta1, beta2, eps, weight_decay
  *   uint16 contributions[steps][world][S]   (bf16 bits; rank q's gradient
- *                                            restricted to the owned range)
+ *                                            restricted to the owned elements,
+ *                                            in shard order)
  *   float  master[S]                        (initial fp32 master shard; m = v = 0)
  * OUT:
  *   int64  T, S
  *   float  master[S], m[S], v[S]
  *   uint16 grad[S], param[S], full[T]       (full starts as 0x5A5A everywhere)
  *
+ * The owned shard lives in one allocation per array in both layouts; with
+ * the PER_TENSOR layout every piece points into them at its shard offset and
+ * into `full` (the tensors' gathered buffers, packed) at its tensor's offset.
  * Step t (1-based) takes one of three routes, all of which must give the
  * same bytes: t % 3 == 1 the fused call, t % 3 == 2 the unfused calls
- * (reduce in two buckets, AdamW, gather), t % 3 == 0 the fused call with its
- * scalars read from device memory. Before the steps, an invalid plan request
- * must fail with ZS_EINVAL and a message. Exit status 0 on success, 1 on any
- * failure (the failing call and zs_last_error() on stderr), 2 on bad usage. */
+ * (FLAT: reduce in two buckets, AdamW, gather), t % 3 == 0 the fused call
+ * with its scalars read from device memory. Before the steps, an invalid plan
+ * request must fail with ZS_EINVAL and a message. Exit status 0 on success,
+ * 1 on any failure (the failing call and zs_last_error() on stderr), 2 on bad
+ * usage. */
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -89,12 +94,13 @@ int main(int argc, char** argv) {
         perror(argv[1]);
         return 1;
     }
-    int64_t hdr[6];
+    int64_t hdr[7];
     read_exact(in, hdr, sizeof hdr, "header");
     const int32_t n_tensors = (int32_t)hdr[0], world = (int32_t)hdr[1], rank = (int32_t)hdr[2];
-    const int32_t align = (int32_t)hdr[3], steps = (int32_t)hdr[4];
+    const int32_t align = (int32_t)hdr[3], steps = (int32_t)hdr[4], layout = (int32_t)hdr[6];
     const int64_t S_file = hdr[5];
-    if (n_tensors < 1 || world < 1 || world > ZS_MAX_CONTRIBS || steps < 1 || S_file < 0) {
+    if (n_tensors < 1 || world < 1 || world > ZS_MAX_CONTRIBS || steps < 1 || S_file < 0 ||
+        (layout != ZS_LAYOUT_FLAT && layout != ZS_LAYOUT_PER_TENSOR)) {
         fprintf(stderr, "bad header\n");
         return 1;
     }
@@ -113,9 +119,9 @@ int main(int argc, char** argv) {
     printf("expected error: %s\n", zs_last_error());
 
     zs_plan* plan = NULL;
-    ZS_CHECK(zs_shard_plan(numels, n_tensors, world, rank, align, ZS_LAYOUT_FLAT, &plan));
+    ZS_CHECK(zs_shard_plan(numels, n_tensors, world, rank, align, layout, &plan));
     const int64_t T = zs_plan_padded_numel(plan), S = zs_plan_shard_numel(plan);
-    if (S != S_file || T != S * world) {
+    if (S != S_file || (layout == ZS_LAYOUT_FLAT && T != S * world)) {
         fprintf(stderr, "plan gives S = %lld, T = %lld; the input holds S = %lld\n", (long long)S, (long long)T,
                 (long long)S_file);
         return 1;
@@ -146,6 +152,32 @@ int main(int argc, char** argv) {
     HIP_CHECK(hipMemsetD16((hipDeviceptr_t)full, 0x5A5A, (size_t)T));
     HIP_CHECK(hipDeviceSynchronize());
 
+    /* PER_TENSOR: the pieces' pointers into the shard arrays and the packed
+     * gathered buffers, and the bound multi-tensor table */
+    void* ws = NULL;
+    if (layout == ZS_LAYOUT_PER_TENSOR) {
+        zs_piece_ptrs* pieces = (zs_piece_ptrs*)host_alloc(sizeof(zs_piece_ptrs) * (size_t)n_tensors);
+        const void** cptr = (const void**)host_alloc(sizeof(void*) * (size_t)n_tensors * (size_t)world);
+        for (int32_t i = 0; i < n_tensors; ++i) {
+            zs_tensor_info ti;
+            ZS_CHECK(zs_plan_tensor(plan, i, &ti));
+            const int64_t o = ti.shard_off;
+            pieces[i].grad = (char*)grad + 2 * o;
+            pieces[i].master = master + o;
+            pieces[i].m = m + o;
+            pieces[i].v = v + o;
+            pieces[i].param = (char*)param + 2 * o;
+            pieces[i].full = (char*)full + 2 * ti.flat_off;
+            for (int32_t q = 0; q < world; ++q)
+                cptr[(size_t)q * (size_t)n_tensors + (size_t)i] = (const char*)contribs_d[q] + 2 * o;
+        }
+        const int64_t ws_bytes = zs_multi_workspace_bytes(plan, world);
+        ws = dev_alloc((size_t)ws_bytes);
+        ZS_CHECK(zs_multi_bind(plan, pieces, cptr, world, ws, ws_bytes, stream));
+        free(pieces);
+        free(cptr);
+    }
+
     const int64_t half = S / 16 * 8; /* first bucket: a multiple of 8 */
     for (int32_t t = 1; t <= steps; ++t) {
         for (int32_t q = 0; q < world; ++q)
@@ -153,7 +185,20 @@ int main(int argc, char** argv) {
                                      b16, hipMemcpyHostToDevice, stream));
         const zs_adamw_hparams hp = {h[0], h[1], h[2], h[3], h[4], t};
         const void* const* cs = (const void* const*)contribs_d;
-        if (t % 3 == 1) {
+        if (layout == ZS_LAYOUT_PER_TENSOR) {
+            if (t % 3 == 1) {
+                ZS_CHECK(zs_fused_shard_step_multi(plan, &hp, ws, stream));
+            } else if (t % 3 == 2) {
+                ZS_CHECK(zs_reduce_shard_multi(plan, ws, stream));
+                ZS_CHECK(zs_adamw_shard_step_multi(plan, &hp, ws, stream));
+                ZS_CHECK(zs_gather_params_multi(plan, ws, stream));
+            } else {
+                zs_adamw_coefs c;
+                ZS_CHECK(zs_adamw_coefs_compute(&hp, &c));
+                HIP_CHECK(hipMemcpyAsync(coefs_d, &c, sizeof c, hipMemcpyHostToDevice, stream));
+                ZS_CHECK(zs_fused_shard_step_multi_dc(plan, coefs_d, 1, ws, stream));
+            }
+        } else if (t % 3 == 1) {
             ZS_CHECK(zs_fused_shard_step(plan, &hp, cs, world, master, m, v, grad, param, full, stream));
         } else if (t % 3 == 2) {
             ZS_CHECK(zs_reduce_shard(plan, cs, world, grad, 0, half, stream));
@@ -195,6 +240,10 @@ int main(int argc, char** argv) {
         return 1;
     }
 
+    if (ws) {
+        ZS_CHECK(zs_multi_unbind(ws, stream));
+        HIP_CHECK(hipFree(ws));
+    }
     for (int32_t q = 0; q < world; ++q) HIP_CHECK(hipFree(contribs_d[q]));
     HIP_CHECK(hipFree(master));
     HIP_CHECK(hipFree(m));
@@ -211,6 +260,7 @@ int main(int argc, char** argv) {
     free(out32);
     free(out16);
     free(numels);
-    printf("ok: %d steps, T = %lld, S = %lld, world = %d, rank = %d\n", steps, (long long)T, (long long)S, world, rank);
+    printf("ok: %s layout, %d steps, T = %lld, S = %lld, world = %d, rank = %d\n",
+           layout == ZS_LAYOUT_FLAT ? "FLAT" : "PER_TENSOR", steps, (long long)T, (long long)S, world, rank);
     return 0;
 }
