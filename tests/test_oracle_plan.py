@@ -117,6 +117,16 @@ def test_norm_768_over_64():
     assert reals[47].real_hi - reals[47].real_lo == 16 and reals[48].real_hi == reals[48].real_lo
 
 
+def _tiles(spans, total):
+    """True when the [start, end) spans, in order, cover [0, total) with no gap or overlap."""
+    pos = 0
+    for a, b in sorted(spans):
+        if a != pos or b < a:
+            return False
+        pos = b
+    return pos == total
+
+
 @pytest.mark.parametrize("seed", range(20))
 def test_brute_force_coverage(seed):
     rnd = random.Random(seed)
@@ -127,9 +137,24 @@ def test_brute_force_coverage(seed):
     for layout in ("flat", "per_tensor"):
         cover = {}
         Ss = set()
+        gathered = []  # every rank's pieces as [start, end) of the gathered buffer
         for r in range(world):
             p = plan_flat(numels, world, r, align) if layout == "flat" else plan_per_tensor(numels, world, r)
             Ss.add(p.S)
+            for pc in p.pieces:
+                n_pc = pc.own_hi - pc.own_lo
+                gathered.append((pc.full_off, pc.full_off + n_pc))
+                if layout == "flat":
+                    # the gather writes the shard at r*S: a piece's two coordinates agree
+                    assert pc.full_off == r * p.S + pc.shard_off
+                else:
+                    # inside its tensor's padded span, at the r-th of its N equal slices
+                    Ti = p.padded[pc.tensor]
+                    assert pc.full_off == p.offsets[pc.tensor] + r * (Ti // world)
+            if layout == "per_tensor":
+                # tensors packed in order; the pieces tile the shard
+                assert p.offsets == [sum(p.padded[:i]) for i in range(len(numels))]
+                assert _tiles([(pc.shard_off, pc.shard_off + pc.own_hi - pc.own_lo) for pc in p.pieces], p.S)
             assert p.T == world * p.S and p.S % 8 == 0
             if layout == "flat":
                 assert p.T % (8 * world) == 0
@@ -146,6 +171,12 @@ def test_brute_force_coverage(seed):
                     cover[key] = r
         assert len(Ss) == 1
         assert len(cover) == sum(numels)
+        # across the ranks, pieces never overlap in the gathered buffer; with
+        # per-tensor sharding they tile all of it, padding included
+        gathered.sort()
+        assert all(b0 <= a1 for (_a0, b0), (a1, _b1) in zip(gathered, gathered[1:]))
+        if layout == "per_tensor":
+            assert _tiles(gathered, p.T)
 
 
 def _units(sizes, per_block, n_layers=32, per_layer=9):

@@ -51,12 +51,23 @@ def test_coverage_with_threshold(seed):
     world = rnd.choice([1, 2, 3, 4, 8])
     thr = rnd.choice([0, 8, 100, 1000, 10_000])
     owners = {}
+    written = {}  # gathered-buffer position -> ranks whose piece writes it
     for r in range(world):
         p = plan_per_tensor(numels, world, r, thr)
         assert p.S % 8 == 0 and p.persistent_bytes == 16 * p.S
         for pc in p.pieces:
             for k in range(pc.real_lo, pc.real_hi):
                 owners.setdefault((pc.tensor, k), []).append(r)
+            assert p.offsets[pc.tensor] <= pc.full_off
+            assert pc.full_off + pc.own_hi - pc.own_lo <= p.offsets[pc.tensor] + p.padded[pc.tensor]
+            for x in range(pc.full_off, pc.full_off + pc.own_hi - pc.own_lo):
+                written.setdefault(x, []).append(r)
+    # every position of the gathered buffer is written: by every rank for a
+    # replicated tensor, by exactly one rank otherwise
+    assert sorted(written) == list(range(p.T))
+    for i, (o, Ti) in enumerate(zip(p.offsets, p.padded)):
+        for x in range(o, o + Ti):
+            assert written[x] == (list(range(world)) if numels[i] < thr else written[x][:1]), (i, x)
     for (i, k), rs in owners.items():
         if numels[i] < thr:
             assert rs == list(range(world))
