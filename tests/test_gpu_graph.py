@@ -388,3 +388,78 @@ def test_graph_replays_with_new_scalars(zs):
     nd += check_f32(host32(A["v"]), o["v"], "v") + check_bf16(host16(A["p"]), o["p"], "param")
     assert np.array_equal(host16(A["full"]), o["full"])
     assert nd == 0
+
+
+def test_quantized_step_and_gather_in_graph(zs):
+    """The quantized parameter gather captured whole: the fused step writes
+    this rank's codes and scales straight into its slot of the all-ranks
+    payload, and the dequantizing gather decodes every rank's slot into the
+    gathered buffer. Before each replay the other ranks' payloads change (as
+    a new all-gather would deliver them) together with the gradients."""
+    import torch
+    bits, B = 4, 64
+    numels, N, r, seed = [1_048_573], 4, 2, 9404
+    plan = zs.zs_shard_plan(numels, N, r, 1)
+    T, S = plan.padded_numel, plan.shard_numel
+    cb, nb = zs.zs_quant_code_bytes(plan, bits), zs.zs_quant_num_scales(plan, B)
+    assert cb % 16 == 0 and (nb * 4) % 16 == 0  # every rank's slot starts 16-byte aligned
+    lo = r * S
+    hp = zs.AdamWHParams(lr=1e-3, weight_decay=0.1, step=2)
+    master0 = synth.cpu_f32(T, 0, synth.spec(seed, synth.STREAM_MASTER, 0, 0.02, sum(numels)))[lo:lo + S].copy()
+    rng = np.random.default_rng(seed)
+
+    def grads(k):
+        return [synth.cpu_bf16(T, 0, synth.spec(seed, synth.STREAM_CONTRIB + q, k, 1e-3, sum(numels)))[lo:lo + S]
+                .copy() for q in range(N)]
+
+    def state():
+        return dict(master=dev32(master0), m=torch.zeros(S, device="cuda"), v=torch.zeros(S, device="cuda"),
+                    g=torch.zeros(S, dtype=torch.int16, device="cuda"),
+                    p=torch.zeros(S, dtype=torch.int16, device="cuda"),
+                    codes=torch.zeros(N * cb, dtype=torch.uint8, device="cuda"),
+                    scales=torch.zeros(N * nb, dtype=torch.float32, device="cuda"),
+                    full=dev16(np.full(T, SENT, np.uint16)))
+
+    contribs = [torch.zeros(S, dtype=torch.int16, device="cuda") for _ in range(N)]
+
+    def step(d):
+        zs.zs_fused_shard_step_quant(plan, hp, contribs, d["master"], d["m"], d["v"], bits, B,
+                                     d["codes"][r * cb:(r + 1) * cb], d["scales"][r * nb:(r + 1) * nb],
+                                     grad=d["g"], param=d["p"])
+        zs.zs_dequant_gather(plan, bits, B, d["codes"], d["scales"], d["full"])
+
+    warm = state()
+    step(warm)
+    torch.cuda.synchronize()
+    A, Bst = state(), state()
+    graph = _capture(lambda: step(A))
+    o = dict(g=np.zeros(S, np.uint16), master=master0.copy(), m=np.zeros(S, np.float32),
+             v=np.zeros(S, np.float32), p=np.zeros(S, np.uint16))
+    for k in range(1, REPLAYS + 1):
+        gk = grads(k)
+        for q in range(N):
+            contribs[q].copy_(dev16(gk[q]))
+        codes_all = rng.integers(0, 256, N * cb, dtype=np.uint8)
+        scales_all = (rng.random(N * nb) * 1e-2).astype(np.float32)
+        for d in (A, Bst):  # the other ranks' slots; this rank's is rewritten by the step
+            d["codes"].copy_(torch.from_numpy(codes_all).cuda())
+            d["scales"].copy_(torch.from_numpy(scales_all).cuda())
+        torch.cuda.synchronize()
+        graph.replay()
+        step(Bst)
+        torch.cuda.synchronize()
+        for key in A:
+            _same(A[key], Bst[key], f"replay {k}: {key}")
+        oracle.shard_step(_ora_hp(hp), gk, o["g"], o["master"], o["m"], o["v"], o["p"], None, r)
+        q_own, s_own = oracle.quantize(o["p"], bits, B)
+        codes_all[r * cb:(r + 1) * cb] = q_own
+        scales_all[r * nb:(r + 1) * nb] = s_own
+        ref_full = oracle.dequant_gather(codes_all, scales_all, S, N, bits, B)
+        assert np.array_equal(A["codes"].cpu().numpy(), codes_all), f"replay {k}: codes"
+        assert np.array_equal(A["scales"].cpu().numpy().view(np.uint32), scales_all.view(np.uint32)), \
+            f"replay {k}: scales"
+        assert check_bf16(host16(A["full"]), ref_full, f"replay {k}: full") == 0
+    nd = check_f32(host32(A["master"]), o["master"], "master") + check_f32(host32(A["m"]), o["m"], "m")
+    nd += check_f32(host32(A["v"]), o["v"], "v") + check_bf16(host16(A["g"]), o["g"], "grad")
+    nd += check_bf16(host16(A["p"]), o["p"], "param")
+    assert nd == 0
