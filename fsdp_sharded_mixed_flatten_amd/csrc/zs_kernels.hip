@@ -669,14 +669,23 @@ __global__ __launch_bounds__(kBlock) void k_quant(const u32x4* __restrict__ p, Q
 // every block size), so the scales they use are the n_sc consecutive words
 // from s0 on: the block loads them once into LDS instead of every lane
 // loading its units' scales (32 lanes of a wave reading the same word, four
-// times over: 5% slower at the Llama-7B shape).
-template <int QB, int U>
+// times over: 5% slower at the Llama-7B shape). WIDE (every rank's code
+// payload a multiple of 16 bytes, so each block's codes start on a 16-byte
+// boundary): the block's codes arrive as 16-byte loads, one or two per lane,
+// and are handed to the lanes that decode them through LDS; otherwise each
+// lane loads its own units' 4 or 8 code bytes (1.7% slower at int4, 4.6% at
+// int8 in a probe at the Llama-7B shape).
+template <int QB, int U, bool WIDE>
 __global__ __launch_bounds__(kBlock) void k_dequant(const char* __restrict__ codes_all,
                                                     const float* __restrict__ scales_all, int64_t code_bytes,
                                                     int64_t n_scales, int block_shift, u32x4* __restrict__ full,
                                                     int64_t s8) {
     static_assert(8 * kBlock * U >= kQuantMaxBlock, "a block's span covers whole quantization blocks");
+    constexpr int kWords = QB / 4;                     // code words per 8-element unit
+    constexpr int kPieces = kBlock * U * kWords / 4;   // 16-byte pieces of a block's codes
+    static_assert(kPieces % kBlock == 0, "whole 16-byte pieces per lane");
     __shared__ float sl[kBlock * U];
+    __shared__ u32x4 cl[WIDE ? kPieces : 1];
     const int64_t r = blockIdx.y;
     const int64_t ub = (int64_t)blockIdx.x * kBlock * U;  // the block's first unit
     const char* cb = codes_all + r * code_bytes;
@@ -689,15 +698,29 @@ __global__ __launch_bounds__(kBlock) void k_dequant(const char* __restrict__ cod
     for (int k = 0; k < U; ++k) {
         const int j = threadIdx.x + k * kBlock;
         sv[k] = j < n_sc && s0 + j < n_scales ? ld_in(sb + s0 + j) : 0.0f;
-        const int64_t u = ub + j;
-        if (u >= s8) continue;
-        if constexpr (QB == 8) {
-            const u32x2 c = ld_in(reinterpret_cast<const u32x2*>(cb + u * 8));
-            lo[k] = c.x;
-            hi[k] = c.y;
-        } else {
-            lo[k] = ld_in(reinterpret_cast<const uint32_t*>(cb + u * 4));
-            hi[k] = 0u;
+    }
+    if constexpr (WIDE) {
+        // the shard's units end on a piece boundary: a piece is wholly inside or outside
+        const u32x4* src = reinterpret_cast<const u32x4*>(cb) + ub * kWords / 4;
+        const int64_t pieces_left = (s8 - ub) * kWords / 4;
+#pragma unroll
+        for (int h = 0; h < kPieces / kBlock; ++h) {
+            const int pc = threadIdx.x + h * kBlock;
+            cl[pc] = pc < pieces_left ? ld_in(src + pc) : u32x4{0u, 0u, 0u, 0u};
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int64_t u = ub + threadIdx.x + k * kBlock;
+            if (u >= s8) continue;
+            if constexpr (QB == 8) {
+                const u32x2 c = ld_in(reinterpret_cast<const u32x2*>(cb + u * 8));
+                lo[k] = c.x;
+                hi[k] = c.y;
+            } else {
+                lo[k] = ld_in(reinterpret_cast<const uint32_t*>(cb + u * 4));
+                hi[k] = 0u;
+            }
         }
     }
 #pragma unroll
@@ -708,6 +731,11 @@ __global__ __launch_bounds__(kBlock) void k_dequant(const char* __restrict__ cod
         const int j = threadIdx.x + k * kBlock;
         const int64_t u = ub + j;
         if (u >= s8) continue;
+        if constexpr (WIDE) {
+            const uint32_t* words = reinterpret_cast<const uint32_t*>(cl);
+            lo[k] = words[j * kWords];
+            hi[k] = kWords == 2 ? words[j * kWords + 1] : 0u;
+        }
         const float sc = sl[(j * 8) >> block_shift];
         float x[8];
 #pragma unroll
@@ -1257,12 +1285,22 @@ int launch_dequant(int bits, int block, const void* codes_all, const float* scal
     const dim3 grid(grid_for(s8, kDequantU), (unsigned)n_ranks);
     hipStream_t s = (hipStream_t)stream;
     const char* cb = static_cast<const char*>(codes_all);
-    if (bits == 8)
-        hipLaunchKernelGGL((k_dequant<8, kDequantU>), grid, dim3(kBlock), kDequantLds, s, cb, scales_all, code_bytes,
-                           n_scales, shift, reinterpret_cast<u32x4*>(full), s8);
+    u32x4* out = reinterpret_cast<u32x4*>(full);
+    // 16-byte code loads need every rank's payload to start 16-byte aligned
+    // (codes_all itself is 16-byte aligned)
+    const bool wide = code_bytes % 16 == 0;
+    if (bits == 8 && wide)
+        hipLaunchKernelGGL((k_dequant<8, kDequantU, true>), grid, dim3(kBlock), kDequantLds, s, cb, scales_all,
+                           code_bytes, n_scales, shift, out, s8);
+    else if (bits == 8)
+        hipLaunchKernelGGL((k_dequant<8, kDequantU, false>), grid, dim3(kBlock), kDequantLds, s, cb, scales_all,
+                           code_bytes, n_scales, shift, out, s8);
+    else if (wide)
+        hipLaunchKernelGGL((k_dequant<4, kDequantU, true>), grid, dim3(kBlock), kDequantLds, s, cb, scales_all,
+                           code_bytes, n_scales, shift, out, s8);
     else
-        hipLaunchKernelGGL((k_dequant<4, kDequantU>), grid, dim3(kBlock), kDequantLds, s, cb, scales_all, code_bytes,
-                           n_scales, shift, reinterpret_cast<u32x4*>(full), s8);
+        hipLaunchKernelGGL((k_dequant<4, kDequantU, false>), grid, dim3(kBlock), kDequantLds, s, cb, scales_all,
+                           code_bytes, n_scales, shift, out, s8);
     return (int)hipGetLastError();
 }
 

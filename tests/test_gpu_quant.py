@@ -108,13 +108,16 @@ def test_dequant_gather(zs, bits, world, block):
     assert np.all(got[world * S:] == 0x5A5A)
 
 
-@pytest.mark.parametrize("bits,block,S", [(4, 256, 15_560), (4, 128, 24_896), (4, 8, 1_000), (8, 256, 15_560)])
+@pytest.mark.parametrize("bits,block,S", [(4, 256, 15_560), (4, 128, 24_896), (4, 8, 1_000), (4, 16, 4_160),
+                                          (8, 256, 15_560), (8, 64, 24_896), (8, 32, 1_000)])
 def test_dequant_gather_arbitrary_payload(zs, bits, block, S):
     """Payloads no quantizer writes: every code value (the 4-bit -8 and the
     8-bit -128 included) under scales that are random, zero, negative, tiny
     (products round to bf16 subnormals), huge (products overflow to
-    infinity), infinite and NaN of either sign; shards whose last 16-unit
-    group is cut short (the 4-bit decode's lookup groups)."""
+    infinity), infinite and NaN of either sign. Shard lengths with and without
+    16-byte-aligned per-rank code payloads (S a multiple of 32 at int4, of 16
+    at int8), the two ways the kernel loads codes, each with a last block of
+    the launch cut short."""
     import torch
     world = 3
     plan = zs.zs_shard_plan([world * S], world, 0, 1)
@@ -122,6 +125,7 @@ def test_dequant_gather_arbitrary_payload(zs, bits, block, S):
     rng = np.random.default_rng(block + S)
     nq = zs.zs_quant_code_bytes(plan, bits)
     ns = zs.zs_quant_num_scales(plan, block)
+    assert (nq % 16 == 0) == (S % (128 // bits) == 0)
     codes_all = rng.integers(0, 256, world * nq, dtype=np.uint8)
     sc = (rng.standard_normal(world * ns) * 1e-3).astype(np.float32)
     special = np.array([0.0, -0.0, -1e-3, 1e-40, 2e-38, 3.0e38, -3.0e38, np.inf, -np.inf], np.float32)
