@@ -136,12 +136,18 @@ constexpr int kFusedU = ZS_FUSED_U;
 constexpr unsigned kFusedLds = ZS_FUSED_LDS_KB * 1024u;
 constexpr unsigned kFusedNarrowLds = ZS_FUSED_NARROW_LDS_KB * 1024u;
 constexpr unsigned kFusedQuantLds = ZS_FUSED_QUANT_LDS_KB * 1024u;
-// Accumulation micro-steps at 4 or fewer ranks (reads 2N+4 bytes, writes 4
-// per element) run fastest with more resident waves than the fused kernel.
+// Accumulation micro-steps (read 2N+4 bytes, write 4 per element): 16 KiB
+// (8 to 40 KiB measured at the Llama-7B and -70B shapes; 32 KiB and more lose
+// 11% at N=64), and at 4 or fewer ranks more resident waves than the fused
+// kernel (8 KiB).
+#ifndef ZS_ACCUM_LDS_KB
+#define ZS_ACCUM_LDS_KB 16
+#endif
 #ifndef ZS_ACCUM_NARROW_LDS_KB
 #define ZS_ACCUM_NARROW_LDS_KB 8
 #endif
 constexpr unsigned kAccumNarrowLds = ZS_ACCUM_NARROW_LDS_KB * 1024u;
+constexpr unsigned kAccumLds = ZS_ACCUM_LDS_KB * 1024u;
 constexpr unsigned kReduceLds = ZS_REDUCE_LDS_KB * 1024u;
 constexpr unsigned kReduceWideLds = ZS_REDUCE_WIDE_LDS_KB * 1024u;
 constexpr int kWideN = ZS_WIDE_N;
@@ -1230,7 +1236,7 @@ int launch_accum_t(const void* const* contribs, int n, float* acc, int first, in
     Ptrs<CAP> cp{};
     for (int q = 0; q < n; ++q) cp.p[q] = contribs[q];
     const int64_t n4 = len / 4;
-    const unsigned lds = n <= 4 ? kAccumNarrowLds : kFusedLds;
+    const unsigned lds = n <= 4 ? kAccumNarrowLds : kAccumLds;
     if (first)
         hipLaunchKernelGGL((k_accum<N, CAP, true>), dim3(grid_for(n4, kFusedU)), dim3(kBlock), lds, s, cp, n,
                            (float)n, reinterpret_cast<f32x4*>(acc), n4);
