@@ -16,8 +16,7 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# ZS_LIB selects another build of the same library (launch-shape variants).
-LIB_PATH = os.environ.get("ZS_LIB") or os.path.join(_HERE, "libzs.so")
+LIB_PATH = os.path.join(_HERE, "libzs.so")
 
 ZS_OK, ZS_EINVAL, ZS_EALIGN, ZS_ERANGE, ZS_EHIP, ZS_ENOMEM = 0, -1, -2, -3, -4, -5
 ZS_LAYOUT_FLAT, ZS_LAYOUT_PER_TENSOR = 0, 1
@@ -466,10 +465,19 @@ def zs_multi_workspace_bytes(plan, n_contribs):
     return n
 
 
+# Bound workspaces, keyed by device address: the workspace tensor and every
+# tensor whose address its table holds. Keeping them referenced until
+# zs_multi_unbind means no bound buffer can be freed (and its memory reused by
+# the caching allocator) while a step may still write through the table.
+_bindings = {}
+
+
 def zs_multi_bind(plan, pieces, contribs, workspace, stream=None):
     """pieces[i]: dict with keys grad, master, m, v, param, full (tensors or
     None) for tensor i; contribs: None or contribs[q][i] = rank q's piece of
-    tensor i. workspace: a CUDA uint8 tensor of zs_multi_workspace_bytes."""
+    tensor i. workspace: a CUDA uint8 tensor of zs_multi_workspace_bytes.
+    The binding keeps references to the workspace and every bound tensor
+    until zs_multi_unbind(workspace)."""
     n = plan.num_tensors
     if len(pieces) != n:
         raise ValueError(f"{len(pieces)} piece records for a plan of {n} tensors")
@@ -497,10 +505,15 @@ def zs_multi_bind(plan, pieces, contribs, workspace, stream=None):
     _check(_lib.zs_multi_bind(plan.handle, recs, _ptr_array(flat) if nq else None, nq,
                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                               _stream(stream)))
+    refs = [t for pc in pieces for t in pc.values() if t is not None and not isinstance(t, int)]
+    if nq:
+        refs += [t for row in contribs for t in row if not isinstance(t, int)]
+    _bindings[workspace.data_ptr()] = (workspace, refs)
 
 
 def zs_multi_unbind(workspace, stream=None):
     _check(_lib.zs_multi_unbind(workspace.data_ptr(), _stream(stream)))
+    _bindings.pop(workspace.data_ptr(), None)
 
 
 def zs_reduce_shard_multi(plan, workspace, stream=None):

@@ -34,14 +34,12 @@ def _run(cmd, verbose):
         print(err)
 
 
-def build(verbose=False, out=None, defines=()):
-    """Builds libzs.so (or ``out``); ``defines`` are extra -D flags for the
-    kernels' launch-shape constants."""
+def build(verbose=False, out=None):
+    """Builds libzs.so (or ``out``)."""
     os.makedirs(BUILD, exist_ok=True)
     objs = []
     api_o = os.path.join(BUILD, "zs_api.o")
-    _run(["g++", *COMMON, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, "zs_api.cpp"), "-o", api_o],
-         verbose)
+    _run(["g++", *COMMON, "-c", os.path.join(CSRC, "zs_api.cpp"), "-o", api_o], verbose)
     objs.append(api_o)
     host_o = os.path.join(BUILD, "zs_host_adamw.o")
     # host AdamW: same one-rounding-per-operation rule; -fno-math-errno lets
@@ -51,8 +49,7 @@ def build(verbose=False, out=None, defines=()):
     objs.append(host_o)
     for name in ("zs_kernels", "zs_offload"):
         o = os.path.join(BUILD, f"{name}.o")
-        _run([HIPCC, *COMMON, *HIP_ONLY, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, f"{name}.hip"),
-              "-o", o], verbose)
+        _run([HIPCC, *COMMON, *HIP_ONLY, "-c", os.path.join(CSRC, f"{name}.hip"), "-o", o], verbose)
         objs.append(o)
     target = out or LIB
     tmp = target + ".tmp"

@@ -52,16 +52,12 @@ struct zs_plan {
 
 namespace zs {
 
-// Launch shape shared by the host (chunk table) and the kernels. Overridable
-// at build time for sweeps.
-#ifndef ZS_BLOCK
-#define ZS_BLOCK 64
-#endif
-#ifndef ZS_MULTI_U
-#define ZS_MULTI_U 1
-#endif
-constexpr int kBlockThreads = ZS_BLOCK;  // threads per block of every kernel
-constexpr int kMultiU = ZS_MULTI_U;      // 4-element units per lane in a multi-tensor chunk
+// Launch shape shared by the host (chunk table) and the kernels: one 64-lane
+// wave per block (128- to 512-thread blocks measured slower), and one
+// 4-element unit per lane in a multi-tensor chunk (2-8 measured slower for
+// the fused step).
+constexpr int kBlockThreads = 64;  // threads per block of every kernel
+constexpr int kMultiU = 1;         // 4-element units per lane in a multi-tensor chunk
 // Multi-tensor chunk length (elements): one block per chunk, one tile each.
 constexpr int32_t kChunkElems = kBlockThreads * 4 * kMultiU;
 

@@ -34,93 +34,6 @@
 
 #include "zs_internal.h"
 
-// ------------------------------------------------------------------ tuning switches
-// Build-time constants (overridable with -D for sweeps). kBlockThreads and
-// kMultiU live in zs_internal.h because the host's chunk table depends on them.
-
-// Units of work per lane: 8 elements (reduce) or 4 elements (the others).
-#ifndef ZS_REDUCE_U
-#define ZS_REDUCE_U 1
-#endif
-#ifndef ZS_ADAMW_U
-#define ZS_ADAMW_U 1
-#endif
-#ifndef ZS_FUSED_U
-#define ZS_FUSED_U 1
-#endif
-// Ranks whose loads a lane issues together.
-#ifndef ZS_GROUP
-#define ZS_GROUP 8
-#endif
-// Occupancy throttle: KiB of untouched dynamic LDS per block (160 KiB per CU).
-#ifndef ZS_FUSED_LDS_KB
-#define ZS_FUSED_LDS_KB 16
-#endif
-// ... for the fused kernel at 4 or fewer ranks, whose lighter reads leave
-// room for more resident waves: eleven per CU (14 KiB) measured 1.4% faster
-// than ten (16 KiB) or thirteen (12 KiB) at the Qwen2.5-3B shape.
-#ifndef ZS_FUSED_NARROW_LDS_KB
-#define ZS_FUSED_NARROW_LDS_KB 14
-#endif
-// ... for the fused kernel writing quantized codes (any number of ranks):
-// 12 KiB measured 3% faster than 14 or 16 KiB at the Qwen2.5-3B shape and
-// than 16 KiB at the Llama-7B shape.
-#ifndef ZS_FUSED_QUANT_LDS_KB
-#define ZS_FUSED_QUANT_LDS_KB 12
-#endif
-#ifndef ZS_REDUCE_LDS_KB
-#define ZS_REDUCE_LDS_KB 8
-#endif
-// ... and from ZS_WIDE_N ranks on: 64 concurrent read streams per lane group
-// run fastest with only a few resident waves per CU.
-#ifndef ZS_REDUCE_WIDE_LDS_KB
-#define ZS_REDUCE_WIDE_LDS_KB 32
-#endif
-#ifndef ZS_WIDE_N
-#define ZS_WIDE_N 32
-#endif
-#ifndef ZS_ADAMW_LDS_KB
-#define ZS_ADAMW_LDS_KB 8
-#endif
-#ifndef ZS_GATHER_LDS_KB
-#define ZS_GATHER_LDS_KB 8
-#endif
-#ifndef ZS_MULTI_LDS_KB
-#define ZS_MULTI_LDS_KB 12
-#endif
-// ... for the multi-tensor fused step: 14 KiB measured 1.6% faster than 12
-// and 3% faster than 16 at the Llama-7B wrap-stress shape, where the unfused
-// multi-tensor kernels are 3% faster at 12 KiB
-#ifndef ZS_MULTI_FUSED_LDS_KB
-#define ZS_MULTI_FUSED_LDS_KB 14
-#endif
-// Dequantizing gather: 8-element units per lane, and its occupancy throttle.
-#ifndef ZS_DEQUANT_U
-#define ZS_DEQUANT_U 4
-#endif
-#ifndef ZS_DEQUANT_LDS_KB
-#define ZS_DEQUANT_LDS_KB 0
-#endif
-// World size from which the fused entry point runs reduce, then AdamW +
-// gather, when the caller provides the grad buffer (0: never).
-#ifndef ZS_SPLIT_MIN_N
-#define ZS_SPLIT_MIN_N 64
-#endif
-// Cache policy per access class (1 = nontemporal): read-once inputs, the
-// read-modify-write optimizer state, write-once outputs.
-#ifndef ZS_NT_IN
-#define ZS_NT_IN 1
-#endif
-#ifndef ZS_NT_STATE_LD
-#define ZS_NT_STATE_LD 1
-#endif
-#ifndef ZS_NT_STATE_ST
-#define ZS_NT_STATE_ST 1
-#endif
-#ifndef ZS_NT_OUT
-#define ZS_NT_OUT 1
-#endif
-
 namespace zs {
 namespace {
 
@@ -128,36 +41,55 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// ------------------------------------------------------------------ launch shape
+// Every value below was measured against its neighbours on MI355X at the
+// model shapes (Qwen2.5-3B N=4, Llama-7B N=8, Llama-70B N=64).
+
 constexpr int kBlock = kBlockThreads;
-constexpr int kGroup = ZS_GROUP;
-constexpr int kReduceU = ZS_REDUCE_U;
-constexpr int kAdamwU = ZS_ADAMW_U;
-constexpr int kFusedU = ZS_FUSED_U;
-constexpr unsigned kFusedLds = ZS_FUSED_LDS_KB * 1024u;
-constexpr unsigned kFusedNarrowLds = ZS_FUSED_NARROW_LDS_KB * 1024u;
-constexpr unsigned kFusedQuantLds = ZS_FUSED_QUANT_LDS_KB * 1024u;
-// Accumulation micro-steps (read 2N+4 bytes, write 4 per element): 16 KiB
-// (8 to 40 KiB measured at the Llama-7B and -70B shapes; 32 KiB and more lose
-// 11% at N=64), and at 4 or fewer ranks more resident waves than the fused
-// kernel (8 KiB).
-#ifndef ZS_ACCUM_LDS_KB
-#define ZS_ACCUM_LDS_KB 16
-#endif
-#ifndef ZS_ACCUM_NARROW_LDS_KB
-#define ZS_ACCUM_NARROW_LDS_KB 8
-#endif
-constexpr unsigned kAccumNarrowLds = ZS_ACCUM_NARROW_LDS_KB * 1024u;
-constexpr unsigned kAccumLds = ZS_ACCUM_LDS_KB * 1024u;
-constexpr unsigned kReduceLds = ZS_REDUCE_LDS_KB * 1024u;
-constexpr unsigned kReduceWideLds = ZS_REDUCE_WIDE_LDS_KB * 1024u;
-constexpr int kWideN = ZS_WIDE_N;
-constexpr unsigned kAdamwLds = ZS_ADAMW_LDS_KB * 1024u;
-constexpr unsigned kGatherLds = ZS_GATHER_LDS_KB * 1024u;
-constexpr unsigned kMultiLds = ZS_MULTI_LDS_KB * 1024u;
-constexpr unsigned kMultiFusedLds = ZS_MULTI_FUSED_LDS_KB * 1024u;
-constexpr int kSplitMinN = ZS_SPLIT_MIN_N;
-constexpr int kDequantU = ZS_DEQUANT_U;
-constexpr unsigned kDequantLds = ZS_DEQUANT_LDS_KB * 1024u;
+// Ranks whose loads a lane issues together (16 or 32 measured within noise).
+constexpr int kGroup = 8;
+// Units of work per lane: 8 elements (reduce) or 4 elements (the others);
+// two or four units per lane measured slower in every kernel.
+constexpr int kReduceU = 1;
+constexpr int kAdamwU = 1;
+constexpr int kFusedU = 1;
+// Occupancy throttle: bytes of untouched dynamic LDS per block (160 KiB per
+// CU), which caps the resident 64-thread blocks per CU.
+//   fused step, N > 4: 16 KiB (ten waves per CU);
+constexpr unsigned kFusedLds = 16u << 10;
+//   fused step at 4 or fewer ranks, whose lighter reads leave room for more
+//   resident waves: eleven per CU (14 KiB) measured 1.4% faster than ten or
+//   thirteen at the Qwen2.5-3B shape;
+constexpr unsigned kFusedNarrowLds = 14u << 10;
+//   fused step writing quantized codes (more registers): 12 KiB, 3% faster
+//   than 14 or 16 KiB at the Qwen2.5-3B and Llama-7B shapes;
+constexpr unsigned kFusedQuantLds = 12u << 10;
+//   accumulation micro-steps (read 2N+4 bytes, write 4 per element): 16 KiB
+//   (8 to 40 KiB measured at the Llama-7B and -70B shapes; 32 KiB and more
+//   lose 11% at N=64), and 8 KiB at 4 or fewer ranks (10% faster than 16);
+constexpr unsigned kAccumLds = 16u << 10;
+constexpr unsigned kAccumNarrowLds = 8u << 10;
+//   reduce: 8 KiB (4-16 KiB within noise); from kWideN ranks on 32 KiB, about
+//   five waves per CU (3-8% faster at N=64 than 8 KiB; 48 KiB and up lose);
+constexpr unsigned kReduceLds = 8u << 10;
+constexpr unsigned kReduceWideLds = 32u << 10;
+constexpr int kWideN = 32;
+//   AdamW, gather and the bf16 codes of a shard: 8 KiB (6-14 KiB within noise);
+constexpr unsigned kAdamwLds = 8u << 10;
+constexpr unsigned kGatherLds = 8u << 10;
+//   multi-tensor kernels: 12 KiB unfused (3% faster than 14, 5% than 16) and
+//   14 KiB for the fused step (1.6% faster than 12, 3% than 16 at the
+//   Llama-7B wrap-stress shape);
+constexpr unsigned kMultiLds = 12u << 10;
+constexpr unsigned kMultiFusedLds = 14u << 10;
+//   dequantizing gather, a nearly pure write stream: none (a throttle cost it
+//   up to 2x). Its lanes decode four 8-element units each.
+constexpr unsigned kDequantLds = 0;
+constexpr int kDequantU = 4;
+// World size from which the fused entry point runs the reduce into the grad
+// shard, then AdamW + gather, when the caller provides the grad buffer: at
+// N=64 every one-pass layout measured 7-25% slower than the two passes.
+constexpr int kSplitMinN = 64;
 
 // ------------------------------------------------------------------ bf16
 
@@ -250,22 +182,17 @@ __device__ __forceinline__ AdamCoef pick_coef(const AdamCoef& c, const AdamCoef*
     return d;
 }
 
+// Cache policy per access class: read-once inputs, the read-modify-write
+// optimizer state and write-once outputs are all nontemporal (each class was
+// swept; every cached variant was slower).
 template <typename T>
-__device__ __forceinline__ T ld_in(const T* p) {
-    if constexpr (ZS_NT_IN) return ld_nt(p); else return *(gptr<const T>)p;
-}
+__device__ __forceinline__ T ld_in(const T* p) { return ld_nt(p); }
 template <typename T>
-__device__ __forceinline__ T ld_state(const T* p) {
-    if constexpr (ZS_NT_STATE_LD) return ld_nt(p); else return *(gptr<const T>)p;
-}
+__device__ __forceinline__ T ld_state(const T* p) { return ld_nt(p); }
 template <typename T>
-__device__ __forceinline__ void st_state(T* p, T x) {
-    if constexpr (ZS_NT_STATE_ST) st_nt(p, x); else *(gptr<T>)p = x;
-}
+__device__ __forceinline__ void st_state(T* p, T x) { st_nt(p, x); }
 template <typename T>
-__device__ __forceinline__ void st_out(T* p, T x) {
-    if constexpr (ZS_NT_OUT) st_nt(p, x); else *(gptr<T>)p = x;
-}
+__device__ __forceinline__ void st_out(T* p, T x) { st_nt(p, x); }
 
 template <int CAP>
 struct Ptrs {
@@ -879,10 +806,7 @@ __global__ __launch_bounds__(kBlock) void k_multi_gather(const MultiHeader* __re
 // Multi-tensor reduce in the same shape: 8 elements (16-byte loads) per lane,
 // two chunks per row of the wave, kReduceRows rows per block; the rows' table
 // lookups are batched, then each row sums its N contributions in rank order.
-#ifndef ZS_MULTI_REDUCE_ROWS
-#define ZS_MULTI_REDUCE_ROWS 2
-#endif
-constexpr int kReduceRows = ZS_MULTI_REDUCE_ROWS;
+constexpr int kReduceRows = 2;
 constexpr int kReduceChunksPerBlock = kGatherChunksPerRow * kReduceRows;
 
 template <int N>

@@ -106,16 +106,37 @@ def spec(seed, stream, step, sigma, valid_hi=2**62, tail_sigma=0.0, tail_prob=0.
 # ---------------------------------------------------------------- host build
 
 
-def cpu_f32(n, base, sp):
+def _fill_threaded(fn, out, base, sp, threads):
+    """fn(ptr, n, base, spec) over contiguous slices of out on `threads` host
+    threads (the foreign call releases the GIL); element j is always the
+    value of global index base + j."""
+    n = out.size
+    if threads <= 1 or n < (1 << 20):
+        fn(out.ctypes.data, n, base, ctypes.byref(sp))
+        return out
+    from concurrent.futures import ThreadPoolExecutor
+    step = (n + threads - 1) // threads
+    item = out.itemsize
+
+    def part(k):
+        lo = k * step
+        hi = min(n, lo + step)
+        if hi > lo:
+            fn(out.ctypes.data + lo * item, hi - lo, base + lo, ctypes.byref(sp))
+
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(part, range(threads)))
+    return out
+
+
+def cpu_f32(n, base, sp, threads=1):
     out = np.empty(n, dtype=np.float32)
-    cpu_lib().synth_cpu_fill_f32(out.ctypes.data, n, base, ctypes.byref(sp))
-    return out
+    return _fill_threaded(cpu_lib().synth_cpu_fill_f32, out, base, sp, threads)
 
 
-def cpu_bf16(n, base, sp):
+def cpu_bf16(n, base, sp, threads=1):
     out = np.empty(n, dtype=np.uint16)
-    cpu_lib().synth_cpu_fill_bf16(out.ctypes.data, n, base, ctypes.byref(sp))
-    return out
+    return _fill_threaded(cpu_lib().synth_cpu_fill_bf16, out, base, sp, threads)
 
 
 def cpu_at_f32(idx, sp):

@@ -53,3 +53,29 @@ def syn():
     import synth
     synth.cpu_lib()
     return synth
+
+
+@pytest.fixture(autouse=True)
+def _release_multi_bindings():
+    """The binding keeps every tensor of a multi-tensor binding alive until
+    its workspace is unbound; unbind whatever a test left bound so its
+    buffers are freed before the next test allocates."""
+    yield
+    zs = sys.modules.get("fsdp_sharded_mixed_flatten_amd")
+    bound = getattr(zs, "_bindings", None) if zs is not None else None
+    if not bound:
+        return
+    for ws, _refs in list(bound.values()):
+        try:
+            zs.zs_multi_unbind(ws)
+        except Exception:  # pragma: no cover - a failed test may leave the device unusable
+            pass
+    bound.clear()
+    # hand the freed blocks back to the device, so the next test's free
+    # memory check sees them
+    import gc
+
+    import torch
+    gc.collect()
+    if torch.cuda.is_initialized():
+        torch.cuda.empty_cache()

@@ -401,10 +401,13 @@ def test_device_scalar_calls_validate_without_device(zs):
 def test_binding_fails_loudly_without_the_library(tmp_path):
     """No fallback path: without the built library the binding raises on
     import, and so does everything that runs the step through it."""
+    import shutil
     import subprocess
     import sys
-    env = dict(os.environ, ZS_LIB=str(tmp_path / "missing" / "libzs.so"))
-    res = subprocess.run([sys.executable, "-c", "import fsdp_sharded_mixed_flatten_amd"], cwd=ROOT, env=env,
+    pkg = tmp_path / "fsdp_sharded_mixed_flatten_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "fsdp_sharded_mixed_flatten_amd", "__init__.py"), pkg / "__init__.py")
+    res = subprocess.run([sys.executable, "-c", "import fsdp_sharded_mixed_flatten_amd"], cwd=str(tmp_path),
                          capture_output=True, text=True, timeout=120)
     assert res.returncode != 0
     assert "ImportError" in res.stderr and "is not built" in res.stderr, res.stderr

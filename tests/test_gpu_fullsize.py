@@ -2,11 +2,15 @@
 
 Inputs are generated on the device by the GPU build of the seeded generator;
 the oracle recomputes each sampled element from the host build's values of the
-same global indices (no input of the oracle comes from the device). The path
-runs in the launch configuration the benchmark times. Samples: the first and
-last 2,048 owned elements, both sides of every reduce-bucket boundary, and
-random positions; fused and unfused results are also compared on every
-element.
+same global indices (no input of the oracle comes from the device). Each
+workload runs through the entry points the benchmark times, in the same
+launch configuration: the one-pass fused kernel at N <= 8, and at N = 64 the
+fused entry point with the grad shard given, which runs the reduce and then
+AdamW writing the gathered slice (the one-pass form is checked there too).
+Samples: the first and last 2,048 owned elements, both sides of every
+reduce-bucket boundary, and random positions; fused and unfused results are
+also compared on every element. Ranks other than 0 are included, so the owned
+slice of the gathered buffer starts at a nonzero offset r*S.
 """
 import numpy as np
 import pytest
@@ -56,19 +60,20 @@ def _samples(S, bucket, n_random, seed):
 class FlatBig:
     """One rank's FLAT shard at full size; device inputs from the GPU generator."""
 
-    def __init__(self, zs, wl, n_random=200_000):
+    def __init__(self, zs, wl, n_random=200_000, rank=None):
         import torch
         self.zs, self.wl = zs, wl
-        self.plan = zs.zs_shard_plan(wl.numels, wl.world, wl.rank, wl.align, zs.ZS_LAYOUT_FLAT)
+        self.rank = wl.rank if rank is None else rank
+        self.plan = zs.zs_shard_plan(wl.numels, wl.world, self.rank, wl.align, zs.ZS_LAYOUT_FLAT)
         self.S, self.T = self.plan.shard_numel, self.plan.padded_numel
-        self.base = wl.rank * self.S
+        self.base = self.rank * self.S
         self.valid_hi = sum(wl.numels)  # only tail padding in these shapes (checked below)
-        assert oracle.plan_flat(wl.numels, wl.world, wl.rank, wl.align).T == self.T
+        assert oracle.plan_flat(wl.numels, wl.world, self.rank, wl.align).T == self.T
         assert all(n % wl.align == 0 for n in wl.numels[:-1])
         self.idx = _samples(self.S, wl.bucket_elems, n_random, 17)
         self.didx = torch.from_numpy(self.idx).cuda()
         S = self.S
-        print(f"[{wl.name}] N={wl.world} S={S:,} samples={self.idx.size:,}", flush=True)
+        print(f"[{wl.name}] N={wl.world} rank={self.rank} S={S:,} samples={self.idx.size:,}", flush=True)
         self.contribs = [torch.empty(S, dtype=torch.int16, device="cuda") for _ in range(wl.world)]
         self.master = torch.empty(S, dtype=torch.float32, device="cuda")
         synth.gpu_f32(self.master, self.base, wl.master_spec(self.valid_hi))
@@ -262,32 +267,76 @@ def test_llama7b_wrap_stress_multi_tensor(zs, persist):
     _release()
 
 
-def test_llama70b_shape_fused(zs):
+@pytest.mark.parametrize("form,rank", [("two_pass", 63), ("one_pass", 0)])
+def test_llama70b_shape_fused(zs, form, rank):
+    """The 70B shard at N=64. two_pass: the fused entry point with the grad
+    shard given, as the benchmark runs it (the reduce into the grad shard,
+    then AdamW writing the gathered slice), at rank 63, whose owned slice
+    starts at 63*S in the 70.6 G-element gathered buffer. one_pass: no grad
+    shard, the single fused kernel, at rank 0."""
     import torch
     wl = synth.workloads()["llama70b"]
-    plan_o = oracle.plan_flat(wl.numels, wl.world, wl.rank, wl.align)
-    S = plan_o.S
-    need = (wl.world * 2 + 12) * S / 2**30 + 4
+    plan_o = oracle.plan_flat(wl.numels, wl.world, rank, wl.align)
+    S, T = plan_o.S, plan_o.T
+    need = (wl.world * 2 + 14) * S / 2**30 + 4
     free = _free_gib()
+    # the owned slice of a nonzero rank lies at r*S, so it needs the whole T
+    # gathered buffer; rank 0 can use [0, S) plus a guard band
+    full_elems = T if (rank > 0 or free - need > T * 2 / 2**30 + 4) else S + 1_000_000
+    need += full_elems * 2 / 2**30
     if free < need:
         pytest.skip(f"needs {need:.0f} GiB of free device memory, {free:.0f} GiB free")
-    # The full gathered buffer (T elements, 131 GiB) is allocated when it fits;
-    # otherwise rank 0's owned slice [0, S) plus a guard band stands in for it.
-    full_elems = plan_o.T if free - need > plan_o.T * 2 / 2**30 + 4 else S + 1_000_000
-    run = FlatBig(zs, wl, n_random=100_000)
+    run = FlatBig(zs, wl, n_random=100_000, rank=rank)
+    lo = rank * S
     hp = _hp(zs, wl)
     full = torch.full((full_elems,), SENT, dtype=torch.int16, device="cuda")
-    print(f"[llama70b] gathered buffer elements {full_elems:,}", flush=True)
+    grad = torch.full((S,), SENT, dtype=torch.int16, device="cuda") if form == "two_pass" else None
+    print(f"[llama70b] {form} rank {rank}: gathered buffer elements {full_elems:,}", flush=True)
     run.gen_contribs(1)
-    zs.zs_fused_shard_step(run.plan, hp, run.contribs, run.master, run.m, run.v, full=full)
+    zs.zs_fused_shard_step(run.plan, hp, run.contribs, run.master, run.m, run.v, grad=grad, full=full)
     run.oracle_step(1, hp)
     torch.cuda.synchronize()
-    nd = run.check_state("llama70b")
-    nd += check_bf16(run.pick16(full), run.o_p, "gathered param")
+    nd = run.check_state(f"llama70b {form}")
+    nd += check_bf16(run.pick16(full[lo:lo + S]), run.o_p, "gathered param")
+    if grad is not None:
+        nd += check_bf16(run.pick16(grad), run.o_g, "grad")
     assert nd == 0, f"{nd} sampled elements not bit-identical"
-    assert bool((full[S:S + 1_000_000] == SENT).all())
+    # guard bands on both sides of the owned slice keep their sentinels
+    if lo > 0:
+        assert bool((full[lo - 1_000_000:lo] == SENT).all()), "the gather wrote before the owned slice"
+    if lo + S < full_elems:
+        assert bool((full[lo + S:lo + S + 1_000_000] == SENT).all()), "the gather wrote past the owned slice"
     # heavy tails are present in the sampled contributions' average
     assert np.abs(oracle.bf16_to_f32(run.o_g)).max() > 3e-3
+    del run, full, grad
+    _release()
+
+
+def test_llama7b_shape_fused_at_rank_5(zs):
+    """The 7B shard (N=8) of rank 5 through the one-pass fused kernel as the
+    benchmark runs it (gathered slice written, no grad or param shard), two
+    steps: the owned slice starts at 5*S of the gathered buffer, the ranks'
+    slices around it keep their sentinels."""
+    import torch
+    wl = synth.workloads()["llama7b"]
+    if _free_gib() < 60:
+        pytest.skip("needs ~50 GiB of free device memory")
+    rank = 5
+    run = FlatBig(zs, wl, rank=rank)
+    S, T = run.S, run.T
+    lo = rank * S
+    hp = _hp(zs, wl)
+    full = torch.full((T,), SENT, dtype=torch.int16, device="cuda")
+    for t in (1, 2):
+        run.gen_contribs(t)
+        zs.zs_fused_shard_step(run.plan, hp.at(t), run.contribs, run.master, run.m, run.v, full=full)
+        run.oracle_step(t, hp)
+    torch.cuda.synchronize()
+    nd = run.check_state("llama7b rank 5")
+    nd += check_bf16(run.pick16(full[lo:lo + S]), run.o_p, "gathered param")
+    assert nd == 0, f"{nd} sampled elements not bit-identical"
+    assert bool((full[:lo] == SENT).all()), "the gather wrote into lower ranks' slices"
+    assert bool((full[lo + S:] == SENT).all()), "the gather wrote into higher ranks' slices"
     del run, full
     _release()
 
