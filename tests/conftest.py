@@ -56,26 +56,24 @@ def syn():
 
 
 @pytest.fixture(autouse=True)
-def _release_multi_bindings():
-    """The binding keeps every tensor of a multi-tensor binding alive until
-    its workspace is unbound; unbind whatever a test left bound so its
-    buffers are freed before the next test allocates."""
+def _release_device_memory():
+    """After each test: unbind whatever multi-tensor workspace it left bound
+    (the binding keeps every bound tensor alive until then), and hand the
+    blocks torch's caching allocator holds back to the device, so the next
+    test's free-memory check sees them (the full-size tests need nearly the
+    whole of it)."""
     yield
     zs = sys.modules.get("fsdp_sharded_mixed_flatten_amd")
     bound = getattr(zs, "_bindings", None) if zs is not None else None
-    if not bound:
-        return
-    for ws, _refs in list(bound.values()):
-        try:
-            zs.zs_multi_unbind(ws)
-        except Exception:  # pragma: no cover - a failed test may leave the device unusable
-            pass
-    bound.clear()
-    # hand the freed blocks back to the device, so the next test's free
-    # memory check sees them
-    import gc
-
-    import torch
-    gc.collect()
-    if torch.cuda.is_initialized():
+    if bound:
+        for ws, _refs in list(bound.values()):
+            try:
+                zs.zs_multi_unbind(ws)
+            except Exception:  # pragma: no cover - a failed test may leave the device unusable
+                pass
+        bound.clear()
+    torch = sys.modules.get("torch")
+    if torch is not None and torch.cuda.is_initialized():
+        import gc
+        gc.collect()
         torch.cuda.empty_cache()

@@ -276,6 +276,7 @@ def test_llama70b_shape_fused(zs, form, rank):
     shard, the single fused kernel, at rank 0."""
     import torch
     wl = synth.workloads()["llama70b"]
+    _release()
     plan_o = oracle.plan_flat(wl.numels, wl.world, rank, wl.align)
     S, T = plan_o.S, plan_o.T
     need = (wl.world * 2 + 14) * S / 2**30 + 4
