@@ -22,6 +22,7 @@ ZS_OK, ZS_EINVAL, ZS_EALIGN, ZS_ERANGE, ZS_EHIP, ZS_ENOMEM = 0, -1, -2, -3, -4, 
 ZS_LAYOUT_FLAT, ZS_LAYOUT_PER_TENSOR = 0, 1
 ZS_MAX_CONTRIBS = 256
 ZS_MAX_GROUPS = 8
+GRAD_STATS_NOALLOC_MAX_ELEMS = 1431568384
 
 _STATUS_NAMES = {0: "ZS_OK", -1: "ZS_EINVAL", -2: "ZS_EALIGN", -3: "ZS_ERANGE", -4: "ZS_EHIP",
                  -5: "ZS_ENOMEM"}
@@ -123,6 +124,7 @@ def _load():
         "zs_accumulate_shard": (st, [vp, ctypes.POINTER(vp), i32, vp, i64, i64, i32, vp]),
         "zs_grad_stats_workspace_bytes": (i64, [vp]),
         "zs_grad_stats": (st, [vp, vp, ctypes.c_float, vp, vp, vp, i64, vp]),
+        "zs_grad_stats_noalloc": (st, [vp, vp, ctypes.c_float, vp, vp, vp]),
         "zs_clip_scale": (st, [vp, vp, i32, ctypes.c_double, vp, vp, vp]),
         "zs_adamw_shard_step_accum": (st, [vp, ctypes.POINTER(AdamWHParams), vp, ctypes.c_float, vp, vp, vp, vp,
                                            vp, vp, vp, vp]),
@@ -154,7 +156,8 @@ EXPORTED = ("zs_shard_plan", "zs_shard_plan_ex", "zs_plan_tensor_group", "zs_pla
             "zs_fused_shard_step_multi_groups", "zs_quant_code_bytes", "zs_quant_num_scales", "zs_quantize_shard",
             "zs_fused_shard_step_quant", "zs_dequant_gather", "zs_host_adamw_step", "zs_offload_adamw_step",
             "zs_accumulate_shard", "zs_grad_stats_workspace_bytes",
-            "zs_grad_stats", "zs_clip_scale", "zs_adamw_shard_step_accum", "zs_adamw_coefs_compute",
+            "zs_grad_stats", "zs_grad_stats_noalloc", "zs_clip_scale", "zs_adamw_shard_step_accum",
+            "zs_adamw_coefs_compute",
             "zs_fused_shard_step_dc", "zs_adamw_shard_step_dc", "zs_adamw_shard_step_accum_dc",
             "zs_fused_shard_step_multi_dc", "zs_last_error", "zs_version")
 
@@ -582,6 +585,14 @@ def zs_grad_stats(plan, acc, grad_divisor, sumsq_out, nonfinite_out, workspace, 
                               _scalar_ptr(sumsq_out, "float64", "sumsq_out"),
                               _scalar_ptr(nonfinite_out, "int32", "nonfinite_out"), workspace.data_ptr(),
                               workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def zs_grad_stats_noalloc(plan, acc, grad_divisor, sumsq_out, nonfinite_out, stream=None):
+    """zs_grad_stats with the partials in the library's static device array
+    (no workspace, no allocation); shards up to GRAD_STATS_NOALLOC_MAX_ELEMS."""
+    _check(_lib.zs_grad_stats_noalloc(plan.handle, _ptr(acc, "f32", plan.shard_numel, "acc"),
+                                      ctypes.c_float(grad_divisor), _scalar_ptr(sumsq_out, "float64", "sumsq_out"),
+                                      _scalar_ptr(nonfinite_out, "int32", "nonfinite_out"), _stream(stream)))
 
 
 def zs_clip_scale(sumsq, nonfinite, max_norm, scale_out, skip_out, stream=None):

@@ -648,6 +648,27 @@ zs_status zs_grad_stats(const zs_plan* plan, const float* acc_f32, float grad_di
                       "grad stats launch");
 }
 
+zs_status zs_grad_stats_noalloc(const zs_plan* plan, const float* acc_f32, float grad_divisor, double* sumsq_out,
+                                int32_t* nonfinite_out, void* stream) {
+    if (zs_status st = check_plan(plan)) return st;
+    if (zs_status st = check_ptr(acc_f32, "acc_f32")) return st;
+    if (!std::isfinite(grad_divisor) || grad_divisor == 0.0f)
+        return fail(ZS_EINVAL, "grad_divisor = %g must be finite and nonzero", (double)grad_divisor);
+    if (!sumsq_out || !nonfinite_out) return fail(ZS_EINVAL, "sumsq_out and nonfinite_out must not be NULL");
+    if ((reinterpret_cast<uintptr_t>(sumsq_out) & 7) || (reinterpret_cast<uintptr_t>(nonfinite_out) & 3))
+        return fail(ZS_EALIGN, "sumsq_out must be 8-byte and nonfinite_out 4-byte aligned");
+    const int64_t need = zs_grad_stats_workspace_bytes(plan);
+    if (need > zs::kNoallocScratchBytes)
+        return fail(ZS_ENOMEM,
+                    "a shard of %lld elements needs %lld bytes of partials, more than the %lld-byte static scratch "
+                    "of zs_grad_stats_noalloc (at most %lld elements); use zs_grad_stats with a workspace",
+                    (long long)plan->S, (long long)need, (long long)zs::kNoallocScratchBytes,
+                    (long long)ZS_GRAD_STATS_NOALLOC_MAX_ELEMS);
+    trace("zs_grad_stats_noalloc", plan, 0, 0, plan->S, stream);
+    return hip_status(zs::launch_grad_stats_noalloc(acc_f32, grad_divisor, sumsq_out, nonfinite_out, plan->S, stream),
+                      "grad stats launch");
+}
+
 zs_status zs_clip_scale(const double* sumsq, const int32_t* nonfinite, int32_t n_ranks, double max_norm,
                         float* scale_out, int32_t* skip_out, void* stream) {
     if (!sumsq || !nonfinite || !scale_out || !skip_out) return fail(ZS_EINVAL, "a pointer argument is NULL");

@@ -131,6 +131,12 @@ constexpr int64_t kStatsChunk = (int64_t)kBlockThreads * 4 * 16;
 int launch_accumulate(const void* const* contribs, int n, float* acc, int first, int64_t len, void* stream);
 int launch_grad_stats(const float* acc, float divisor, double* sumsq_out, int32_t* nonfinite_out, void* workspace,
                       int64_t len, void* stream);
+// The same two kernels with their partials in the library's statically
+// allocated device array (kNoallocScratchBytes per GPU) instead of a caller
+// workspace; the caller has checked that the shard's partials fit.
+constexpr int64_t kNoallocScratchBytes = (int64_t)4 << 20;
+int launch_grad_stats_noalloc(const float* acc, float divisor, double* sumsq_out, int32_t* nonfinite_out,
+                              int64_t len, void* stream);
 int launch_clip_scale(const double* sumsq, const int32_t* nonfinite, int n_ranks, double max_norm, float* scale_out,
                       int32_t* skip_out, void* stream);
 int launch_adamw_accum(const AdamCoef& c, const float* acc, float divisor, const float* scale, const int32_t* skip,

@@ -32,6 +32,8 @@
 //     results are bit-identical to a plain sequential implementation.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "zs_internal.h"
 
 namespace zs {
@@ -1327,6 +1329,42 @@ int launch_grad_stats(const float* acc, float divisor, double* sumsq_out, int32_
                            divisor, len / 4, part, flags);
     hipLaunchKernelGGL(k_stats_final, dim3(1), dim3(kFinalThreads), 0, s, part, flags, nb, sumsq_out, nonfinite_out);
     return (int)hipGetLastError();
+}
+
+// Partials of zs_grad_stats_noalloc, for callers that cannot allocate device
+// memory. Each GPU the library runs on holds its own copy until the process
+// ends. In host code `scratch` names a host-side stand-in, not device memory:
+// its device address on the current GPU comes from hipGetSymbolAddress, taken
+// once per device and kept.
+static __device__ __align__(256) char scratch[kNoallocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int launch_grad_stats_noalloc(const float* acc, float divisor, double* sumsq_out, int32_t* nonfinite_out,
+                              int64_t len, void* stream) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+    void* ptr = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (!g_scratch_ptr[dev]) {
+            e = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+            if (e != hipSuccess) {
+                g_scratch_ptr[dev] = nullptr;
+                return (int)e;
+            }
+        }
+        ptr = g_scratch_ptr[dev];
+    }
+    // k_stats writes every partial and flag before k_stats_final reads them,
+    // so nothing of a previous call's contents needs clearing.
+    return launch_grad_stats(acc, divisor, sumsq_out, nonfinite_out, ptr, len, stream);
 }
 
 int launch_clip_scale(const double* sumsq, const int32_t* nonfinite, int n_ranks, double max_norm, float* scale_out,

@@ -408,6 +408,21 @@ int64_t zs_grad_stats_workspace_bytes(const zs_plan* plan);
 zs_status zs_grad_stats(const zs_plan* plan, const float* acc_f32, float grad_divisor, double* sumsq_out,
                         int32_t* nonfinite_out, void* workspace, int64_t workspace_bytes, void* stream);
 
+/* zs_grad_stats for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and the same result bits, with the per-block partials in a
+ * 4 MiB array the library holds statically on each GPU it runs on (until the
+ * process ends) instead of a caller workspace. The call itself allocates
+ * nothing; its first call on a GPU looks up that GPU's copy of the array
+ * (call it there once outside a capture). Shards of more than
+ * ZS_GRAD_STATS_NOALLOC_MAX_ELEMS elements give ZS_ENOMEM and enqueue
+ * nothing. All calls on one GPU share its array: two of them in flight at
+ * once (on different streams) race and give wrong sums; calls on one stream
+ * are ordered and safe, each overwriting every partial it reads. */
+#define ZS_GRAD_STATS_NOALLOC_MAX_ELEMS 1431568384LL
+zs_status zs_grad_stats_noalloc(const zs_plan* plan, const float* acc_f32, float grad_divisor, double* sumsq_out,
+                                int32_t* nonfinite_out, void* stream);
+
 /* From the squared norms of all n_ranks shards (device array, added in rank
  * order) and their flags (device array): *scale_out = (float) min(1,
  * max_norm / (sqrt(sum) + 1e-6)) and *skip_out = 1 if any flag is set.

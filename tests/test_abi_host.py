@@ -411,3 +411,24 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
                          capture_output=True, text=True, timeout=120)
     assert res.returncode != 0
     assert "ImportError" in res.stderr and "is not built" in res.stderr, res.stderr
+
+
+def test_grad_stats_noalloc_validation_without_device(zs):
+    """The static-scratch norm call refuses bad arguments and shards whose
+    partials exceed its array before any device work (the array's address is
+    looked up only on a call that launches)."""
+    L = zs.lib()
+    big = zs.zs_shard_plan([zs.GRAD_STATS_NOALLOC_MAX_ELEMS + 8], 1, 0, 1)
+    assert L.zs_grad_stats_noalloc(big.handle, FAKE, 1.0, FAKE, FAKE + 64, None) == zs.ZS_ENOMEM
+    assert "static scratch" in zs.zs_last_error()
+    at_max = zs.zs_shard_plan([zs.GRAD_STATS_NOALLOC_MAX_ELEMS], 1, 0, 1)
+    assert zs.zs_grad_stats_workspace_bytes(at_max) == 4 << 20  # the largest shard fills the array exactly
+    assert zs.zs_grad_stats_workspace_bytes(big) > 4 << 20
+    h = zs.zs_shard_plan([4096], 4, 0).handle
+    assert L.zs_grad_stats_noalloc(h, FAKE, 0.0, FAKE, FAKE + 64, None) == zs.ZS_EINVAL  # zero divisor
+    assert L.zs_grad_stats_noalloc(h, FAKE, float("nan"), FAKE, FAKE + 64, None) == zs.ZS_EINVAL
+    assert L.zs_grad_stats_noalloc(h, None, 1.0, FAKE, FAKE + 64, None) == zs.ZS_EINVAL
+    assert L.zs_grad_stats_noalloc(h, FAKE, 1.0, None, FAKE + 64, None) == zs.ZS_EINVAL
+    assert L.zs_grad_stats_noalloc(h, FAKE + 4, 1.0, FAKE, FAKE + 64, None) == zs.ZS_EALIGN
+    assert L.zs_grad_stats_noalloc(h, FAKE, 1.0, FAKE + 4, FAKE + 64, None) == zs.ZS_EALIGN
+    assert L.zs_grad_stats_noalloc(None, FAKE, 1.0, FAKE, FAKE + 64, None) == zs.ZS_EINVAL
