@@ -14,7 +14,7 @@ import os
 
 import numpy as np
 
-from .plan import OraclePlan, plan_flat, plan_per_tensor, roundup  # noqa: F401
+from .plan import OraclePlan, ReshardSlice, plan_flat, plan_per_tensor, reshard_slice, roundup  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libzs_oracle.so")
@@ -142,6 +142,24 @@ def gather(p, rank, full, lo=0, hi=None):
     hi = S if hi is None else hi
     assert full.size >= (rank + 1) * S
     lib().ora_gather(_p16(p), S, rank, lo, hi, _p16(full))
+
+
+def gather_to_slice(p, own_off, slice_buf):
+    """The own updated bf16 shard p written into the kept k-way slice that
+    holds it (plan.reshard_slice's owner_slice), at own_off; nothing else of
+    the slice is touched."""
+    assert own_off >= 0 and own_off + p.size <= slice_buf.size
+    slice_buf[own_off:own_off + p.size] = p
+
+
+def gather_slice(shards, slice_buf):
+    """The receiving side of the group's gather: shard i (the updated shard of
+    the slice's i-th source rank) at i*S of the kept slice."""
+    S = shards[0].size
+    assert len(shards) * S == slice_buf.size
+    for i, sh in enumerate(shards):
+        assert sh.size == S
+        slice_buf[i * S:(i + 1) * S] = sh
 
 
 def shard_step(hp, contribs, g, master, m, v, p, full, rank, lo=0, hi=None):

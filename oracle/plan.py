@@ -124,3 +124,41 @@ def plan_per_tensor(numels, world, rank, persist_below=0):
         full_acc += Ti
     return OraclePlan("per_tensor", world, rank, 1, list(numels), offs, padded, full_acc, shard_acc,
                       pieces)
+
+
+@dataclass
+class ReshardSlice:
+    group_size: int  # k: ranks the parameters stay sharded over after forward
+    slice_index: int  # j = r mod k: which of the k equal slices of [0, T) this rank keeps
+    slice_off: int  # j * T/k
+    slice_len: int  # T/k
+    first_source: int  # the kept slice is the N-way shards of ranks first_source ..
+    n_sources: int  # .. first_source + n_sources - 1, in order (n_sources = N/k)
+    owner_slice: int  # the slice index that holds this rank's own shard: r div (N/k)
+    own_off: int  # where this rank's shard starts inside that slice: (r mod (N/k)) * S
+    retained_bytes: int  # bf16 parameter bytes this rank keeps after forward: 2 * T/k
+
+
+def reshard_slice(plan, k):
+    """The slice of the gathered flat buffer a rank keeps after forward when
+    parameters are resharded to a group of k ranks instead of all N.
+
+    "FSDP2's parameter lifecycle..." section "Reshard policy: pay for the
+    memory, or pay for the communication again": reshard_after_forward also
+    takes an integer, resharding to a smaller world size than N (intra-node,
+    say), so the backward AllGather only runs over that smaller group. The
+    plainest reading that makes the group intra-node: k divides N, the groups
+    are k consecutive ranks, and the k members of a group split the flat
+    buffer [0, T) into k equal contiguous slices, member position j = r mod k
+    keeping slice j. A slice of T/k elements is N/k consecutive N-way shards,
+    those of ranks j*N/k .. (j+1)*N/k - 1. k = N keeps only the own shard
+    (full resharding); k = 1 keeps the whole buffer (no resharding)."""
+    if plan.layout != "flat":
+        raise ValueError("reshard slices are defined on FLAT plans")
+    N, r, S, T = plan.world, plan.rank, plan.S, plan.T
+    if k < 1 or k > N or N % k:
+        raise ValueError(f"reshard group size {k} must divide the world size {N}")
+    per_slice = N // k
+    L = T // k
+    j = r % k
+    return ReshardSlice(k, j, j * L, L, j * per_slice, per_slice, r // per_slice, (r % per_slice) * S, 2 * L)
