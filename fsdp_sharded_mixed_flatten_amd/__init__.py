@@ -68,6 +68,13 @@ class PlanOptions(ctypes.Structure):
                 ("persist_below_elems", ctypes.c_int64), ("groups", ctypes.POINTER(ctypes.c_int32))]
 
 
+class ReshardSlice(ctypes.Structure):
+    _fields_ = [("group_size", ctypes.c_int32), ("slice_index", ctypes.c_int32), ("slice_off", ctypes.c_int64),
+                ("slice_len", ctypes.c_int64), ("first_source", ctypes.c_int32), ("n_sources", ctypes.c_int32),
+                ("owner_slice", ctypes.c_int32), ("reserved", ctypes.c_int32), ("own_off", ctypes.c_int64),
+                ("retained_bytes", ctypes.c_int64)]
+
+
 class PiecePtrs(ctypes.Structure):
     _fields_ = [("grad", ctypes.c_void_p), ("master", ctypes.c_void_p), ("m", ctypes.c_void_p),
                 ("v", ctypes.c_void_p), ("param", ctypes.c_void_p), ("full", ctypes.c_void_p)]
@@ -98,6 +105,9 @@ def _load():
         "zs_reduce_shard": (st, [vp, ctypes.POINTER(vp), i32, vp, i64, i64, vp]),
         "zs_adamw_shard_step": (st, [vp, ctypes.POINTER(AdamWHParams), vp, vp, vp, vp, vp, vp]),
         "zs_gather_params": (st, [vp, vp, vp, vp]),
+        "zs_plan_reshard_slice": (st, [vp, i32, ctypes.POINTER(ReshardSlice)]),
+        "zs_gather_params_to_slice": (st, [vp, i32, vp, vp, vp]),
+        "zs_gather_slice": (st, [vp, i32, ctypes.POINTER(vp), i32, vp, vp]),
         "zs_fused_shard_step": (st, [vp, ctypes.POINTER(AdamWHParams), ctypes.POINTER(vp), i32, vp, vp,
                                      vp, vp, vp, vp, vp]),
         "zs_fused_shard_step_bucket": (st, [vp, ctypes.POINTER(AdamWHParams), ctypes.POINTER(vp), i32, vp, vp,
@@ -148,7 +158,8 @@ EXPORTED = ("zs_shard_plan", "zs_shard_plan_ex", "zs_plan_tensor_group", "zs_pla
             "zs_plan_destroy", "zs_plan_padded_numel", "zs_plan_shard_numel",
             "zs_plan_persistent_bytes", "zs_plan_num_tensors", "zs_plan_world_size", "zs_plan_rank",
             "zs_plan_layout", "zs_plan_tensor", "zs_reduce_shard", "zs_adamw_shard_step",
-            "zs_gather_params", "zs_fused_shard_step", "zs_fused_shard_step_bucket", "zs_multi_workspace_bytes",
+            "zs_gather_params", "zs_plan_reshard_slice", "zs_gather_params_to_slice", "zs_gather_slice",
+            "zs_fused_shard_step", "zs_fused_shard_step_bucket", "zs_multi_workspace_bytes",
             "zs_plan_workspace_bytes",
             "zs_multi_bind", "zs_multi_unbind",
             "zs_reduce_shard_multi", "zs_adamw_shard_step_multi", "zs_gather_params_multi",
@@ -340,6 +351,29 @@ def zs_gather_params(plan, param, full, stream=None):
     S, r = plan.shard_numel, plan.rank
     _check(_lib.zs_gather_params(plan.handle, _ptr(param, "bf16", S, "param"),
                                  _ptr(full, "bf16", (r + 1) * S, "full"), _stream(stream)))
+
+
+def zs_plan_reshard_slice(plan, group_size):
+    out = ReshardSlice()
+    _check(_lib.zs_plan_reshard_slice(plan.handle, group_size, ctypes.byref(out)))
+    return out
+
+
+def zs_gather_params_to_slice(plan, group_size, param, slice_buf, stream=None):
+    """param: the own updated bf16 shard (S); slice_buf: the buffer holding the
+    k-way slice that contains it (T/k elements)."""
+    sl = zs_plan_reshard_slice(plan, group_size)
+    _check(_lib.zs_gather_params_to_slice(plan.handle, group_size, _ptr(param, "bf16", plan.shard_numel, "param"),
+                                          _ptr(slice_buf, "bf16", sl.slice_len, "slice"), _stream(stream)))
+
+
+def zs_gather_slice(plan, group_size, shards, slice_buf, stream=None):
+    """shards[i]: the updated bf16 shard (S) of rank first_source + i;
+    slice_buf: this rank's kept slice (T/k elements)."""
+    sl = zs_plan_reshard_slice(plan, group_size)
+    ptrs = [_ptr(t, "bf16", plan.shard_numel, f"shards[{i}]") for i, t in enumerate(shards)]
+    _check(_lib.zs_gather_slice(plan.handle, group_size, _ptr_array(ptrs), len(ptrs),
+                                _ptr(slice_buf, "bf16", sl.slice_len, "slice"), _stream(stream)))
 
 
 def zs_fused_shard_step(plan, hp, contribs, master, m, v, grad=None, param=None, full=None,

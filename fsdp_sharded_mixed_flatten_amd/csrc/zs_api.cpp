@@ -399,6 +399,74 @@ zs_status zs_gather_params(const zs_plan* plan, const void* param_bf16, void* fu
     return hip_status(zs::launch_gather(param_bf16, own, plan->S, stream), "gather launch");
 }
 
+// ------------------------------------------------------------------ resharding to a smaller group
+
+namespace {
+
+zs_status check_group(const zs_plan* plan, int32_t k) {
+    if (zs_status st = check_plan(plan)) return st;
+    if (plan->layout != ZS_LAYOUT_FLAT) return fail(ZS_EINVAL, "reshard slices need a FLAT plan");
+    if (k < 1 || k > plan->world || plan->world % k)
+        return fail(ZS_EINVAL, "reshard group size %d must divide the world size %d", k, plan->world);
+    return ZS_OK;
+}
+
+zs_reshard_slice make_slice(const zs_plan* plan, int32_t k) {
+    const int32_t per_slice = plan->world / k;
+    const int64_t len = plan->T / k;
+    zs_reshard_slice s{};
+    s.group_size = k;
+    s.slice_index = plan->rank % k;
+    s.slice_off = (int64_t)s.slice_index * len;
+    s.slice_len = len;
+    s.first_source = s.slice_index * per_slice;
+    s.n_sources = per_slice;
+    s.owner_slice = plan->rank / per_slice;
+    s.reserved = 0;
+    s.own_off = (int64_t)(plan->rank % per_slice) * plan->S;
+    s.retained_bytes = 2 * len;
+    return s;
+}
+
+}  // namespace
+
+zs_status zs_plan_reshard_slice(const zs_plan* plan, int32_t group_size, zs_reshard_slice* out) {
+    if (zs_status st = check_group(plan, group_size)) return st;
+    if (!out) return fail(ZS_EINVAL, "out is NULL");
+    *out = make_slice(plan, group_size);
+    return ZS_OK;
+}
+
+zs_status zs_gather_params_to_slice(const zs_plan* plan, int32_t group_size, const void* param_bf16,
+                                    void* slice_bf16, void* stream) {
+    if (zs_status st = check_group(plan, group_size)) return st;
+    if (zs_status st = check_ptr(param_bf16, "param_bf16")) return st;
+    if (zs_status st = check_ptr(slice_bf16, "slice_bf16")) return st;
+    if (plan->S == 0) return ZS_OK;
+    const zs_reshard_slice s = make_slice(plan, group_size);
+    char* own = static_cast<char*>(slice_bf16) + 2 * s.own_off;
+    trace("zs_gather_params_to_slice", plan, 0, s.own_off, plan->S, stream);
+    return hip_status(zs::launch_gather(param_bf16, own, plan->S, stream), "gather launch");
+}
+
+zs_status zs_gather_slice(const zs_plan* plan, int32_t group_size, const void* const* shards, int32_t n_shards,
+                          void* slice_bf16, void* stream) {
+    if (zs_status st = check_group(plan, group_size)) return st;
+    const int32_t need = plan->world / group_size;
+    if (!shards) return fail(ZS_EINVAL, "shards is NULL");
+    if (n_shards != need)
+        return fail(ZS_EINVAL, "a slice of a %d-rank group is %d shards, got %d", group_size, need, n_shards);
+    for (int32_t i = 0; i < n_shards; ++i) {
+        char what[32];
+        std::snprintf(what, sizeof what, "shards[%d]", i);
+        if (zs_status st = check_ptr(shards[i], what)) return st;
+    }
+    if (zs_status st = check_ptr(slice_bf16, "slice_bf16")) return st;
+    if (plan->S == 0) return ZS_OK;
+    trace("zs_gather_slice", plan, n_shards, 0, plan->T / group_size, stream);
+    return hip_status(zs::launch_gather_sources(shards, n_shards, slice_bf16, plan->S, stream), "gather launch");
+}
+
 zs_status zs_fused_shard_step(const zs_plan* plan, const zs_adamw_hparams* hp, const void* const* contribs,
                               int32_t n_contribs, float* master, float* m, float* v, void* grad_bf16,
                               void* param_bf16, void* full_bf16, void* stream) {

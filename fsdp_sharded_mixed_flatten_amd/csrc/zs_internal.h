@@ -115,6 +115,9 @@ int launch_adamw(const AdamCoef& c, const void* grad, float* master, float* m, f
                  void* param, void* full_at_own, int64_t len, void* stream, const QuantOut* q = nullptr,
                  const AdamCoef* cdev = nullptr);
 int launch_gather(const void* param, void* full_at_own, int64_t len, void* stream);
+// n shards of len elements each, srcs[q] copied to dst + q*len (one launch per
+// ZS_MAX_CONTRIBS sources).
+int launch_gather_sources(const void* const* srcs, int n, void* dst, int64_t len, void* stream);
 int launch_fused(const AdamCoef& c, const void* const* contribs, int n, float* master, float* m,
                  float* v, void* grad, void* param, void* full_at_own, int64_t len, void* stream,
                  const QuantOut* q = nullptr, const AdamCoef* cdev = nullptr);

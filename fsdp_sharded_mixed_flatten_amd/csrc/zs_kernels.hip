@@ -595,6 +595,14 @@ __global__ __launch_bounds__(kBlock) void k_fused(AdamCoef c, const AdamCoef* __
                          qo);
 }
 
+// The receiving side of a gather into a k-way slice: blockIdx.y is the source
+// whose S-element shard a block copies (8 elements per lane) to dst + y*S.
+__global__ __launch_bounds__(kBlock) void k_gather_sources(Ptrs<ZS_MAX_CONTRIBS> src, u32x4* __restrict__ dst,
+                                                           int64_t n8) {
+    const int q = blockIdx.y;
+    copy_tile<u32x4, 1>(reinterpret_cast<const u32x4*>(src.p[q]), dst + (int64_t)q * n8, tile_base(1), n8);
+}
+
 // Codes of a bf16 shard, 8 elements per lane.
 template <int QB>
 __global__ __launch_bounds__(kBlock) void k_quant(const u32x4* __restrict__ p, QuantOut qo, int64_t n8) {
@@ -1258,6 +1266,20 @@ int launch_gather(const void* param, void* full_at_own, int64_t len, void* strea
     hipLaunchKernelGGL(k_gather, dim3(grid_for(n8, 1)), dim3(kBlock), kGatherLds, (hipStream_t)stream,
                        reinterpret_cast<const u32x4*>(param), reinterpret_cast<u32x4*>(full_at_own), n8);
     return (int)hipGetLastError();
+}
+
+int launch_gather_sources(const void* const* srcs, int n, void* dst, int64_t len, void* stream) {
+    if (len <= 0 || n <= 0) return 0;
+    const int64_t n8 = len / 8;
+    for (int q0 = 0; q0 < n; q0 += ZS_MAX_CONTRIBS) {
+        const int cnt = n - q0 < ZS_MAX_CONTRIBS ? n - q0 : ZS_MAX_CONTRIBS;
+        Ptrs<ZS_MAX_CONTRIBS> sp{};
+        for (int q = 0; q < cnt; ++q) sp.p[q] = srcs[q0 + q];
+        hipLaunchKernelGGL(k_gather_sources, dim3(grid_for(n8, 1), (unsigned)cnt), dim3(kBlock), kGatherLds,
+                           (hipStream_t)stream, sp, reinterpret_cast<u32x4*>(dst) + (int64_t)q0 * n8, n8);
+        if (int e = (int)hipGetLastError()) return e;
+    }
+    return 0;
 }
 
 int launch_fused(const AdamCoef& c, const void* const* contribs, int n, float* master, float* m, float* v,

@@ -239,6 +239,47 @@ zs_status zs_fused_shard_step_bucket(const zs_plan* plan, const zs_adamw_hparams
                                      float* v, void* grad_bf16, void* param_bf16, void* full_bf16, int64_t off,
                                      int64_t len, void* stream);
 
+/* ------------------------------------------------------------------ resharding to a smaller group
+ * FSDP2's reshard_after_forward also takes an integer k: after forward the
+ * parameters stay sharded over a group of k ranks instead of all N, e.g.
+ * within a node, so the backward all-gather spans only that group ("FSDP2's
+ * parameter lifecycle...", section "Reshard policy: pay for the memory, or
+ * pay for the communication again"). Here k divides N and the groups are k
+ * consecutive ranks; the k members of a group split the gathered flat buffer
+ * [0, T) into k equal slices, the member at position j = r mod k keeping
+ * slice j: T/k elements, the N-way shards of ranks j*N/k .. (j+1)*N/k - 1 in
+ * order. k = N keeps only the own shard (full resharding), k = 1 the whole
+ * buffer (no resharding). FLAT plans only. */
+typedef struct zs_reshard_slice {
+    int32_t group_size;     /* k */
+    int32_t slice_index;    /* j = r mod k: the slice this rank keeps */
+    int64_t slice_off;      /* j*T/k: its start in the gathered flat buffer */
+    int64_t slice_len;      /* T/k elements */
+    int32_t first_source;   /* the kept slice is the shards of ranks first_source .. */
+    int32_t n_sources;      /* .. first_source + n_sources - 1 (n_sources = N/k) */
+    int32_t owner_slice;    /* r div (N/k): the slice that holds this rank's own shard */
+    int32_t reserved;       /* 0 */
+    int64_t own_off;        /* (r mod (N/k))*S: the own shard's start inside that slice */
+    int64_t retained_bytes; /* 2*T/k: bf16 parameter bytes a rank keeps after forward */
+} zs_reshard_slice;
+
+/* Fills *out for group size k (1 <= k <= N, N % k == 0). Host only. */
+zs_status zs_plan_reshard_slice(const zs_plan* plan, int32_t group_size, zs_reshard_slice* out);
+
+/* The gather write of the step into a k-way slice: the own updated shard
+ * (param_bf16, S elements) goes to slice_bf16[own_off + j], where
+ * slice_bf16 holds slice owner_slice (T/k elements); nothing else of the
+ * buffer is touched. With k = 1 this is zs_gather_params. */
+zs_status zs_gather_params_to_slice(const zs_plan* plan, int32_t group_size, const void* param_bf16,
+                                    void* slice_bf16, void* stream);
+
+/* The receiving side of the gather into the kept slice: shards is a host
+ * array of n_shards = N/k device pointers, shards[i] the updated bf16 shard
+ * (S elements) of rank first_source + i; each is written to slice_bf16 at
+ * i*S, filling this rank's kept slice (T/k elements). */
+zs_status zs_gather_slice(const zs_plan* plan, int32_t group_size, const void* const* shards, int32_t n_shards,
+                          void* slice_bf16, void* stream);
+
 /* ------------------------------------------------------------------ multi-tensor
  * Multi-tensor apply over the owned pieces of a PER_TENSOR plan whose
  * per-tensor state lives in separate allocations (FSDP2's per-parameter

@@ -20,6 +20,7 @@ int launch_adamw(const AdamCoef&, const void*, float*, float*, float*, void*, vo
     return ++g_launches, 0;
 }
 int launch_gather(const void*, void*, int64_t, void*) { return ++g_launches, 0; }
+int launch_gather_sources(const void* const*, int, void*, int64_t, void*) { return ++g_launches, 0; }
 int launch_fused(const AdamCoef&, const void* const*, int, float*, float*, float*, void*, void*, void*, int64_t,
                  void*, const QuantOut*, const AdamCoef*) {
     return ++g_launches, 0;

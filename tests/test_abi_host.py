@@ -432,3 +432,51 @@ def test_grad_stats_noalloc_validation_without_device(zs):
     assert L.zs_grad_stats_noalloc(h, FAKE + 4, 1.0, FAKE, FAKE + 64, None) == zs.ZS_EALIGN
     assert L.zs_grad_stats_noalloc(h, FAKE, 1.0, FAKE + 4, FAKE + 64, None) == zs.ZS_EALIGN
     assert L.zs_grad_stats_noalloc(None, FAKE, 1.0, FAKE, FAKE + 64, None) == zs.ZS_EINVAL
+
+
+def test_reshard_slice_query_equals_oracle(zs):
+    """The library's k-way reshard slice (host-only query) equals the oracle's
+    for every divisor k of N on random FLAT plans, every rank."""
+    import random
+    from oracle.plan import plan_flat, reshard_slice
+    rng = random.Random(11)
+    fields = ("group_size", "slice_index", "slice_off", "slice_len", "first_source", "n_sources", "owner_slice",
+              "own_off", "retained_bytes")
+    for _ in range(25):
+        N = rng.choice([1, 2, 3, 4, 6, 8, 12, 16, 64, 96])
+        numels = [rng.randrange(0, 70_000) for _ in range(rng.randrange(1, 5))]
+        align = rng.choice([1, 8, 128])
+        for r in sorted({0, N - 1, rng.randrange(N)}):
+            plan = zs.zs_shard_plan(numels, N, r, align)
+            op = plan_flat(numels, N, r, align)
+            for k in [d for d in range(1, N + 1) if N % d == 0]:
+                got = zs.zs_plan_reshard_slice(plan, k)
+                want = reshard_slice(op, k)
+                assert tuple(getattr(got, f) for f in fields) == tuple(getattr(want, f) for f in fields), (N, r, k)
+                assert got.reserved == 0
+
+
+def test_reshard_validation_without_device(zs):
+    L = zs.lib()
+    vp = ctypes.c_void_p
+    plan = zs.zs_shard_plan([1000], 8, 3)
+    h = plan.handle
+    out = zs.ReshardSlice()
+    for k in (0, 3, 9, -1):
+        assert L.zs_plan_reshard_slice(h, k, ctypes.byref(out)) == zs.ZS_EINVAL
+    assert L.zs_plan_reshard_slice(h, 4, None) == zs.ZS_EINVAL
+    pt = zs.zs_shard_plan([1000], 8, 3, 1, zs.ZS_LAYOUT_PER_TENSOR)
+    assert L.zs_plan_reshard_slice(pt.handle, 4, ctypes.byref(out)) == zs.ZS_EINVAL
+    assert L.zs_gather_params_to_slice(h, 3, FAKE, FAKE, None) == zs.ZS_EINVAL
+    assert L.zs_gather_params_to_slice(h, 4, None, FAKE, None) == zs.ZS_EINVAL
+    assert L.zs_gather_params_to_slice(h, 4, FAKE + 8, FAKE, None) == zs.ZS_EALIGN
+    assert L.zs_gather_params_to_slice(h, 4, FAKE, FAKE + 2, None) == zs.ZS_EALIGN
+    two = (vp * 2)(FAKE, FAKE + 4096)
+    assert L.zs_gather_slice(h, 4, two, 3, FAKE, None) == zs.ZS_EINVAL  # N/k = 2 shards
+    assert L.zs_gather_slice(h, 4, None, 2, FAKE, None) == zs.ZS_EINVAL
+    bad = (vp * 2)(FAKE, None)
+    assert L.zs_gather_slice(h, 4, bad, 2, FAKE, None) == zs.ZS_EINVAL
+    mis = (vp * 2)(FAKE, FAKE + 4)
+    assert L.zs_gather_slice(h, 4, mis, 2, FAKE, None) == zs.ZS_EALIGN
+    assert L.zs_gather_slice(h, 4, two, 2, FAKE + 2, None) == zs.ZS_EALIGN
+    assert L.zs_gather_slice(pt.handle, 4, two, 2, FAKE, None) == zs.ZS_EINVAL
