@@ -510,7 +510,6 @@ def flat_extra_legs(zs, synth, torch, wl, plan, hp0, st, args, head):
         paths["accum_clip"] = {"micro_steps": G, "max_norm": args.clip, "ms_per_step": a_wall,
                                "device_ms_per_step": a_dev, "events_ms_median": statistics.median(a_t.ms()),
                                "bytes_per_param": a_bytes, "gbps": S * a_bytes / a_dev / 1e6}
-        del acc, ws
     if S <= GRAPH_MAX_ELEMS:
         # launch-bound: the same steps replayed from a HIP graph, 20 per graph
         for name, fn in graphable.items():
