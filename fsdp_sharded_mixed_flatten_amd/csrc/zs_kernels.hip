@@ -1368,15 +1368,25 @@ void* g_scratch_ptr[kMaxDevices] = {};
 
 int launch_grad_stats_noalloc(const float* acc, float divisor, double* sumsq_out, int32_t* nonfinite_out,
                               int64_t len, void* stream) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+    // the copy of the array on the GPU the kernels run on: the stream's device
+    // (the current device for the null stream)
+    hipDevice_t dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, &dev) : hipGetDevice(&dev);
     if (e != hipSuccess) return (int)e;
     if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
     void* ptr = nullptr;
     {
         std::lock_guard<std::mutex> lock(g_scratch_mu);
         if (!g_scratch_ptr[dev]) {
-            e = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+            // looked up once per device, with that device current
+            int cur = 0;
+            e = hipGetDevice(&cur);
+            if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+            if (e == hipSuccess) e = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+            if (cur != dev) {
+                const hipError_t r = hipSetDevice(cur);
+                if (e == hipSuccess) e = r;
+            }
             if (e != hipSuccess) {
                 g_scratch_ptr[dev] = nullptr;
                 return (int)e;

@@ -454,8 +454,9 @@ zs_status zs_grad_stats(const zs_plan* plan, const float* acc_f32, float grad_di
  * same kernels and the same result bits, with the per-block partials in a
  * 4 MiB array the library holds statically on each GPU it runs on (until the
  * process ends) instead of a caller workspace. The call itself allocates
- * nothing; its first call on a GPU looks up that GPU's copy of the array
- * (call it there once outside a capture). Shards of more than
+ * nothing and uses the copy on the stream's GPU (the current GPU for the
+ * null stream); its first call for a GPU looks up that GPU's copy (call it
+ * there once outside a capture). Shards of more than
  * ZS_GRAD_STATS_NOALLOC_MAX_ELEMS elements give ZS_ENOMEM and enqueue
  * nothing. All calls on one GPU share its array: two of them in flight at
  * once (on different streams) race and give wrong sums; calls on one stream
