@@ -57,7 +57,8 @@ constexpr int kAdamwU = 1;
 constexpr int kFusedU = 1;
 // Occupancy throttle: bytes of untouched dynamic LDS per block (160 KiB per
 // CU), which caps the resident 64-thread blocks per CU.
-//   fused step, N > 4: 16 KiB (ten waves per CU);
+//   fused step, N > 4: 16 KiB (ten waves per CU; 12 KiB 2% slower, 20 KiB
+//   the same);
 constexpr unsigned kFusedLds = 16u << 10;
 //   fused step at 4 or fewer ranks, whose lighter reads leave room for more
 //   resident waves: eleven per CU (14 KiB) measured 1.4% faster than ten or
@@ -76,14 +77,19 @@ constexpr unsigned kAccumNarrowLds = 8u << 10;
 constexpr unsigned kReduceLds = 8u << 10;
 constexpr unsigned kReduceWideLds = 32u << 10;
 constexpr int kWideN = 32;
-//   AdamW, gather and the bf16 codes of a shard: 8 KiB (6-14 KiB within noise);
-constexpr unsigned kAdamwLds = 8u << 10;
-constexpr unsigned kGatherLds = 8u << 10;
-//   multi-tensor kernels: 12 KiB unfused (3% faster than 14, 5% than 16) and
-//   14 KiB for the fused step (1.6% faster than 12, 3% than 16 at the
-//   Llama-7B wrap-stress shape);
+//   AdamW (from the grad shard or the accumulator): 12 KiB (1-3% faster than
+//   8 or 16 KiB at all three shapes with the nt sc1 stores);
+constexpr unsigned kAdamwLds = 12u << 10;
+//   gather copies and the bf16 codes of a shard: 4 KiB (3.5% faster than 8;
+//   0 and 2 KiB the same as 4, 16 KiB 50% slower);
+constexpr unsigned kGatherLds = 4u << 10;
+//   multi-tensor kernels: 12 KiB for reduce and AdamW (10 and 14 KiB slower),
+//   14 KiB for the fused step (12 KiB 2% slower, 16 the same, 18 and 20 KiB
+//   slower at the Llama-7B wrap-stress shape) and 8 KiB for the gather (12%
+//   faster than 12 KiB, 2% faster than 4 KiB or none);
 constexpr unsigned kMultiLds = 12u << 10;
 constexpr unsigned kMultiFusedLds = 14u << 10;
+constexpr unsigned kMultiGatherLds = 8u << 10;
 //   dequantizing gather, a nearly pure write stream: none (a throttle cost it
 //   up to 2x). Its lanes decode four 8-element units each.
 constexpr unsigned kDequantLds = 0;
@@ -184,15 +190,46 @@ __device__ __forceinline__ AdamCoef pick_coef(const AdamCoef& c, const AdamCoef*
     return d;
 }
 
-// Cache policy per access class: read-once inputs, the read-modify-write
-// optimizer state and write-once outputs are all nontemporal (each class was
-// swept; every cached variant was slower).
+// Streamed store of one unit of a wave's row: lane L of the wave writes unit
+// L of a row of kBlock consecutive units, which starts at p - L. The store
+// goes through a buffer resource based at the row's first unit (the same
+// address in every lane, taken into scalar registers) and bounded by the
+// row's bytes, with the lane's byte offset as its vector offset, so that it
+// can carry the full cache policy: nontemporal with sc1 set. At the Llama-7B
+// shape this is 2-3% faster for the fused step and up to 4% for AdamW than
+// the global nontemporal store (nt alone, which a buffer store with nt alone
+// times the same as); sc1 without nt is slower than both.
+constexpr int kBufferWord3 = 0x00020000;  // raw (untyped) buffer: 32-bit data format
+constexpr int kStreamAux = 2 | 16;        // nt | sc1
+
+template <typename T>
+__device__ __forceinline__ void st_lane(T* p, T x) {
+    static_assert(kBlock == 64, "a row is one wave: blocks are single waves");
+    const uintptr_t row = reinterpret_cast<uintptr_t>(p - threadIdx.x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)row);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(row >> 32));
+    void* base = reinterpret_cast<void*>(((uintptr_t)hi << 32) | lo);
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(base, (short)0, kBlock * (int)sizeof(T), kBufferWord3);
+    const int off = (int)(threadIdx.x * sizeof(T));
+    if constexpr (sizeof(T) == 16)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, kStreamAux);
+    else {
+        static_assert(sizeof(T) == 8, "rows of 8- or 16-byte units");
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), r, off, 0, kStreamAux);
+    }
+}
+
+// Cache policy per access class: read-once inputs and the read-modify-write
+// optimizer state are nontemporal loads (each class was swept; every cached
+// variant was slower); rows written by a whole wave (the state, the grad and
+// parameter outputs, gather copies) are st_lane stores, other writes (codes,
+// scales, the multi-tensor gather and reduce, whose lanes write two chunks)
+// nontemporal global stores.
 template <typename T>
 __device__ __forceinline__ T ld_in(const T* p) { return ld_nt(p); }
 template <typename T>
 __device__ __forceinline__ T ld_state(const T* p) { return ld_nt(p); }
-template <typename T>
-__device__ __forceinline__ void st_state(T* p, T x) { st_nt(p, x); }
 template <typename T>
 __device__ __forceinline__ void st_out(T* p, T x) { st_nt(p, x); }
 
@@ -293,8 +330,10 @@ __device__ __forceinline__ u32x2 avg_bf16x4(const float* a, float nf) {
 // ------------------------------------------------------------------ tiles
 //
 // A tile is kBlock lanes x U units; a lane's units sit at base, base + kBlock,
-// ... (in units of the tile's vector type); units at or past `limit` are
-// skipped. Optional outputs are nullptr when not written (uniform per block).
+// ... (in units of the tile's vector type), where base is the tile's first
+// unit plus the lane's index (the row layout st_lane stores); units at or past
+// `limit` are skipped. Optional outputs are nullptr when not written (uniform
+// per block).
 
 // reduce in units of 8 elements (bf16 only)
 template <int N, int U>
@@ -317,7 +356,7 @@ __device__ __forceinline__ void reduce8_tile(const void* const* cp, int n_rt, fl
         o.y = pack2(div_n<N>(a[k][2], nf), div_n<N>(a[k][3], nf));
         o.z = pack2(div_n<N>(a[k][4], nf), div_n<N>(a[k][5], nf));
         o.w = pack2(div_n<N>(a[k][6], nf), div_n<N>(a[k][7], nf));
-        st_out(out + u[k], o);
+        st_lane(out + u[k], o);
     }
 }
 
@@ -466,11 +505,11 @@ __device__ __forceinline__ void adamw_tile(const AdamCoef& c, const u32x2* __res
 #pragma unroll
     for (int k = 0; k < U; ++k) {
         if (!ok[k]) continue;
-        st_state(master + u[k], wv[k]);
-        st_state(m + u[k], mv[k]);
-        st_state(v + u[k], vv[k]);
-        if (param) st_out(param + u[k], pv[k]);
-        if (full) st_out(full + u[k], pv[k]);
+        st_lane(master + u[k], wv[k]);
+        st_lane(m + u[k], mv[k]);
+        st_lane(v + u[k], vv[k]);
+        if (param) st_lane(param + u[k], pv[k]);
+        if (full) st_lane(full + u[k], pv[k]);
         if constexpr (QB != 0) quant_emit<QB, 4>(qw[k], u[k], qo);
     }
 }
@@ -487,7 +526,7 @@ __device__ __forceinline__ void copy_tile(const V* __restrict__ src, V* __restri
 #pragma unroll
     for (int k = 0; k < U; ++k) {
         const int64_t u = base + (int64_t)k * kBlock;
-        if (u < limit) st_out(dst + u, x[k]);
+        if (u < limit) st_lane(dst + u, x[k]);
     }
 }
 
@@ -521,13 +560,13 @@ __device__ __forceinline__ void fused_tile(const AdamCoef& c, const void* const*
             if (!ok[k]) continue;
             const u32x2 g = avg_bf16x4<N>(a[k], nf);
             adamw_unit(c, g, wv[k], mv[k], vv[k]);
-            st_state(master + u[k], wv[k]);
-            st_state(m + u[k], mv[k]);
-            st_state(v + u[k], vv[k]);
+            st_lane(master + u[k], wv[k]);
+            st_lane(m + u[k], mv[k]);
+            st_lane(v + u[k], vv[k]);
             const u32x2 p = to_bf16x4(wv[k]);
-            if (grad) st_out(grad + u[k], g);
-            if (param) st_out(param + u[k], p);
-            if (full) st_out(full + u[k], p);
+            if (grad) st_lane(grad + u[k], g);
+            if (param) st_lane(param + u[k], p);
+            if (full) st_lane(full + u[k], p);
         }
     } else {
         // Codes are computed by every lane before any store is issued.
@@ -547,12 +586,12 @@ __device__ __forceinline__ void fused_tile(const AdamCoef& c, const void* const*
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             if (!ok[k]) continue;
-            st_state(master + u[k], wv[k]);
-            st_state(m + u[k], mv[k]);
-            st_state(v + u[k], vv[k]);
-            if (grad) st_out(grad + u[k], gv[k]);
-            if (param) st_out(param + u[k], pv[k]);
-            if (full) st_out(full + u[k], pv[k]);
+            st_lane(master + u[k], wv[k]);
+            st_lane(m + u[k], mv[k]);
+            st_lane(v + u[k], vv[k]);
+            if (grad) st_lane(grad + u[k], gv[k]);
+            if (param) st_lane(param + u[k], pv[k]);
+            if (full) st_lane(full + u[k], pv[k]);
             quant_emit<QB, 4>(qw[k], u[k], qo);
         }
     }
@@ -717,7 +756,7 @@ __global__ __launch_bounds__(kBlock) void k_dequant(const char* __restrict__ cod
         o.z = pack2_finite(x[4], x[5]);
         o.w = pack2_finite(x[6], x[7]);
         if (sc != sc) o = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
-        st_out(full + r * s8 + u, o);
+        st_lane(full + r * s8 + u, o);
     }
 }
 
@@ -897,7 +936,7 @@ __device__ __forceinline__ void accum_tile(const void* const* cp, int n_rt, floa
         r.y = av[k].y + hi_bf16(g.x);
         r.z = av[k].z + lo_bf16(g.y);
         r.w = av[k].w + hi_bf16(g.y);
-        st_state(acc + u[k], r);
+        st_lane(acc + u[k], r);
     }
 }
 
@@ -1051,12 +1090,12 @@ __device__ __forceinline__ void adamw_accum_tile(const AdamCoef& c, const f32x4*
             adamw_elem(c, g, w[e], mm[e], vv4[e]);
         }
         const f32x4 wn{w[0], w[1], w[2], w[3]};
-        st_state(master + u, wn);
-        st_state(m + u, f32x4{mm[0], mm[1], mm[2], mm[3]});
-        st_state(v + u, f32x4{vv4[0], vv4[1], vv4[2], vv4[3]});
+        st_lane(master + u, wn);
+        st_lane(m + u, f32x4{mm[0], mm[1], mm[2], mm[3]});
+        st_lane(v + u, f32x4{vv4[0], vv4[1], vv4[2], vv4[3]});
         const u32x2 p = to_bf16x4(wn);
-        if (param) st_out(param + u, p);
-        if (full) st_out(full + u, p);
+        if (param) st_lane(param + u, p);
+        if (full) st_lane(full + u, p);
     }
 }
 
@@ -1317,8 +1356,8 @@ int launch_multi(int op, const CoefTable* c, const void* workspace, const MultiO
         case kOpGather:
             hipLaunchKernelGGL(k_multi_gather, dim3((unsigned)((n_chunks + kGatherChunksPerBlock - 1) /
                                                                kGatherChunksPerBlock)),
-                               dim3(kBlock), kMultiLds, s, reinterpret_cast<const MultiHeader*>(workspace), off,
-                               n_chunks);
+                               dim3(kBlock), kMultiGatherLds, s, reinterpret_cast<const MultiHeader*>(workspace),
+                               off, n_chunks);
             return (int)hipGetLastError();
         default: return launch_multi_op<kOpFused>(cc, cdev, workspace, off, n_chunks, n_contribs, s);
     }
