@@ -90,9 +90,11 @@ constexpr unsigned kGatherLds = 4u << 10;
 constexpr unsigned kMultiLds = 12u << 10;
 constexpr unsigned kMultiFusedLds = 14u << 10;
 constexpr unsigned kMultiGatherLds = 8u << 10;
-//   dequantizing gather, a nearly pure write stream: none (a throttle cost it
-//   up to 2x). Its lanes decode four 8-element units each.
-constexpr unsigned kDequantLds = 0;
+//   dequantizing gather, a nearly pure write stream: 4 KiB (2% faster than
+//   none, 2 or 3 KiB at the Llama-7B and Qwen2.5-3B shapes, 5 KiB 0.5%
+//   slower; 6 KiB and up 13-20% slower, larger throttles up to 2x). Its
+//   lanes decode four 8-element units each.
+constexpr unsigned kDequantLds = 4u << 10;
 constexpr int kDequantU = 4;
 // World size from which the fused entry point runs the reduce into the grad
 // shard, then AdamW + gather, when the caller provides the grad buffer: at
@@ -190,27 +192,33 @@ __device__ __forceinline__ AdamCoef pick_coef(const AdamCoef& c, const AdamCoef*
     return d;
 }
 
-// Streamed store of one unit of a wave's row: lane L of the wave writes unit
-// L of a row of kBlock consecutive units, which starts at p - L. The store
-// goes through a buffer resource based at the row's first unit (the same
-// address in every lane, taken into scalar registers) and bounded by the
-// row's bytes, with the lane's byte offset as its vector offset, so that it
-// can carry the full cache policy: nontemporal with sc1 set. At the Llama-7B
-// shape this is 2-3% faster for the fused step and up to 4% for AdamW than
-// the global nontemporal store (nt alone, which a buffer store with nt alone
-// times the same as); sc1 without nt is slower than both.
+// Rows: lane L of the wave accesses unit L of a row of kBlock consecutive
+// units, which starts at p - L. Such an access can go through a buffer
+// resource based at the row's first unit (the same address in every lane,
+// taken into scalar registers) and bounded by the row's bytes, with the
+// lane's byte offset as its vector offset; a buffer access carries the full
+// cache-policy field, a global one written in HIP only nt.
 constexpr int kBufferWord3 = 0x00020000;  // raw (untyped) buffer: 32-bit data format
-constexpr int kStreamAux = 2 | 16;        // nt | sc1
 
 template <typename T>
-__device__ __forceinline__ void st_lane(T* p, T x) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const T* p) {
     static_assert(kBlock == 64, "a row is one wave: blocks are single waves");
     const uintptr_t row = reinterpret_cast<uintptr_t>(p - threadIdx.x);
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)row);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(row >> 32));
     void* base = reinterpret_cast<void*>(((uintptr_t)hi << 32) | lo);
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(base, (short)0, kBlock * (int)sizeof(T), kBufferWord3);
+    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, kBlock * (int)sizeof(T), kBufferWord3);
+}
+
+// Row stores: nontemporal with sc1 set. At the Llama-7B shape this is 2-3%
+// faster for the fused step and up to 4% for AdamW than the global
+// nontemporal store (nt alone, which a buffer store with nt alone times the
+// same as); sc1 without nt is slower than both.
+constexpr int kStreamAux = 2 | 16;  // nt | sc1
+
+template <typename T>
+__device__ __forceinline__ void st_lane(T* p, T x) {
+    const __amdgpu_buffer_rsrc_t r = row_rsrc(p);
     const int off = (int)(threadIdx.x * sizeof(T));
     if constexpr (sizeof(T) == 16)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, kStreamAux);
@@ -218,6 +226,15 @@ __device__ __forceinline__ void st_lane(T* p, T x) {
         static_assert(sizeof(T) == 8, "rows of 8- or 16-byte units");
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), r, off, 0, kStreamAux);
     }
+}
+
+// Row loads of 16-byte units, nontemporal: the N-way reduce's contribution
+// reads (0.2-1.2% faster at N=64 than global loads; sc0 or sc1 added change
+// nothing, sc0|sc1 without nt is 5% slower). The fused step and the
+// accumulation micro-step measured the same or slower with them (4% slower
+// for the accumulation at N=8) and keep global loads.
+__device__ __forceinline__ u32x4 ld_lane(const u32x4* p) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(row_rsrc(p), (int)(threadIdx.x * 16), 0, 2));
 }
 
 // Cache policy per access class: read-once inputs and the read-modify-write
@@ -272,7 +289,7 @@ __device__ __forceinline__ void acc_add(float* a, const V& x) {
 }
 
 // Adds ranks [q0, q0 + G) into a[k][*] for the U units u[k] with ok[k].
-template <typename V, int U, int G>
+template <typename V, int U, int G, bool ROW>
 __device__ __forceinline__ void sum_group(const void* const* p, int q0, const int64_t* u, const bool* ok,
                                           float (*a)[Lanes<V>::E]) {
     V x[G][U];
@@ -280,7 +297,13 @@ __device__ __forceinline__ void sum_group(const void* const* p, int q0, const in
     for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int k = 0; k < U; ++k)
-            if (ok[k]) x[g][k] = ld_in(reinterpret_cast<const V*>(p[q0 + g]) + u[k]);
+            if (ok[k]) {
+                const V* src = reinterpret_cast<const V*>(p[q0 + g]) + u[k];
+                if constexpr (ROW)
+                    x[g][k] = ld_lane(src);
+                else
+                    x[g][k] = ld_in(src);
+            }
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -289,8 +312,9 @@ __device__ __forceinline__ void sum_group(const void* const* p, int q0, const in
 }
 
 // Full rank sum: compile-time N in groups of min(N, kGroup); runtime N in
-// groups of 4 plus a remainder loop.
-template <typename V, int U, int N>
+// groups of 4 plus a remainder loop. ROW: the units are rows (u[k] is the
+// row's first unit plus the lane), loaded with ld_lane.
+template <typename V, int U, int N, bool ROW = false>
 __device__ __forceinline__ void rank_sum(const void* const* p, int n_rt, const int64_t* u, const bool* ok,
                                          float (*a)[Lanes<V>::E]) {
 #pragma unroll
@@ -301,11 +325,11 @@ __device__ __forceinline__ void rank_sum(const void* const* p, int n_rt, const i
         constexpr int G = N < kGroup ? N : kGroup;
         static_assert(N % G == 0, "world sizes with compiled loops are powers of two");
 #pragma unroll
-        for (int q0 = 0; q0 < N; q0 += G) sum_group<V, U, G>(p, q0, u, ok, a);
+        for (int q0 = 0; q0 < N; q0 += G) sum_group<V, U, G, ROW>(p, q0, u, ok, a);
     } else {
         int q0 = 0;
-        for (; q0 + 4 <= n_rt; q0 += 4) sum_group<V, U, 4>(p, q0, u, ok, a);
-        for (; q0 < n_rt; ++q0) sum_group<V, U, 1>(p, q0, u, ok, a);
+        for (; q0 + 4 <= n_rt; q0 += 4) sum_group<V, U, 4, ROW>(p, q0, u, ok, a);
+        for (; q0 < n_rt; ++q0) sum_group<V, U, 1, ROW>(p, q0, u, ok, a);
     }
 }
 
@@ -347,7 +371,7 @@ __device__ __forceinline__ void reduce8_tile(const void* const* cp, int n_rt, fl
         ok[k] = u[k] < limit;
     }
     float a[U][8];
-    rank_sum<u32x4, U, N>(cp, n_rt, u, ok, a);
+    rank_sum<u32x4, U, N, true>(cp, n_rt, u, ok, a);
 #pragma unroll
     for (int k = 0; k < U; ++k) {
         if (!ok[k]) continue;
