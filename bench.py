@@ -34,7 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E peak
-KERNEL_SRC = os.path.join(ROOT, "fsdp_sharded_mixed_flatten_amd", "csrc", "zs_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "fsdp_sharded_mixed_flatten_amd", "csrc", f) for f in ("zs_kernels.hip", "zs_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 METRIC = "shard step: params updated/s + achieved HBM GB/s (% of MI355X peak)"
@@ -61,9 +61,40 @@ def unfused_bpp(N):
     return reduce_bpp(N) + adamw_bpp() + 4  # + gather (2 read + 2 write)
 
 
+def code_text(src):
+    """C++ source without its comments, whitespace runs collapsed: what the
+    compiler sees of it (string and character literals kept as written)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_hash():
-    with open(KERNEL_SRC, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    """Hash of the kernels' code (the kernel source and its internal header,
+    comments and layout excluded): counter-measured traffic stays valid
+    across comment edits and is dropped by any change to the code."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path) as fh:
+            h.update(code_text(fh.read()).encode())
+    return h.hexdigest()[:16]
 
 
 def parse():
@@ -181,7 +212,8 @@ def graph_time(torch, fn, steps_per_graph, replays):
 
 def read_traffic(kernel_name, workload):
     """Counter-measured HBM bytes per launch (profiles/traffic.json), or None
-    once the kernel source has changed since the counters were taken."""
+    once the kernels' code (kernel_hash) has changed since the counters were
+    taken."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     try:
@@ -190,7 +222,7 @@ def read_traffic(kernel_name, workload):
     except ValueError:
         return None
     rec = data.get(f"{workload}:{kernel_name}")
-    if not rec or rec.get("kernel_src_sha256_16") != kernel_hash():
+    if not rec or rec.get("kernel_code_sha256_16") != kernel_hash():
         return None
     return rec.get("bytes_per_launch")
 

@@ -22,7 +22,9 @@
 //   * Each lane issues the loads of a group of ranks, and of the state arrays,
 //     before consuming any, so many independent loads are in flight.
 //   * Every access is nontemporal (each access class was swept; the cached
-//     variants were slower).
+//     variants were slower). Rows a whole wave writes go out as buffer stores
+//     that also set sc1, which only a buffer access can express from HIP
+//     (2-5% faster for the kernels that mix reads and writes).
 //   * Writes that interleave with heavy read traffic cost several times their
 //     share of bytes, so at large N the fused entry point runs as a nearly
 //     read-only reduce followed by AdamW writing the gathered slice directly.
