@@ -332,10 +332,11 @@ def unbind(zs, st):
 
 
 def fused_step_fn(zs, plan, hp0, st, N):
-    """The fused entry point as a caller runs it: at N >= 64 with the grad
-    shard given (part of the persistent 16 B/param state), which selects the
-    reduce + AdamW/gather two-pass form; one kernel otherwise."""
-    grad = st["grad"] if N >= 64 else None
+    """The fused entry point as a caller runs it: from
+    zs.FUSED_TWO_PASS_MIN_CONTRIBS contributions on with the grad shard given
+    (part of the persistent 16 B/param state), which selects the reduce +
+    AdamW/gather two-pass form; one kernel otherwise."""
+    grad = st["grad"] if N >= zs.FUSED_TWO_PASS_MIN_CONTRIBS else None
 
     def step(t, timer):
         e = timer.start() if timer else None
@@ -347,7 +348,7 @@ def fused_step_fn(zs, plan, hp0, st, N):
 
 
 def split_kernels_fn(zs, plan, hp0, st):
-    """The two kernels of the N >= 64 fused step issued as their own calls,
+    """The two kernels of the two-pass fused step issued as their own calls,
     so each gets its own event pair: the reduce into the grad shard (the
     kernel k_reduce), then AdamW writing the owned slice of the gathered
     buffer (k_adamw). Same kernels, same bytes as the fused entry point."""
@@ -372,7 +373,7 @@ def flat_workload(zs, synth, torch, wl, args, primary):
     plan = zs.zs_shard_plan(wl.numels, wl.world, wl.rank, wl.align, zs.ZS_LAYOUT_FLAT)
     S, T = plan.shard_numel, plan.padded_numel
     hp0 = zs.AdamWHParams(wl.lr, wl.beta1, wl.beta2, wl.eps, wl.weight_decay, 1)
-    two_pass = N >= 64
+    two_pass = N >= zs.FUSED_TWO_PASS_MIN_CONTRIBS
     bpp = fused_bpp(N, write_grad=two_pass)
     log(f"[bench] workload={wl.name} N={N} rank={wl.rank} S={S:,} T={T:,}")
     free, _ = torch.cuda.mem_get_info()
@@ -426,7 +427,7 @@ def flat_workload(zs, synth, torch, wl, args, primary):
     else:
         out["roofline"] = roofline("k_fused", wl.name, S, bpp, med["device_ms_per_step"])
     # the whole step against the minimum the method moves: 2N+26 B per owned
-    # element (plus the grad shard written at N >= 64, which the ledger keeps)
+    # element (plus the grad shard written by the two-pass form, which the ledger keeps)
     step_ms = med["device_ms_per_step"]
     out["step_roofline"] = {"min_bytes_per_param": fused_bpp(N), "bytes_per_param_counted": bpp,
                             "frac_at_min_bytes": S * fused_bpp(N) / (step_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
@@ -447,7 +448,7 @@ def flat_workload(zs, synth, torch, wl, args, primary):
 def flat_extra_legs(zs, synth, torch, wl, plan, hp0, st, args, head):
     """Unfused, quantized, accumulation + clipping and offload legs on one buffer set."""
     N, S, T = wl.world, plan.shard_numel, plan.padded_numel
-    two_pass = N >= 64
+    two_pass = N >= zs.FUSED_TWO_PASS_MIN_CONTRIBS
     grad_out = st["grad"] if two_pass else None
     paths, graphable = {}, {"fused": fused_step_fn(zs, plan, hp0, st, N)}
     B = wl.bucket_elems or S

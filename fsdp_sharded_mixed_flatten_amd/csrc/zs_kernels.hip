@@ -59,9 +59,12 @@ constexpr int kAdamwU = 1;
 constexpr int kFusedU = 1;
 // Occupancy throttle: bytes of untouched dynamic LDS per block (160 KiB per
 // CU), which caps the resident 64-thread blocks per CU.
-//   fused step, N > 4: 16 KiB (ten waves per CU; 12 KiB 2% slower, 20 KiB
-//   the same);
+//   fused step, N > 4: 16 KiB (ten waves per CU; at N=8 12 KiB 2% slower,
+//   20 KiB the same, 24 KiB 7% slower), except the compiled 16 and 32 rank
+//   loops: 24 KiB (1.4-3% faster than 16 or 20 KiB); the runtime rank loop,
+//   which holds two register sets of loads, loses 2-14% at 24 KiB;
 constexpr unsigned kFusedLds = 16u << 10;
+constexpr unsigned kFusedMidLds = 24u << 10;
 //   fused step at 4 or fewer ranks, whose lighter reads leave room for more
 //   resident waves: eleven per CU (14 KiB) measured 1.4% faster than ten or
 //   thirteen at the Qwen2.5-3B shape;
@@ -74,11 +77,15 @@ constexpr unsigned kFusedQuantLds = 12u << 10;
 //   lose 11% at N=64), and 8 KiB at 4 or fewer ranks (10% faster than 16);
 constexpr unsigned kAccumLds = 16u << 10;
 constexpr unsigned kAccumNarrowLds = 8u << 10;
-//   reduce: 8 KiB (4-16 KiB within noise); from kWideN ranks on 32 KiB, about
-//   five waves per CU (3-8% faster at N=64 than 8 KiB; 48 KiB and up lose);
-constexpr unsigned kReduceLds = 8u << 10;
+//   reduce: 16 KiB below kMidN ranks (2-7% faster than 8 KiB at N = 8, 12,
+//   16 and 24), 24 KiB from kMidN (2-7% faster than 16 or 32 KiB at N = 32,
+//   40 and 48) and 32 KiB from kWideN ranks on, about five waves per CU (at
+//   N=64 3-8% faster than 8 KiB, 0.2-1.6% than 24 KiB; 48 KiB and up lose);
+constexpr unsigned kReduceLds = 16u << 10;
+constexpr unsigned kReduceMidLds = 24u << 10;
 constexpr unsigned kReduceWideLds = 32u << 10;
-constexpr int kWideN = 32;
+constexpr int kMidN = 32;
+constexpr int kWideN = 64;
 //   AdamW (from the grad shard or the accumulator): 12 KiB (1-3% faster than
 //   8 or 16 KiB at all three shapes with the nt sc1 stores);
 constexpr unsigned kAdamwLds = 12u << 10;
@@ -99,9 +106,13 @@ constexpr unsigned kMultiGatherLds = 8u << 10;
 constexpr unsigned kDequantLds = 4u << 10;
 constexpr int kDequantU = 4;
 // World size from which the fused entry point runs the reduce into the grad
-// shard, then AdamW + gather, when the caller provides the grad buffer: at
-// N=64 every one-pass layout measured 7-25% slower than the two passes.
-constexpr int kSplitMinN = 64;
+// shard, then AdamW + gather, when the caller provides the grad buffer. At
+// the Llama-7B shape the two passes are 3-6% faster at N=56, 11% at N=64
+// and 14% at N=128 (at the Llama-70B shape every one-pass layout measured
+// 7-25% slower at N=64); from 33 to 48 ranks the two forms land within 3% of
+// each other either way round, depending on buffer placement, and below 32
+// the one pass wins (5-7% at N=16 and 24).
+constexpr int kSplitMinN = ZS_FUSED_TWO_PASS_MIN_CONTRIBS;
 
 // ------------------------------------------------------------------ bf16
 
@@ -290,11 +301,10 @@ __device__ __forceinline__ void acc_add(float* a, const V& x) {
     }
 }
 
-// Adds ranks [q0, q0 + G) into a[k][*] for the U units u[k] with ok[k].
+// Loads ranks [q0, q0 + G) of the U units u[k] with ok[k] into x.
 template <typename V, int U, int G, bool ROW>
-__device__ __forceinline__ void sum_group(const void* const* p, int q0, const int64_t* u, const bool* ok,
-                                          float (*a)[Lanes<V>::E]) {
-    V x[G][U];
+__device__ __forceinline__ void load_group(const void* const* p, int q0, const int64_t* u, const bool* ok,
+                                           V (*x)[U]) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -306,6 +316,11 @@ __device__ __forceinline__ void sum_group(const void* const* p, int q0, const in
                 else
                     x[g][k] = ld_in(src);
             }
+}
+
+// Adds a loaded group into a[k][*], rank by rank.
+template <typename V, int U, int G>
+__device__ __forceinline__ void add_group(const V (*x)[U], const bool* ok, float (*a)[Lanes<V>::E]) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -313,9 +328,23 @@ __device__ __forceinline__ void sum_group(const void* const* p, int q0, const in
             if (ok[k]) acc_add<V>(a[k], x[g][k]);
 }
 
-// Full rank sum: compile-time N in groups of min(N, kGroup); runtime N in
-// groups of 4 plus a remainder loop. ROW: the units are rows (u[k] is the
-// row's first unit plus the lane), loaded with ld_lane.
+// Adds ranks [q0, q0 + G) into a[k][*] for the U units u[k] with ok[k].
+template <typename V, int U, int G, bool ROW>
+__device__ __forceinline__ void sum_group(const void* const* p, int q0, const int64_t* u, const bool* ok,
+                                          float (*a)[Lanes<V>::E]) {
+    V x[G][U];
+    load_group<V, U, G, ROW>(p, q0, u, ok, x);
+    add_group<V, U, G>(x, ok, a);
+}
+
+// Full rank sum. Compile-time N: groups of min(N, kGroup), fully unrolled.
+// Runtime N: groups of kGroup with the next group's loads issued before the
+// current group is added (two register sets in turn, so a lane keeps up to
+// 2 * kGroup loads in flight; a plain loop waits for each group before
+// issuing the next: 5.0 TB/s against 6.6 for the N=48 reduce), then 4, 2
+// and 1 ranks. Either way the adds run in rank order 0..N-1. ROW: the units
+// are rows (u[k] is the row's first unit plus the lane), loaded with
+// ld_lane.
 template <typename V, int U, int N, bool ROW = false>
 __device__ __forceinline__ void rank_sum(const void* const* p, int n_rt, const int64_t* u, const bool* ok,
                                          float (*a)[Lanes<V>::E]) {
@@ -329,9 +358,38 @@ __device__ __forceinline__ void rank_sum(const void* const* p, int n_rt, const i
 #pragma unroll
         for (int q0 = 0; q0 < N; q0 += G) sum_group<V, U, G, ROW>(p, q0, u, ok, a);
     } else {
+        constexpr int G = kGroup;
         int q0 = 0;
-        for (; q0 + 4 <= n_rt; q0 += 4) sum_group<V, U, 4, ROW>(p, q0, u, ok, a);
-        for (; q0 < n_rt; ++q0) sum_group<V, U, 1, ROW>(p, q0, u, ok, a);
+        if (n_rt >= G) {
+            V x[G][U], y[G][U];
+            load_group<V, U, G, ROW>(p, 0, u, ok, x);
+            q0 = G;
+            bool y_pending = false;  // which set holds the loaded, not yet added group
+            while (q0 + G <= n_rt) {
+                load_group<V, U, G, ROW>(p, q0, u, ok, y);
+                add_group<V, U, G>(x, ok, a);
+                q0 += G;
+                y_pending = true;
+                if (q0 + G > n_rt) break;
+                load_group<V, U, G, ROW>(p, q0, u, ok, x);
+                add_group<V, U, G>(y, ok, a);
+                q0 += G;
+                y_pending = false;
+            }
+            if (y_pending)
+                add_group<V, U, G>(y, ok, a);
+            else
+                add_group<V, U, G>(x, ok, a);
+        }
+        if (q0 + 4 <= n_rt) {
+            sum_group<V, U, 4, ROW>(p, q0, u, ok, a);
+            q0 += 4;
+        }
+        if (q0 + 2 <= n_rt) {
+            sum_group<V, U, 2, ROW>(p, q0, u, ok, a);
+            q0 += 2;
+        }
+        if (q0 < n_rt) sum_group<V, U, 1, ROW>(p, q0, u, ok, a);
     }
 }
 
@@ -1154,8 +1212,8 @@ int launch_reduce_t(const void* const* contribs, int n, void* grad, int64_t len,
     for (int q = 0; q < n; ++q) cp.p[q] = contribs[q];
     const int64_t n8 = len / 8;
     hipLaunchKernelGGL((k_reduce<N, CAP, kReduceU>), dim3(grid_for(n8, kReduceU)), dim3(kBlock),
-                       n >= kWideN ? kReduceWideLds : kReduceLds, s, cp, n, (float)n, reinterpret_cast<u32x4*>(grad),
-                       n8);
+                       n >= kWideN ? kReduceWideLds : n >= kMidN ? kReduceMidLds : kReduceLds, s, cp, n, (float)n,
+                       reinterpret_cast<u32x4*>(grad), n8);
     return (int)hipGetLastError();
 }
 
@@ -1166,8 +1224,11 @@ int launch_fused_q(const AdamCoef& c, const AdamCoef* cdev, const void* const* c
     Ptrs<CAP> cp{};
     for (int q = 0; q < n; ++q) cp.p[q] = contribs[q];
     const int64_t n4 = len / 4;
-    hipLaunchKernelGGL((k_fused<N, CAP, kFusedU, QB>), dim3(grid_for(n4, kFusedU)), dim3(kBlock),
-                       QB == 0 ? (n <= 4 ? kFusedNarrowLds : kFusedLds) : kFusedQuantLds, s, c, cdev,
+    const unsigned lds = QB != 0 ? kFusedQuantLds
+                         : n <= 4 ? kFusedNarrowLds
+                         : (N == 16 || N == 32) ? kFusedMidLds
+                                                : kFusedLds;
+    hipLaunchKernelGGL((k_fused<N, CAP, kFusedU, QB>), dim3(grid_for(n4, kFusedU)), dim3(kBlock), lds, s, c, cdev,
                        cp, n, (float)n, reinterpret_cast<f32x4*>(master), reinterpret_cast<f32x4*>(m),
                        reinterpret_cast<f32x4*>(v), reinterpret_cast<u32x2*>(grad),
                        reinterpret_cast<u32x2*>(param), reinterpret_cast<u32x2*>(full), n4, qo);

@@ -214,10 +214,12 @@ zs_status zs_gather_params(const zs_plan* plan, const void* param_bf16, void* fu
 /* reduce + AdamW + gather over the shard, bit-identical to zs_reduce_shard
  * over the whole shard, then zs_adamw_shard_step, then zs_gather_params.
  * grad_bf16, param_bf16 and full_bf16 are each optional (NULL: not
- * written); full_bf16 requires a FLAT plan. One kernel pass; at large world
- * sizes (N >= 64) with grad_bf16 given, two passes -- the reduce into
- * grad_bf16, then AdamW writing param/full -- which keep the read-heavy and
- * write-heavy traffic apart and run faster on MI355X. */
+ * written); full_bf16 requires a FLAT plan. One kernel pass; with
+ * n_contribs >= ZS_FUSED_TWO_PASS_MIN_CONTRIBS and grad_bf16 given, two
+ * passes -- the reduce into grad_bf16, then AdamW writing param/full --
+ * which keep the read-heavy and write-heavy traffic apart and run faster on
+ * MI355X at those sizes. Either form leaves the same bytes. */
+#define ZS_FUSED_TWO_PASS_MIN_CONTRIBS 56
 zs_status zs_fused_shard_step(const zs_plan* plan, const zs_adamw_hparams* hp,
                               const void* const* contribs, int32_t n_contribs, float* master,
                               float* m, float* v, void* grad_bf16, void* param_bf16,

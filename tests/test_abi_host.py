@@ -31,6 +31,15 @@ def test_exports_every_declared_symbol(zs):
     assert declared == set(zs.EXPORTED)
 
 
+def test_binding_constants_match_the_header(zs):
+    text = open(HEADER).read()
+    macros = {m: int(v.rstrip("L"), 0) for m, v in re.findall(r"#define\s+(ZS_[A-Z0-9_]+)\s+([0-9xXa-fA-FL]+)", text)}
+    assert macros["ZS_MAX_CONTRIBS"] == zs.ZS_MAX_CONTRIBS
+    assert macros["ZS_MAX_GROUPS"] == zs.ZS_MAX_GROUPS
+    assert macros["ZS_GRAD_STATS_NOALLOC_MAX_ELEMS"] == zs.GRAD_STATS_NOALLOC_MAX_ELEMS
+    assert macros["ZS_FUSED_TWO_PASS_MIN_CONTRIBS"] == zs.FUSED_TWO_PASS_MIN_CONTRIBS
+
+
 def _compare_plan(zs, numels, world, rank, align, layout):
     p = zs.zs_shard_plan(numels, world, rank, align, layout)
     o = plan_flat(numels, world, rank, align) if layout == zs.ZS_LAYOUT_FLAT else plan_per_tensor(numels, world, rank)

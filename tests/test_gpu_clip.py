@@ -37,10 +37,13 @@ def _contribs(T, N, micro, seed, valid, nan_at=None):
     return out
 
 
-@pytest.mark.parametrize("G,max_norm", [(1, 1e-4), (3, 1e-4), (3, 100.0), (4, 3e-5)])
-def test_accumulate_clip_step_all_ranks(zs, G, max_norm):
+@pytest.mark.parametrize("G,max_norm,N", [(1, 1e-4, 4), (3, 1e-4, 4), (3, 100.0, 4), (4, 3e-5, 4),
+                                          (3, 1e-4, 13), (2, 3e-5, 24)])
+def test_accumulate_clip_step_all_ranks(zs, G, max_norm, N):
+    """N = 13 and 24 take the runtime rank loop (a group of 8 plus 4 + 1, and
+    three groups of 8 in the two register sets in turn)."""
     import torch
-    numels, N = [1_000_003], 4
+    numels = [1_000_003]
     plans = [zs.zs_shard_plan(numels, N, r, 1) for r in range(N)]
     T, S = plans[0].padded_numel, plans[0].shard_numel
     seed = 4242 + G

@@ -189,9 +189,13 @@ def test_random_flat_plans(zs, seed):
     run.check()
 
 
-@pytest.mark.parametrize("N", [1, 2, 4, 8, 16, 32, 64, 3, 7, 256])
+@pytest.mark.parametrize("N", [1, 2, 4, 8, 16, 32, 64, 3, 7, 9, 12, 15, 24, 31, 40, 48, 63, 65, 100, 256])
 def test_world_sizes(zs, N):
-    """Every compiled rank-loop variant (N = 1..64) and the runtime loop."""
+    """Every compiled rank-loop variant (N = 1..64) and the runtime loop:
+    remainders of 0 to 7 ranks after its groups of 8, no full group (3, 7),
+    one (9..15), odd and even numbers of groups in the two register sets
+    taken in turn (24, 40, 48, 256), and both sides of the two-pass
+    threshold."""
     rank = N - 1 if N <= 100 else N // 2  # a rank that owns real elements and some padding
     for fused in (False, True):
         run = FlatRun(zs, [50_001], N, rank, 1, 1, 7 + N, _hp(zs), fused=fused)
@@ -517,8 +521,9 @@ def test_multi_tensor_unbound_workspace_is_inert(zs):
         zs.zs_multi_unbind(ws)
 
 
-def test_multi_tensor_runtime_world(zs):
-    run = MultiRun(zs, _small_model(H=128, I=344, V=300, L=1), 5, 4, 1, 78, _hp(zs))
+@pytest.mark.parametrize("N", [5, 24])
+def test_multi_tensor_runtime_world(zs, N):
+    run = MultiRun(zs, _small_model(H=128, I=344, V=300, L=1), N, N - 1, 1, 78, _hp(zs))
     run.step(1, True)
     run.check()
 
