@@ -839,6 +839,22 @@ zs_status lookup_binding(const zs_plan* plan, const void* ws, int32_t need, Bind
     return ZS_OK;
 }
 
+// The fused multi-tensor step: one pass, or, from
+// ZS_FUSED_TWO_PASS_MIN_CONTRIBS contributions on with the grad pieces
+// bound, the reduce into the grad pieces and then AdamW writing the
+// parameter and gathered pieces (the same bytes; faster at those sizes, as
+// for the flat step).
+int launch_fused_multi(const zs_plan* plan, const Binding& b, const zs::CoefTable* ct, const void* workspace,
+                       void* stream, const zs::AdamCoef* cdev) {
+    const zs::MultiOffsets off = multi_offsets(plan, b.n_contribs);
+    const int n_chunks = (int)plan->chunk_piece.size();
+    if ((b.flags & zs::kHasGrad) && b.n_contribs >= ZS_FUSED_TWO_PASS_MIN_CONTRIBS) {
+        if (int e = zs::launch_multi(zs::kOpReduce, nullptr, workspace, off, n_chunks, b.n_contribs, stream)) return e;
+        return zs::launch_multi(zs::kOpAdamwGather, ct, workspace, off, n_chunks, b.n_contribs, stream, cdev);
+    }
+    return zs::launch_multi(zs::kOpFused, ct, workspace, off, n_chunks, b.n_contribs, stream, cdev);
+}
+
 }  // namespace
 
 int64_t zs_plan_workspace_bytes(const zs_plan* plan) {
@@ -991,8 +1007,7 @@ zs_status zs_fused_shard_step_multi(const zs_plan* plan, const zs_adamw_hparams*
     zs::CoefTable ct;
     for (auto& e : ct.c) e = zs::make_coef(*hp);
     trace("zs_fused_shard_step_multi", plan, b.n_contribs, 0, plan->S, stream);
-    return hip_status(zs::launch_multi(zs::kOpFused, &ct, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunk_piece.size(), b.n_contribs, stream),
-                      "multi fused launch");
+    return hip_status(launch_fused_multi(plan, b, &ct, workspace, stream, nullptr), "multi fused launch");
 }
 
 namespace {
@@ -1038,9 +1053,7 @@ zs_status zs_fused_shard_step_multi_dc(const zs_plan* plan, const zs_adamw_coefs
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasContribs | zs::kHasState, &b)) return st;
     const zs::CoefTable unused{};
     trace("zs_fused_shard_step_multi", plan, b.n_contribs, 0, plan->S, stream);
-    return hip_status(zs::launch_multi(zs::kOpFused, &unused, workspace, multi_offsets(plan, b.n_contribs),
-                                       (int)plan->chunk_piece.size(), b.n_contribs, stream, dev_coef(coefs)),
-                      "multi fused launch");
+    return hip_status(launch_fused_multi(plan, b, &unused, workspace, stream, dev_coef(coefs)), "multi fused launch");
 }
 
 zs_status zs_fused_shard_step_multi_groups(const zs_plan* plan, const zs_adamw_hparams* hps, int32_t n_groups,
@@ -1051,8 +1064,7 @@ zs_status zs_fused_shard_step_multi_groups(const zs_plan* plan, const zs_adamw_h
     Binding b;
     if (zs_status st = lookup_binding(plan, workspace, zs::kHasContribs | zs::kHasState, &b)) return st;
     trace("zs_fused_shard_step_multi", plan, b.n_contribs, 0, plan->S, stream);
-    return hip_status(zs::launch_multi(zs::kOpFused, &ct, workspace, multi_offsets(plan, b.n_contribs), (int)plan->chunk_piece.size(), b.n_contribs, stream),
-                      "multi fused launch");
+    return hip_status(launch_fused_multi(plan, b, &ct, workspace, stream, nullptr), "multi fused launch");
 }
 
 }  // extern "C"

@@ -146,7 +146,9 @@ int launch_adamw_accum(const AdamCoef& c, const float* acc, float divisor, const
                        float* master, float* m, float* v, void* param, void* full_at_own, int64_t len, void* stream,
                        const AdamCoef* cdev = nullptr);
 
-enum MultiOp : int32_t { kOpReduce = 0, kOpAdamw = 1, kOpGather = 2, kOpFused = 3 };
+// kOpAdamwGather: AdamW writing the parameter and the gathered slice where
+// bound (the second pass of the two-pass fused step).
+enum MultiOp : int32_t { kOpReduce = 0, kOpAdamw = 1, kOpGather = 2, kOpFused = 3, kOpAdamwGather = 4 };
 // Byte offsets of the tables in a bound workspace (the header holds the same
 // values; the kernels take them as arguments to save a dependent load).
 struct MultiOffsets {

@@ -92,13 +92,15 @@ constexpr unsigned kAdamwLds = 12u << 10;
 //   gather copies and the bf16 codes of a shard: 4 KiB (3.5% faster than 8;
 //   0 and 2 KiB the same as 4, 16 KiB 50% slower);
 constexpr unsigned kGatherLds = 4u << 10;
-//   multi-tensor kernels: 12 KiB for reduce and AdamW (10 and 14 KiB slower),
+//   multi-tensor kernels: 12 KiB for reduce and AdamW (10 and 14 KiB slower;
+//   for the reduce 8, 16, 24 and 32 KiB at N = 8, 24 and 64 too),
 //   14 KiB for the fused step (12 KiB 2% slower, 16 the same, 18 and 20 KiB
 //   slower at the Llama-7B wrap-stress shape) and 8 KiB for the gather (12%
 //   faster than 12 KiB, 2% faster than 4 KiB or none);
 constexpr unsigned kMultiLds = 12u << 10;
 constexpr unsigned kMultiFusedLds = 14u << 10;
 constexpr unsigned kMultiGatherLds = 8u << 10;
+constexpr unsigned kMultiReduceLds = 12u << 10;
 //   dequantizing gather, a nearly pure write stream: 4 KiB (2% faster than
 //   none, 2 or 3 KiB at the Llama-7B and Qwen2.5-3B shapes, 5 KiB 0.5%
 //   slower; 6 KiB and up 13-20% slower, larger throttles up to 2x). Its
@@ -854,7 +856,8 @@ template <int OP, int N>
 __global__ __launch_bounds__(kBlock) void k_multi(CoefTable ct, const AdamCoef* __restrict__ cdev,
                                                   const MultiHeader* __restrict__ hdr, MultiOffsets off, int n_rt,
                                                   float nf) {
-    static_assert(OP == kOpAdamw || OP == kOpFused, "reduce and gather have kernels of their own");
+    static_assert(OP == kOpAdamw || OP == kOpAdamwGather || OP == kOpFused,
+                  "reduce and gather have kernels of their own");
     if (hdr->magic != kMultiMagic) return;  // not a bound table (e.g. reused memory): touch nothing
     const char* ws = reinterpret_cast<const char*>(hdr);
     const int32_t piece = reinterpret_cast<const int32_t*>(ws + off.chunks)[blockIdx.x];
@@ -867,10 +870,11 @@ __global__ __launch_bounds__(kBlock) void k_multi(CoefTable ct, const AdamCoef* 
     const int64_t u0 = start >> 2;
     const int64_t base = u0 + threadIdx.x;
     const int64_t limit = u0 + (len >> 2);
-    if constexpr (OP == kOpAdamw) {
+    if constexpr (OP == kOpAdamw || OP == kOpAdamwGather) {
+        u32x2* full = OP == kOpAdamwGather && (flags & kHasFull) ? reinterpret_cast<u32x2*>(pc.full_own) : nullptr;
         adamw_tile<kMultiU>(c, reinterpret_cast<const u32x2*>(pc.grad), reinterpret_cast<f32x4*>(pc.master),
                             reinterpret_cast<f32x4*>(pc.m), reinterpret_cast<f32x4*>(pc.v),
-                            (flags & kHasParam) ? reinterpret_cast<u32x2*>(pc.param) : nullptr, nullptr, base, limit);
+                            (flags & kHasParam) ? reinterpret_cast<u32x2*>(pc.param) : nullptr, full, base, limit);
     } else {
         const void* const* cps =
             reinterpret_cast<const void* const*>(ws + off.contribs) + (int64_t)piece * (N > 0 ? N : n_rt);
@@ -1259,7 +1263,7 @@ template <int N>
 int launch_multi_reduce_t(const void* ws, const MultiOffsets& off, int n_chunks, int n, hipStream_t s) {
     hipLaunchKernelGGL((k_multi_reduce<N>),
                        dim3((unsigned)((n_chunks + kReduceChunksPerBlock - 1) / kReduceChunksPerBlock)), dim3(kBlock),
-                       kMultiLds, s, reinterpret_cast<const MultiHeader*>(ws), off, n_chunks, n, (float)n);
+                       kMultiReduceLds, s, reinterpret_cast<const MultiHeader*>(ws), off, n_chunks, n, (float)n);
     return (int)hipGetLastError();
 }
 
@@ -1270,8 +1274,10 @@ int launch_multi_reduce(const void* ws, const MultiOffsets& off, int n_chunks, i
         case 4: return launch_multi_reduce_t<4>(ws, off, n_chunks, n, s);
         case 8: return launch_multi_reduce_t<8>(ws, off, n_chunks, n, s);
         case 16: return launch_multi_reduce_t<16>(ws, off, n_chunks, n, s);
-        case 32: return launch_multi_reduce_t<32>(ws, off, n_chunks, n, s);
-        case 64: return launch_multi_reduce_t<64>(ws, off, n_chunks, n, s);
+        // From 32 ranks on the runtime loop: a lane of this kernel loads its
+        // own rank pointers (its chunk's piece), and a fully unrolled 32- or
+        // 64-rank loop keeps them all live (187 and 458 VGPRs; 9% and 2.9x
+        // slower than the runtime loop at the Llama-7B wrap shape).
         default: return launch_multi_reduce_t<0>(ws, off, n_chunks, n, s);
     }
 }
@@ -1440,6 +1446,7 @@ int launch_multi(int op, const CoefTable* c, const void* workspace, const MultiO
     switch (op) {
         case kOpReduce: return launch_multi_reduce(workspace, off, n_chunks, n_contribs, s);
         case kOpAdamw: return launch_multi_t<kOpAdamw, 1>(cc, cdev, workspace, off, n_chunks, 1, s);
+        case kOpAdamwGather: return launch_multi_t<kOpAdamwGather, 1>(cc, cdev, workspace, off, n_chunks, 1, s);
         case kOpGather:
             hipLaunchKernelGGL(k_multi_gather, dim3((unsigned)((n_chunks + kGatherChunksPerBlock - 1) /
                                                                kGatherChunksPerBlock)),

@@ -331,7 +331,10 @@ zs_status zs_adamw_shard_step_multi(const zs_plan* plan, const zs_adamw_hparams*
                                     const void* workspace, void* stream);
 zs_status zs_gather_params_multi(const zs_plan* plan, const void* workspace, void* stream);
 /* reduce + AdamW + gather for every piece in one launch; writes grad, param
- * and full only where those fields were bound non-NULL. */
+ * and full only where those fields were bound non-NULL. With grad bound and
+ * at least ZS_FUSED_TWO_PASS_MIN_CONTRIBS contributions, two launches
+ * instead, as zs_fused_shard_step does: the reduce into the grad pieces,
+ * then AdamW writing param and full. Either form leaves the same bytes. */
 zs_status zs_fused_shard_step_multi(const zs_plan* plan, const zs_adamw_hparams* hp,
                                     const void* workspace, void* stream);
 /* As zs_adamw_shard_step_multi / zs_fused_shard_step_multi with one set of

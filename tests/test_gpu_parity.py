@@ -447,21 +447,25 @@ class MultiRun:
         assert nd == 0, f"{nd} elements not bit-identical"
 
 
+@pytest.mark.parametrize("world", [8, 64])
 @pytest.mark.parametrize("fused", [False, True])
-def test_multi_tensor_apply(zs, fused):
-    run = MultiRun(zs, _small_model(), 8, 3, 2, 77, _hp(zs))
+def test_multi_tensor_apply(zs, fused, world):
+    """At 64 ranks the fused call (grad bound) runs as two launches."""
+    run = MultiRun(zs, _small_model(), world, 3, 2, 77, _hp(zs))
     for t in (1, 2):
         run.step(t, fused)
         run.check()
 
 
+@pytest.mark.parametrize("world", [8, 64])
 @pytest.mark.parametrize("outs", range(8), ids=lambda o: f"grad{o & 1}-param{(o >> 1) & 1}-full{(o >> 2) & 1}")
-def test_multi_tensor_fused_optional_fields(zs, outs):
+def test_multi_tensor_fused_optional_fields(zs, outs, world):
     """The fused multi-tensor step bound with every subset of its optional
     fields (grad, param, gathered tensor): bound outputs equal the oracle's,
-    unbound ones are never written."""
+    unbound ones are never written (at 64 ranks with grad bound: the
+    two-launch form)."""
     import torch
-    run = MultiRun(zs, _small_model(), 8, 5, 2, 90 + outs, _hp(zs))
+    run = MultiRun(zs, _small_model(), world, 5, 2, 90 + outs, _hp(zs))
     keep = dict(grad=bool(outs & 1), param=bool(outs & 2), full=bool(outs & 4))
     for d in run.pieces:
         for k in keep:
