@@ -60,7 +60,7 @@ def test_random_flat(zs, seed):
     rnd = random.Random(seed)
     rng = np.random.default_rng(seed)
     numels = [rnd.choice([1, 9, 255, 4093, 30_011, 70_000]) for _ in range(rnd.randint(1, 6))]
-    world = rnd.choice([1, 2, 3, 4, 7, 8, 16, 64, 65])
+    world = rnd.choice([1, 2, 3, 4, 7, 8, 12, 16, 24, 48, 56, 64, 65])
     replicas = rnd.choice([1, 1, 2, 3]) if world * 3 <= 256 else 1
     rank = rnd.randrange(world)
     align = rnd.choice([1, 8, 128])
@@ -144,7 +144,7 @@ def test_random_per_tensor(zs, seed):
     rnd = random.Random(100 + seed)
     rng = np.random.default_rng(100 + seed)
     numels = [rnd.choice([3, 64, 512, 4096, 12_345, 65_536]) for _ in range(rnd.randint(1, 10))]
-    world = rnd.choice([1, 2, 4, 5, 8, 64])
+    world = rnd.choice([1, 2, 4, 5, 8, 24, 56, 64])
     replicas = rnd.choice([1, 2]) if world <= 64 else 1
     rank = rnd.randrange(world)
     persist = rnd.choice([0, 0, 600, 5000])
@@ -219,7 +219,7 @@ def test_random_accum_clip(zs, seed):
     rnd = random.Random(200 + seed)
     rng = np.random.default_rng(200 + seed)
     numels = [rnd.choice([9, 4093, 30_011, 70_000]) for _ in range(rnd.randint(1, 4))]
-    world = rnd.choice([1, 2, 4, 5, 8, 64])
+    world = rnd.choice([1, 2, 4, 5, 8, 13, 24, 48, 64])
     rank = rnd.randrange(world)
     plan = zs.zs_shard_plan(numels, world, rank, 1)
     oplan = oracle.plan_flat(numels, world, rank, 1)
@@ -291,7 +291,7 @@ def test_random_quant(zs, seed):
     rnd = random.Random(300 + seed)
     rng = np.random.default_rng(300 + seed)
     numels = [rnd.choice([9, 4093, 30_011, 70_000]) for _ in range(rnd.randint(1, 4))]
-    world = rnd.choice([1, 3, 4, 8, 64])
+    world = rnd.choice([1, 3, 4, 8, 24, 56, 64])
     rank = rnd.randrange(world)
     bits, block = rnd.choice([4, 8]), rnd.choice([8, 32, 128, 256])
     plan = zs.zs_shard_plan(numels, world, rank, 1)
