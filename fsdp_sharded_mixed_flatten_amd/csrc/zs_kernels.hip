@@ -73,10 +73,14 @@ constexpr unsigned kFusedNarrowLds = 14u << 10;
 //   than 14 or 16 KiB at the Qwen2.5-3B and Llama-7B shapes;
 constexpr unsigned kFusedQuantLds = 12u << 10;
 //   accumulation micro-steps (read 2N+4 bytes, write 4 per element): 16 KiB
-//   (8 to 40 KiB measured at the Llama-7B and -70B shapes; 32 KiB and more
-//   lose 11% at N=64), and 8 KiB at 4 or fewer ranks (10% faster than 16);
+//   (8 to 40 KiB measured at the Llama-7B and -70B shapes; 24 KiB the same
+//   at N=64 and slower at N = 8 and 24, 32 KiB and more lose 8-11% at N=64),
+//   and 12 KiB at 4 or fewer ranks (2-3% faster than 8 KiB with the nt sc1
+//   stores, 16 KiB 10% slower). Lanes of 8 elements (16-byte contribution
+//   loads, two 16-byte accumulator accesses 32 bytes apart) ran 1.3-2x
+//   slower: each wave access then covers half of every line it touches;
 constexpr unsigned kAccumLds = 16u << 10;
-constexpr unsigned kAccumNarrowLds = 8u << 10;
+constexpr unsigned kAccumNarrowLds = 12u << 10;
 //   reduce: 16 KiB below kMidN ranks (2-7% faster than 8 KiB at N = 8, 12,
 //   16 and 24), 24 KiB from kMidN (2-7% faster than 16 or 32 KiB at N = 32,
 //   40 and 48) and 32 KiB from kWideN ranks on, about five waves per CU (at
