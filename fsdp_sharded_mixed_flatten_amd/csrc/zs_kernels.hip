@@ -75,17 +75,21 @@ constexpr unsigned kFusedQuantLds = 12u << 10;
 //   accumulation micro-steps (read 2N+4 bytes, write 4 per element): 16 KiB
 //   (8 to 40 KiB measured at the Llama-7B and -70B shapes; 24 KiB the same
 //   at N=64 and slower at N = 8 and 24, 32 KiB and more lose 8-11% at N=64),
-//   and 12 KiB at 4 or fewer ranks (2-3% faster than 8 KiB with the nt sc1
-//   stores, 16 KiB 10% slower). Lanes of 8 elements (16-byte contribution
+//   12 KiB at 3 or 4 ranks (2-3% faster than 8 KiB with the nt sc1 stores,
+//   16 KiB 10% slower) and 8 KiB at 1 or 2 (5-13% faster than 12 KiB). Lanes of 8 elements (16-byte contribution
 //   loads, two 16-byte accumulator accesses 32 bytes apart) ran 1.3-2x
 //   slower: each wave access then covers half of every line it touches;
 constexpr unsigned kAccumLds = 16u << 10;
 constexpr unsigned kAccumNarrowLds = 12u << 10;
-//   reduce: 16 KiB below kMidN ranks (2-7% faster than 8 KiB at N = 8, 12,
-//   16 and 24), 24 KiB from kMidN (2-7% faster than 16 or 32 KiB at N = 32,
+constexpr unsigned kAccumTinyLds = 8u << 10;
+//   reduce: 4 KiB per rank up to 16 KiB below kMidN ranks (16 KiB 2-7%
+//   faster than 8 KiB at N = 8, 12, 16 and 24; at N=1 4 KiB against 79%
+//   slower at 16 KiB, at N=2 8 KiB against 33% slower: a light kernel needs
+//   more waves in flight), 24 KiB from kMidN (2-7% faster than 16 or 32 KiB at N = 32,
 //   40 and 48) and 32 KiB from kWideN ranks on, about five waves per CU (at
 //   N=64 3-8% faster than 8 KiB, 0.2-1.6% than 24 KiB; 48 KiB and up lose);
 constexpr unsigned kReduceLds = 16u << 10;
+constexpr unsigned kReduceLdsPerRank = 4u << 10;
 constexpr unsigned kReduceMidLds = 24u << 10;
 constexpr unsigned kReduceWideLds = 32u << 10;
 constexpr int kMidN = 32;
@@ -97,7 +101,9 @@ constexpr unsigned kAdamwLds = 12u << 10;
 //   0 and 2 KiB the same as 4, 16 KiB 50% slower);
 constexpr unsigned kGatherLds = 4u << 10;
 //   multi-tensor kernels: 12 KiB for reduce and AdamW (10 and 14 KiB slower;
-//   for the reduce 8, 16, 24 and 32 KiB at N = 8, 24 and 64 too),
+//   for the reduce 8, 16, 24 and 32 KiB at N = 8, 24 and 64 too; the reduce
+//   at 1 or 2 ranks takes 4 KiB, 44-52% faster, and at 3 or 4 ranks 8 KiB,
+//   15% faster),
 //   14 KiB for the fused step (12 KiB 2% slower, 16 the same, 18 and 20 KiB
 //   slower at the Llama-7B wrap-stress shape) and 8 KiB for the gather (12%
 //   faster than 12 KiB, 2% faster than 4 KiB or none);
@@ -105,6 +111,8 @@ constexpr unsigned kMultiLds = 12u << 10;
 constexpr unsigned kMultiFusedLds = 14u << 10;
 constexpr unsigned kMultiGatherLds = 8u << 10;
 constexpr unsigned kMultiReduceLds = 12u << 10;
+constexpr unsigned kMultiReduceNarrowLds = 8u << 10;
+constexpr unsigned kMultiReduceTinyLds = 4u << 10;
 //   dequantizing gather, a nearly pure write stream: 4 KiB (2% faster than
 //   none, 2 or 3 KiB at the Llama-7B and Qwen2.5-3B shapes, 5 KiB 0.5%
 //   slower; 6 KiB and up 13-20% slower, larger throttles up to 2x). Its
@@ -1214,14 +1222,19 @@ unsigned grid_for(int64_t units, int per_lane) {
     return (unsigned)blocks;
 }
 
+unsigned reduce_lds(int n) {
+    if (n >= kWideN) return kReduceWideLds;
+    if (n >= kMidN) return kReduceMidLds;
+    return (unsigned)n * kReduceLdsPerRank < kReduceLds ? (unsigned)n * kReduceLdsPerRank : kReduceLds;
+}
+
 template <int N, int CAP>
 int launch_reduce_t(const void* const* contribs, int n, void* grad, int64_t len, hipStream_t s) {
     Ptrs<CAP> cp{};
     for (int q = 0; q < n; ++q) cp.p[q] = contribs[q];
     const int64_t n8 = len / 8;
     hipLaunchKernelGGL((k_reduce<N, CAP, kReduceU>), dim3(grid_for(n8, kReduceU)), dim3(kBlock),
-                       n >= kWideN ? kReduceWideLds : n >= kMidN ? kReduceMidLds : kReduceLds, s, cp, n, (float)n,
-                       reinterpret_cast<u32x4*>(grad), n8);
+                       reduce_lds(n), s, cp, n, (float)n, reinterpret_cast<u32x4*>(grad), n8);
     return (int)hipGetLastError();
 }
 
@@ -1267,7 +1280,8 @@ template <int N>
 int launch_multi_reduce_t(const void* ws, const MultiOffsets& off, int n_chunks, int n, hipStream_t s) {
     hipLaunchKernelGGL((k_multi_reduce<N>),
                        dim3((unsigned)((n_chunks + kReduceChunksPerBlock - 1) / kReduceChunksPerBlock)), dim3(kBlock),
-                       kMultiReduceLds, s, reinterpret_cast<const MultiHeader*>(ws), off, n_chunks, n, (float)n);
+                       n <= 2 ? kMultiReduceTinyLds : n <= 4 ? kMultiReduceNarrowLds : kMultiReduceLds, s,
+                       reinterpret_cast<const MultiHeader*>(ws), off, n_chunks, n, (float)n);
     return (int)hipGetLastError();
 }
 
@@ -1306,7 +1320,7 @@ int launch_accum_t(const void* const* contribs, int n, float* acc, int first, in
     Ptrs<CAP> cp{};
     for (int q = 0; q < n; ++q) cp.p[q] = contribs[q];
     const int64_t n4 = len / 4;
-    const unsigned lds = n <= 4 ? kAccumNarrowLds : kAccumLds;
+    const unsigned lds = n <= 2 ? kAccumTinyLds : n <= 4 ? kAccumNarrowLds : kAccumLds;
     if (first)
         hipLaunchKernelGGL((k_accum<N, CAP, true>), dim3(grid_for(n4, kFusedU)), dim3(kBlock), lds, s, cp, n,
                            (float)n, reinterpret_cast<f32x4*>(acc), n4);
