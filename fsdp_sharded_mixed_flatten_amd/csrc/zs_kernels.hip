@@ -69,6 +69,8 @@ constexpr unsigned kFusedMidLds = 24u << 10;
 //   resident waves: eleven per CU (14 KiB) measured 1.4% faster than ten or
 //   thirteen at the Qwen2.5-3B shape;
 constexpr unsigned kFusedNarrowLds = 14u << 10;
+//   and at 1 or 2 ranks 12 KiB (up to 1.7% faster than 14 KiB);
+constexpr unsigned kFusedTinyLds = 12u << 10;
 //   fused step writing quantized codes (more registers): 12 KiB, 3% faster
 //   than 14 or 16 KiB at the Qwen2.5-3B and Llama-7B shapes;
 constexpr unsigned kFusedQuantLds = 12u << 10;
@@ -109,6 +111,7 @@ constexpr unsigned kGatherLds = 4u << 10;
 //   faster than 12 KiB, 2% faster than 4 KiB or none);
 constexpr unsigned kMultiLds = 12u << 10;
 constexpr unsigned kMultiFusedLds = 14u << 10;
+constexpr unsigned kMultiFusedTinyLds = 10u << 10;  // 1 or 2 ranks: 4-6% faster than 14 KiB
 constexpr unsigned kMultiGatherLds = 8u << 10;
 constexpr unsigned kMultiReduceLds = 12u << 10;
 constexpr unsigned kMultiReduceNarrowLds = 8u << 10;
@@ -1246,6 +1249,7 @@ int launch_fused_q(const AdamCoef& c, const AdamCoef* cdev, const void* const* c
     for (int q = 0; q < n; ++q) cp.p[q] = contribs[q];
     const int64_t n4 = len / 4;
     const unsigned lds = QB != 0 ? kFusedQuantLds
+                         : n <= 2 ? kFusedTinyLds
                          : n <= 4 ? kFusedNarrowLds
                          : (N == 16 || N == 32) ? kFusedMidLds
                                                 : kFusedLds;
@@ -1271,7 +1275,7 @@ template <int OP, int N>
 int launch_multi_t(const CoefTable& c, const AdamCoef* cdev, const void* ws, const MultiOffsets& off, int n_chunks,
                    int n, hipStream_t s) {
     hipLaunchKernelGGL((k_multi<OP, N>), dim3((unsigned)n_chunks), dim3(kBlock),
-                       OP == kOpFused ? kMultiFusedLds : kMultiLds, s, c, cdev,
+                       OP == kOpFused ? (n <= 2 ? kMultiFusedTinyLds : kMultiFusedLds) : kMultiLds, s, c, cdev,
                        reinterpret_cast<const MultiHeader*>(ws), off, n, (float)n);
     return (int)hipGetLastError();
 }
