@@ -47,7 +47,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------ launch shape
 // Every value below was measured against its neighbours on MI355X at the
-// model shapes (Qwen2.5-3B N=4, Llama-7B N=8, Llama-70B N=64).
+// model shapes (Qwen2.5-3B N=4, Llama-7B N=8, Llama-70B N=64) and, for the
+// world-size rules, at the Llama-7B shape cut for N = 1 to 128.
 
 constexpr int kBlock = kBlockThreads;
 // Ranks whose loads a lane issues together (16 or 32 measured within noise).
@@ -78,18 +79,20 @@ constexpr unsigned kFusedQuantLds = 12u << 10;
 //   (8 to 40 KiB measured at the Llama-7B and -70B shapes; 24 KiB the same
 //   at N=64 and slower at N = 8 and 24, 32 KiB and more lose 8-11% at N=64),
 //   12 KiB at 3 or 4 ranks (2-3% faster than 8 KiB with the nt sc1 stores,
-//   16 KiB 10% slower) and 8 KiB at 1 or 2 (5-13% faster than 12 KiB). Lanes of 8 elements (16-byte contribution
-//   loads, two 16-byte accumulator accesses 32 bytes apart) ran 1.3-2x
-//   slower: each wave access then covers half of every line it touches;
+//   16 KiB 10% slower) and 8 KiB at 1 or 2 (5-13% faster than 12 KiB).
+//   Lanes of 8 elements (16-byte contribution loads, two 16-byte
+//   accumulator accesses 32 bytes apart) ran 1.3-2x slower: each wave
+//   access then covers half of every line it touches;
 constexpr unsigned kAccumLds = 16u << 10;
 constexpr unsigned kAccumNarrowLds = 12u << 10;
 constexpr unsigned kAccumTinyLds = 8u << 10;
 //   reduce: 4 KiB per rank up to 16 KiB below kMidN ranks (16 KiB 2-7%
-//   faster than 8 KiB at N = 8, 12, 16 and 24; at N=1 4 KiB against 79%
-//   slower at 16 KiB, at N=2 8 KiB against 33% slower: a light kernel needs
-//   more waves in flight), 24 KiB from kMidN (2-7% faster than 16 or 32 KiB at N = 32,
-//   40 and 48) and 32 KiB from kWideN ranks on, about five waves per CU (at
-//   N=64 3-8% faster than 8 KiB, 0.2-1.6% than 24 KiB; 48 KiB and up lose);
+//   faster than 8 KiB at N = 8, 12, 16 and 24; a light kernel needs more
+//   waves in flight: 16 KiB ran 79% slower than 4 KiB at N=1 and 33%
+//   slower than 8 KiB at N=2), 24 KiB from kMidN (2-7% faster than 16 or
+//   32 KiB at N = 32, 40 and 48) and 32 KiB from kWideN ranks on, about
+//   five waves per CU (at N=64 3-8% faster than 8 KiB, 0.2-1.6% than
+//   24 KiB; 48 KiB and up lose);
 constexpr unsigned kReduceLds = 16u << 10;
 constexpr unsigned kReduceLdsPerRank = 4u << 10;
 constexpr unsigned kReduceMidLds = 24u << 10;
@@ -105,8 +108,7 @@ constexpr unsigned kGatherLds = 4u << 10;
 //   multi-tensor kernels: 12 KiB for reduce and AdamW (10 and 14 KiB slower;
 //   for the reduce 8, 16, 24 and 32 KiB at N = 8, 24 and 64 too; the reduce
 //   at 1 or 2 ranks takes 4 KiB, 44-52% faster, and at 3 or 4 ranks 8 KiB,
-//   15% faster),
-//   14 KiB for the fused step (12 KiB 2% slower, 16 the same, 18 and 20 KiB
+//   15% faster), 14 KiB for the fused step (12 KiB 2% slower, 16 the same, 18 and 20 KiB
 //   slower at the Llama-7B wrap-stress shape) and 8 KiB for the gather (12%
 //   faster than 12 KiB, 2% faster than 4 KiB or none);
 constexpr unsigned kMultiLds = 12u << 10;
@@ -1456,7 +1458,8 @@ int launch_fused(const AdamCoef& c, const void* const* contribs, int n, float* m
         case 16: return launch_fused_t<16, 16>(c, cdev, contribs, n, master, m, v, grad, param, f, len, q, s);
         case 32: return launch_fused_t<32, 32>(c, cdev, contribs, n, master, m, v, grad, param, f, len, q, s);
         case 64: return launch_fused_t<64, 64>(c, cdev, contribs, n, master, m, v, grad, param, f, len, q, s);
-        default: return launch_fused_t<0, ZS_MAX_CONTRIBS>(c, cdev, contribs, n, master, m, v, grad, param, f, len, q, s);
+        default:
+            return launch_fused_t<0, ZS_MAX_CONTRIBS>(c, cdev, contribs, n, master, m, v, grad, param, f, len, q, s);
     }
 }
 
