@@ -263,8 +263,9 @@ __device__ __forceinline__ void st_lane(T* p, T x) {
 // Row loads of 16-byte units, nontemporal: the N-way reduce's contribution
 // reads (0.2-1.2% faster at N=64 than global loads; sc0 or sc1 added change
 // nothing, sc0|sc1 without nt is 5% slower). The fused step and the
-// accumulation micro-step measured the same or slower with them (4% slower
-// for the accumulation at N=8) and keep global loads.
+// accumulation micro-step measured the same or slower with them (the
+// accumulation 1% slower at N=64 with its contributions loaded this way, 4%
+// at N=8 with its accumulator too) and keep global loads.
 __device__ __forceinline__ u32x4 ld_lane(const u32x4* p) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(row_rsrc(p), (int)(threadIdx.x * 16), 0, 2));
 }
