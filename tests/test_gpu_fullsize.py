@@ -342,6 +342,43 @@ def test_llama7b_shape_fused_at_rank_5(zs):
     _release()
 
 
+@pytest.mark.parametrize("world,rank", [(48, 47), (56, 13)])
+def test_llama7b_shape_runtime_world_sizes(zs, world, rank):
+    """The Llama-7B shape cut for world sizes without a compiled rank loop,
+    through the runtime loop at full size: N=48 (six groups of 8, the one-pass
+    fused kernel) and N=56 with the grad shard given (seven groups, the
+    two-pass form), two steps each, at a nonzero rank whose slice of the
+    gathered buffer starts at r*S; grad, param and gathered slice sampled
+    against the oracle, the other ranks' slices kept."""
+    import dataclasses
+
+    import torch
+    wl = dataclasses.replace(synth.workloads()["llama7b"], world=world, bucket_elems=0)
+    if _free_gib() < 50:
+        pytest.skip("needs ~40 GiB of free device memory")
+    run = FlatBig(zs, wl, n_random=100_000, rank=rank)
+    S, T = run.S, run.T
+    lo = rank * S
+    hp = _hp(zs, wl)
+    full = torch.full((T,), SENT, dtype=torch.int16, device="cuda")
+    two_pass = world >= zs.FUSED_TWO_PASS_MIN_CONTRIBS
+    grad = torch.full((S,), SENT, dtype=torch.int16, device="cuda") if two_pass else None
+    for t in (1, 2):
+        run.gen_contribs(t)
+        zs.zs_fused_shard_step(run.plan, hp.at(t), run.contribs, run.master, run.m, run.v, grad=grad, full=full)
+        run.oracle_step(t, hp)
+    torch.cuda.synchronize()
+    nd = run.check_state(f"llama7b N={world} rank {rank}")
+    nd += check_bf16(run.pick16(full[lo:lo + S]), run.o_p, "gathered param")
+    if two_pass:
+        nd += check_bf16(run.pick16(grad), run.o_g, "grad")
+    assert nd == 0, f"{nd} sampled elements not bit-identical"
+    assert bool((full[:lo] == SENT).all()), "the gather wrote into lower ranks' slices"
+    assert bool((full[lo + S:] == SENT).all()), "the gather wrote into higher ranks' slices"
+    del run, full, grad
+    _release()
+
+
 def _block_samples(S, B, n_blocks, seed):
     """Element indices of whole quantization blocks: the first, the last (ragged
     if S % B) and n_blocks random ones."""
