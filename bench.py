@@ -121,6 +121,9 @@ def parse():
     ap.add_argument("--quant", default="4:256",
                     help="BITS:BLOCK of the quantized-gather legs; 'none' skips them")
     ap.add_argument("--offload-chunk", type=int, default=1 << 24, help="elements per offload pipeline chunk")
+    ap.add_argument("--world", type=int, default=0,
+                    help="cut the --workload shape for this world size (1..256) instead of its own; "
+                         "the other workloads are then not run")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
     return ap.parse_args()
@@ -728,8 +731,15 @@ def cpu_baseline(oracle, synth, wl, S, window, bpp):
             "single_thread_params_per_s": n / secs1[0]}
 
 
-def run_workload(zs, synth, torch, name, args, primary):
+def workload(synth, name, world=0):
+    """The named workload, cut for `world` ranks when that is nonzero."""
+    import dataclasses
     wl = synth.workloads()["llama7b" if name == "llama7b_bucketed" else name]
+    return dataclasses.replace(wl, world=world) if world else wl
+
+
+def run_workload(zs, synth, torch, name, args, primary):
+    wl = workload(synth, name, args.world if primary else 0)
     try:
         if name == "llama7b_bucketed":
             return bucketed_workload(zs, synth, torch, wl, args)
@@ -768,6 +778,11 @@ def main():
         log(f"[bench] calibration copy: {n * 4:,} bytes read and written per launch, 3 launches")
         del a, b
 
+    if args.world:
+        if not 1 <= args.world <= zs.ZS_MAX_CONTRIBS:
+            print(f"--world {args.world} is outside 1..{zs.ZS_MAX_CONTRIBS}", file=sys.stderr)
+            sys.exit(2)
+        args.also = "none"
     head = run_workload(zs, synth, torch, args.workload, args, primary=True)
     if "skipped" in head:
         print(json.dumps({"metric": METRIC, "error": head["skipped"]}), flush=True)
@@ -778,7 +793,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         import oracle
-        wl = synth.workloads()["llama7b" if args.workload == "llama7b_bucketed" else args.workload]
+        wl = workload(synth, args.workload, args.world)
         log(f"[bench] CPU oracle baseline on a {min(args.cpu_window, head['shard_elems']):,}-element window, "
             f"N={wl.world}")
         cpu = cpu_baseline(oracle, synth, wl, head["shard_elems"], args.cpu_window, fused_bpp(wl.world))
