@@ -189,14 +189,17 @@ def test_llama7b_shape_ten_steps_bucketed_and_fused(zs):
     _release()
 
 
-@pytest.mark.parametrize("persist", [0, 100_000])
-def test_llama7b_wrap_stress_multi_tensor(zs, persist):
+@pytest.mark.parametrize("persist,world,rank", [(0, 8, 0), (100_000, 8, 0), (0, 64, 41)])
+def test_llama7b_wrap_stress_multi_tensor(zs, persist, world, rank):
     """The 291-piece per-tensor plan; with persist=100,000 (the threshold the
     pages suggest) the 65 norm vectors are replicated and updated whole with a
     second hyperparameter group (no weight decay), as an FSDP2 model would
-    hold them."""
+    hold them. At 64 ranks (rank 41) the fused call, with the grad pieces
+    bound, runs as two launches."""
+    import dataclasses
+
     import torch
-    wl = synth.workloads()["llama7b_wrap"]
+    wl = dataclasses.replace(synth.workloads()["llama7b_wrap"], world=world, rank=rank)
     if _free_gib() < 60:
         pytest.skip("needs ~50 GiB of free device memory")
     groups = [1 if n < persist else 0 for n in wl.numels] if persist else None
