@@ -217,7 +217,7 @@ def read_traffic(kernel_name, workload):
     """Counter-measured HBM bytes per launch (profiles/traffic.json), or None
     once the kernels' code (kernel_hash) has changed since the counters were
     taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if workload is None or not os.path.exists(TRAFFIC_FILE):
         return None
     try:
         with open(TRAFFIC_FILE) as fh:
@@ -421,14 +421,14 @@ def flat_workload(zs, synth, torch, wl, args, primary):
            "median_set": med}
     if two_pass:
         # dominant kernel: the N-way reduce (2N+2 bytes per owned element)
-        out["roofline"] = roofline("k_reduce", wl.name, S, reduce_bpp(N), med["reduce_ms_mean"])
+        out["roofline"] = roofline("k_reduce", traffic_key(wl), S, reduce_bpp(N), med["reduce_ms_mean"])
         out["kernels"] = {"k_reduce": {"ms": med["reduce_ms_mean"], "bytes_per_param": reduce_bpp(N),
                                        "gbps": S * reduce_bpp(N) / med["reduce_ms_mean"] / 1e6},
                           "k_adamw": {"ms": med["adamw_ms_mean"], "bytes_per_param": adamw_bpp(),
                                       "gbps": S * adamw_bpp() / med["adamw_ms_mean"] / 1e6,
                                       "note": "also reads the 2-byte grad shard the reduce wrote"}}
     else:
-        out["roofline"] = roofline("k_fused", wl.name, S, bpp, med["device_ms_per_step"])
+        out["roofline"] = roofline("k_fused", traffic_key(wl), S, bpp, med["device_ms_per_step"])
     # the whole step against the minimum the method moves: 2N+26 B per owned
     # element (plus the grad shard written by the two-pass form, which the ledger keeps)
     step_ms = med["device_ms_per_step"]
@@ -507,7 +507,7 @@ def flat_extra_legs(zs, synth, torch, wl, plan, hp0, st, args, head):
             paths["dequant_gather"] = {"bits": bits, "block": qblock, "gathered_elems": T, "ms_per_step": d_wall,
                                        "device_ms_per_step": d_dev, "events_ms_median": statistics.median(d_t.ms()),
                                        "bytes_per_gathered_elem": d_bpe,
-                                       "roofline": roofline("k_dequant", wl.name, T, d_bpe, d_dev)}
+                                       "roofline": roofline("k_dequant", traffic_key(wl), T, d_bpe, d_dev)}
             del codes_all, scales_all
         else:
             paths["dequant_gather"] = {"skipped": "the gathered buffer and all payloads do not fit beside the "
@@ -632,7 +632,7 @@ def bucketed_workload(zs, synth, torch, wl, args):
            "params_per_s": S / (wall / 1e3),
            # the step's kernels are the per-bucket launches of k_fused; their
            # average launch covers S / buckets elements
-           "roofline": roofline("k_fused", f"{wl.name}_bucketed", S / nb, bpp, dev / nb),
+           "roofline": roofline("k_fused", traffic_key(wl, "_bucketed"), S / nb, bpp, dev / nb),
            "paths": {"unfused_bucketed_reduce": {"ms_per_step": u_wall, "device_ms_per_step": u_dev,
                                                  "events_ms_median": statistics.median(u_t.ms()),
                                                  "bytes_per_param": unfused_bpp(N),
@@ -669,7 +669,7 @@ def wrap_workload(zs, synth, torch, wl, args):
         ev = t.ms()
         rec = {"ms_per_step": wall, "device_ms_per_step": dev, "events_ms_median": statistics.median(ev),
                "events_ms_p99": p99(ev), "params_per_s": S / (wall / 1e3),
-               "roofline": roofline("k_multi", wl.name if packed else f"{wl.name}_separate", S, bpp, dev)}
+               "roofline": roofline("k_multi", traffic_key(wl, "" if packed else "_separate"), S, bpp, dev)}
         if packed:
             def unfused(t, timer):
                 e = timer.start() if timer else None
@@ -735,7 +735,15 @@ def workload(synth, name, world=0):
     """The named workload, cut for `world` ranks when that is nonzero."""
     import dataclasses
     wl = synth.workloads()["llama7b" if name == "llama7b_bucketed" else name]
-    return dataclasses.replace(wl, world=world) if world else wl
+    if not world or world == wl.world:
+        return wl
+    return dataclasses.replace(wl, world=world, extra=dict(wl.extra, resized=True))
+
+
+def traffic_key(wl, suffix=""):
+    """The key of the workload's counter-measured traffic; None for a shape
+    cut for another world size, which the counters were not taken on."""
+    return None if wl.extra.get("resized") else wl.name + suffix
 
 
 def run_workload(zs, synth, torch, name, args, primary):

@@ -34,3 +34,14 @@ def test_bytes_per_element(N):
     assert bench.adamw_bpp() == 28
     assert bench.fused_bpp(N) == 2 * N + 26
     assert bench.unfused_bpp(N) == (2 * N + 2) + 28 + 4
+
+
+def test_counter_traffic_only_for_the_measured_world_size():
+    import synth
+    stock = bench.workload(synth, "llama7b")
+    assert bench.traffic_key(stock) == "llama7b"
+    assert bench.traffic_key(stock, "_bucketed") == "llama7b_bucketed"
+    assert bench.traffic_key(bench.workload(synth, "llama7b", stock.world)) == "llama7b"
+    resized = bench.workload(synth, "llama7b", 48)
+    assert resized.world == 48 and bench.traffic_key(resized) is None
+    assert bench.read_traffic("k_fused", None) is None
