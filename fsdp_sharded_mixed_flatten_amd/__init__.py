@@ -23,7 +23,7 @@ ZS_LAYOUT_FLAT, ZS_LAYOUT_PER_TENSOR = 0, 1
 ZS_MAX_CONTRIBS = 256
 ZS_MAX_GROUPS = 8
 GRAD_STATS_NOALLOC_MAX_ELEMS = 1431568384
-FUSED_TWO_PASS_MIN_CONTRIBS = 56  # zs_fused_shard_step runs two passes from here when grad is given
+FUSED_TWO_PASS_MIN_CONTRIBS = 52  # zs_fused_shard_step runs two passes from here when grad is given
 
 _STATUS_NAMES = {0: "ZS_OK", -1: "ZS_EINVAL", -2: "ZS_EALIGN", -3: "ZS_ERANGE", -4: "ZS_EHIP",
                  -5: "ZS_ENOMEM"}

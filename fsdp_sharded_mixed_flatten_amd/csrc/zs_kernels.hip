@@ -126,11 +126,11 @@ constexpr unsigned kDequantLds = 4u << 10;
 constexpr int kDequantU = 4;
 // World size from which the fused entry point runs the reduce into the grad
 // shard, then AdamW + gather, when the caller provides the grad buffer. At
-// the Llama-7B shape the two passes are 3-6% faster at N=56, 11% at N=64
-// and 14% at N=128 (at the Llama-70B shape every one-pass layout measured
-// 7-25% slower at N=64); from 33 to 48 ranks the two forms land within 3% of
-// each other either way round, depending on buffer placement, and below 32
-// the one pass wins (5-7% at N=16 and 24).
+// the Llama-7B shape the two passes are 3.7% faster at N=52 (mean of five
+// buffer sets), 3-6% at N=56, 11% at N=64 and 14% at N=128 (at the
+// Llama-70B shape every one-pass layout measured 7-25% slower at N=64);
+// from 33 to 48 ranks the two forms average within 1.6% of each other
+// either way round, and below 32 the one pass wins (5-7% at N=16 and 24).
 constexpr int kSplitMinN = ZS_FUSED_TWO_PASS_MIN_CONTRIBS;
 
 // ------------------------------------------------------------------ bf16

@@ -219,7 +219,7 @@ zs_status zs_gather_params(const zs_plan* plan, const void* param_bf16, void* fu
  * passes -- the reduce into grad_bf16, then AdamW writing param/full --
  * which keep the read-heavy and write-heavy traffic apart and run faster on
  * MI355X at those sizes. Either form leaves the same bytes. */
-#define ZS_FUSED_TWO_PASS_MIN_CONTRIBS 56
+#define ZS_FUSED_TWO_PASS_MIN_CONTRIBS 52
 zs_status zs_fused_shard_step(const zs_plan* plan, const zs_adamw_hparams* hp,
                               const void* const* contribs, int32_t n_contribs, float* master,
                               float* m, float* v, void* grad_bf16, void* param_bf16,
