@@ -34,7 +34,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E peak
-KERNEL_SRCS = [os.path.join(ROOT, "fsdp_sharded_mixed_flatten_amd", "csrc", f) for f in ("zs_kernels.hip", "zs_internal.h")]
+KERNEL_SRCS = ([os.path.join(ROOT, "fsdp_sharded_mixed_flatten_amd", "csrc", f) for f in ("zs_kernels.hip", "zs_internal.h")]
+               + [os.path.join(ROOT, "include", "zs.h")])
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 METRIC = "shard step: params updated/s + achieved HBM GB/s (% of MI355X peak)"
@@ -87,9 +88,10 @@ def code_text(src):
 
 
 def kernel_hash():
-    """Hash of the kernels' code (the kernel source and its internal header,
-    comments and layout excluded): counter-measured traffic stays valid
-    across comment edits and is dropped by any change to the code."""
+    """Hash of the kernels' code (the kernel source, its internal header and
+    the public header whose constants they use; comments and layout
+    excluded): counter-measured traffic stays valid across comment edits and
+    is dropped by any change to the code."""
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
         with open(path) as fh:
