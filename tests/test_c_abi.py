@@ -56,12 +56,15 @@ CASES = [
     ([4093, 77, 1000], 4, 3, 8, "flat"),        # the last rank owns every padding gap
     ([1_000_003], 8, 5, 1, "flat"),             # one ragged tensor, several tiles
     ([70_000, 3, 4_608], 64, 17, 128, "flat"),  # the two-pass form of the fused call
+    ([300_007, 64], 24, 23, 8, "flat"),         # the runtime rank loop (three groups of 8)
     ([4093, 77, 1000, 65_536, 5], 8, 6, 1, "per_tensor"),  # multi-tensor pieces with per-tensor padding
+    ([4093, 77, 1000, 65_536, 5], 52, 40, 1, "per_tensor"),  # the two-launch multi-tensor step
 ]
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("numels,world,rank,align,layout", CASES, ids=["n4", "n8", "n64", "per_tensor_n8"])
+@pytest.mark.parametrize("numels,world,rank,align,layout", CASES,
+                         ids=["n4", "n8", "n64", "n24", "per_tensor_n8", "per_tensor_n52"])
 def test_c_program_matches_oracle(tmp_path, ora, syn, numels, world, rank, align, layout):
     from oracle.plan import plan_flat, plan_per_tensor
     steps = 3
