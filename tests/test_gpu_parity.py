@@ -189,7 +189,7 @@ def test_random_flat_plans(zs, seed):
     run.check()
 
 
-@pytest.mark.parametrize("N", [1, 2, 4, 8, 16, 32, 64, 3, 7, 9, 12, 15, 24, 31, 40, 48, 63, 65, 100, 256])
+@pytest.mark.parametrize("N", [1, 2, 4, 8, 16, 32, 64, 3, 7, 9, 12, 15, 24, 31, 40, 48, 51, 52, 63, 65, 100, 256])
 def test_world_sizes(zs, N):
     """Every compiled rank-loop variant (N = 1..64) and the runtime loop:
     remainders of 0 to 7 ranks after its groups of 8, no full group (3, 7),
