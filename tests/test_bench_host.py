@@ -45,3 +45,13 @@ def test_counter_traffic_only_for_the_measured_world_size():
     resized = bench.workload(synth, "llama7b", 48)
     assert resized.world == 48 and bench.traffic_key(resized) is None
     assert bench.read_traffic("k_fused", None) is None
+
+
+@pytest.mark.parametrize("gpus", [2, 8])
+def test_more_than_one_gpu_is_refused_with_a_message(gpus):
+    import subprocess
+    import sys
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", str(gpus)],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr and res.stdout == ""
